@@ -1,0 +1,86 @@
+"""Seeded synthetic inputs for the sparse GQA attention hot path.
+
+One PCG64 stream per workload, drawn in a fixed order:
+q_idx, key_state, w, Q, K, V, k_scale, v_scale.
+
+* indexer query/key values: integers uniform in [-8, 8], stored in the indexer
+  dtype (BF16 by default; every such integer is exact there);
+* indexer head weights w_h: integers uniform in [1, 4], one per head, FP32,
+  broadcast over batch and query tokens;
+* Q, K, V: N(0, 1) drawn in FP32 and rounded to nearest-even into the storage
+  dtype;
+* INT8 KV: codes uniform in [-127, 127] and one FP32 scale per token per KV
+  head for K and one for V, uniform in [0.005, 0.05).
+
+With integer indexer inputs every partial sum of a score is an integer below
+2**24 in magnitude, so scores are exact in FP32 whatever the summation order.
+This module returns host tensors only; it does no arithmetic of the method.
+"""
+import numpy as np
+import torch
+
+from .workloads import Workload
+
+_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "i8": torch.int8}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return _TORCH[name]
+
+
+def _normal(rng, shape, dtype_name):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return torch.from_numpy(x).to(_TORCH[dtype_name])
+
+
+def _int_uniform(rng, lo, hi, shape, dtype_name):
+    x = rng.integers(lo, hi + 1, size=shape, dtype=np.int16).astype(np.float32)
+    return torch.from_numpy(x).to(_TORCH[dtype_name])
+
+
+def make_inputs(w: Workload, seed=None, kv_len=None):
+    """Host tensors for one layer of workload `w`.
+
+    Returns a dict with keys q_idx, w_idx, key_state (absent without an
+    indexer), q, k_cache, v_cache, k_scale, v_scale (None unless INT8 KV),
+    kv_len (int32 [B]) and, for dense-selection workloads, indices.
+    `kv_len` overrides the per-sequence live length (default: every sequence
+    full, kv_len = L).
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    B, S, L = w.B, w.S, w.L
+    out = {}
+    if w.has_indexer:
+        out["q_idx"] = _int_uniform(rng, -8, 8, (B, S, w.H_idx, w.D_idx), w.idx_dtype)
+        out["key_state"] = _int_uniform(rng, -8, 8, (B, L, w.D_idx), w.idx_dtype)
+        heads = rng.integers(1, 5, size=(w.H_idx,)).astype(np.float32)
+        out["w_idx"] = torch.from_numpy(np.tile(heads, (B, S, 1)))
+    out["q"] = _normal(rng, (B, S, w.H_q, w.D), w.q_dtype)
+    if w.kv_dtype == "i8":
+        kv_shape = (B, L, w.H_kv, w.D)
+        out["k_cache"] = torch.from_numpy(
+            rng.integers(-127, 128, size=kv_shape, dtype=np.int8))
+        out["v_cache"] = torch.from_numpy(
+            rng.integers(-127, 128, size=kv_shape, dtype=np.int8))
+        out["k_scale"] = torch.from_numpy(
+            rng.uniform(0.005, 0.05, size=(B, L, w.H_kv)).astype(np.float32))
+        out["v_scale"] = torch.from_numpy(
+            rng.uniform(0.005, 0.05, size=(B, L, w.H_kv)).astype(np.float32))
+    else:
+        out["k_cache"] = _normal(rng, (B, L, w.H_kv, w.D), w.kv_dtype)
+        out["v_cache"] = _normal(rng, (B, L, w.H_kv, w.D), w.kv_dtype)
+        out["k_scale"] = None
+        out["v_scale"] = None
+    if kv_len is None:
+        kv_len = [L] * B
+    out["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)
+    if not w.has_indexer:
+        # Dense selection: every cached key of the row, in ascending order.
+        out["indices"] = torch.arange(w.k, dtype=torch.int32).repeat(B, S, 1).contiguous()
+    return out
+
+
+def integer_scores(rng, shape, lo, hi):
+    """FP32 array of integers uniform in [lo, hi] (a tie-heavy score source)."""
+    return torch.from_numpy(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
