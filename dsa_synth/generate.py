@@ -84,3 +84,14 @@ def make_inputs(w: Workload, seed=None, kv_len=None):
 def integer_scores(rng, shape, lo, hi):
     """FP32 array of integers uniform in [lo, hi] (a tie-heavy score source)."""
     return torch.from_numpy(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+
+
+def indexer_like_scores(rng, shape, sigma=2100.0):
+    """FP32 integers drawn from N(0, sigma^2), rounded to nearest.
+
+    The spread of a 16-head x 64-dim indexer score with integer inputs in
+    [-8, 8] and weights in [1, 4]; a stand-in score matrix for top-k tests
+    at full size without running the indexer.
+    """
+    x = np.rint(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma))
+    return torch.from_numpy(x.astype(np.float32))

@@ -1,0 +1,159 @@
+/*
+ * dsa.h -- C ABI of the dynamic sparse GQA attention library (libdsa.so).
+ *
+ * Dynamic sparse attention runs in three stages: an indexer scores every
+ * cached token against each query token, a per-query top-k selects keys, and
+ * softmax attention runs over the selected keys only ("selected only"
+ * attention with grouped query heads: ORT PR #33997 "Support FP16 KV cache
+ * and FP16 query/key in DynamicSparseAttention<BFloat16> ...", Description
+ * item 2 and its test list; ORT PR #33802 "Optimize Qwen3.8-Flash-Next DSA,
+ * Indexer, HC, and QMoE kernels for SM12x and 256K context", Summary
+ * items 1-2).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is DEVICE memory owned by the caller, dense and
+ *    row-major in the layout stated, with a 16-byte-aligned base address.
+ *  - The library never allocates, frees or synchronises.  Calls validate
+ *    their arguments on the host, enqueue kernels on `stream` (a hipStream_t
+ *    passed as void*; NULL is the null stream) and return.  Enqueued work is
+ *    ordered on that stream only.
+ *  - Validation happens before any launch: a non-OK status means nothing was
+ *    enqueued and nothing was written.  dsa_last_error() then describes it.
+ *  - The library keeps no state between calls.  Workspace contents on entry
+ *    are never trusted (each call initialises what it reads).
+ *  - Per-sequence live length kv_len[b] lives on the device; the host passes
+ *    an upper bound max_kv_len (<= L_cap) that sizes the launch grids.
+ *    Query token s of sequence b sits at position pos(b,s) = kv_len[b]-S+s
+ *    and may attend to keys 0..pos(b,s) (its own key included).
+ *    Device preconditions (not checkable on the host):
+ *    S <= kv_len[b] <= max_kv_len.  Rows with pos < 0 select no key.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size or shape        */
+  DSA_ERR_UNSUPPORTED = 2,         /* valid but unimplemented combination    */
+  DSA_ERR_MISALIGNED = 3,          /* a base pointer is not 16-byte aligned  */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace smaller than the query says  */
+  DSA_ERR_HIP = 5                  /* a HIP runtime call or launch failed    */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_F16 = 1, DSA_BF16 = 2, DSA_I8 = 3 } dsa_dtype;
+
+/* DSA_ABI_VERSION of the built library. */
+int dsa_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next call on that thread. */
+const char* dsa_last_error(void);
+
+/*
+ * Indexer score (ORT PR #33802, Summary item 2: per-head scoring of the
+ * key-state cache reduced over the indexer heads).
+ *
+ *   scores[b,s,j] = sum_h w_idx[b,s,h] * sum_d q_idx[b,s,h,d] * key_state[b,j,d]
+ *
+ * for 0 <= j <= pos(b,s).  Accumulation is FP32; with integer-valued inputs
+ * whose partial sums stay below 2^24 the result is exact.
+ *   q_idx      [B, S, H_idx, D_idx]  idx_dtype (DSA_BF16 or DSA_F16)
+ *   w_idx      [B, S, H_idx]         FP32
+ *   key_state  [B, L_cap, D_idx]     idx_dtype
+ *   kv_len     [B]                   int32, device
+ *   scores     [B, S, L_cap]         FP32, written for j < kv_len[b];
+ *              entries pos < j < kv_len[b] hold finite values that mean
+ *              nothing, entries j >= kv_len[b] are left untouched.
+ * Supported: 1 <= H_idx <= 16, D_idx in {32, 64, 128}.
+ */
+dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx,
+                             const void* key_state, dsa_dtype idx_dtype,
+                             const int32_t* kv_len, int B, int S, int H_idx,
+                             int D_idx, int L_cap, int max_kv_len,
+                             float* scores, void* stream);
+
+/*
+ * Per-query top-k (ORT PR #33802, Summary item 2: chunked radix histograms
+ * merged across up to 64+ chunks, then emitted).
+ *
+ * For row (b,s) the candidates are j = 0..pos(b,s).  The k highest scores
+ * are kept, equal scores broken toward the LOWER index; the kept indices are
+ * written in ascending order, and slots beyond the number of candidates hold
+ * -1.  -0.0 ranks equal to +0.0; -inf is allowed; NaN is not supported.
+ *   scores   [B, S, L_cap]  FP32 (only j <= pos(b,s) is read)
+ *   indices  [B, S, k]      int32 output
+ *   workspace: at least dsa_topk_workspace_bytes(B, S, L_cap, k) bytes of
+ *   device memory (may be NULL when that is 0); contents on entry are
+ *   ignored, contents on return are unspecified.
+ * Supported: 1 <= k <= L_cap <= 2^24.
+ */
+size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k);
+dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S,
+                    int L_cap, int max_kv_len, int k, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse GQA attention over selected keys (ORT PR #33997, Description item 2;
+ * ORT PR #33802, Summary item 1 and follow-up #33847 on the rising running
+ * maximum).  For query head h of row (b,s), with g = h / (H_q / H_kv):
+ *
+ *   logit_j = softmax_scale * sum_d q[b,s,h,d] * K[b,j,g,d]
+ *   out[b,s,h,:] = sum_j p_j V[b,j,g,:] / sum_j p_j,  p_j = exp(logit_j - max)
+ *
+ * over the valid entries j of indices[b,s,:]: 0 <= j <= pos(b,s) and
+ * j < L_cap.  Invalid entries (-1 padding included) are skipped.  Entries
+ * must be unique.  A row with no valid entry is written as zeros.
+ * INT8 cache: K = code * k_scale[b,j,g], V = code * v_scale[b,j,g]
+ * (symmetric, no zero point).
+ *
+ *   q        [B, S, H_q, D]      q_dtype
+ *   k_cache  [B, L_cap, H_kv, D] kv_dtype
+ *   v_cache  [B, L_cap, H_kv, D] kv_dtype
+ *   k_scale, v_scale [B, L_cap, H_kv] FP32 for DSA_I8, NULL otherwise
+ *   indices  [B, S, k]           int32
+ *   kv_len   [B]                 int32, device
+ *   out      [B, S, H_q, D]      out_dtype, rounded to nearest-even
+ * Supported combinations: q/kv/out all DSA_F32; or q in {F16, BF16} with
+ * kv in {F16, BF16, I8} and out in {F32, F16, BF16}.  D in {64, 128};
+ * H_q % H_kv == 0 and H_q / H_kv <= 16.  With an F16 cache (or F16 query
+ * against a BF16 cache) both operands are multiplied as FP16: query values
+ * must lie within FP16 range.
+ * softmax_scale <= 0 selects 1/sqrt(D).
+ *
+ * decode: the selected keys of each row are split over several workgroups
+ * whose partial softmax states are merged exactly in a second kernel; it
+ * needs dsa_attention_workspace_bytes(args, 1) bytes of workspace.
+ * prefill: one workgroup per (row, KV head); no workspace (size 0).
+ * Both accept any S and compute the same function.
+ */
+typedef struct {
+  const void* q;        int32_t q_dtype;
+  const void* k_cache;  const void* v_cache;  int32_t kv_dtype;
+  const float* k_scale; const float* v_scale;
+  const int32_t* indices; int32_t k;
+  const int32_t* kv_len;
+  int32_t B, S, H_q, H_kv, D, L_cap, max_kv_len;
+  float softmax_scale;
+  void* out;            int32_t out_dtype;
+} dsa_attention_args;
+
+size_t dsa_attention_workspace_bytes(const dsa_attention_args* args, int is_decode);
+dsa_status dsa_attention_decode(const dsa_attention_args* args, void* workspace,
+                                size_t workspace_bytes, void* stream);
+dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

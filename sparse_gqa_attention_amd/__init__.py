@@ -1,0 +1,14 @@
+"""Dynamic sparse GQA attention on MI355X (gfx950): indexer -> top-k -> attention.
+
+The compute runs in libdsa.so (hand-written HIP kernels behind the C ABI of
+include/dsa.h); this package is its Python binding.
+"""
+from .dsa import (DsaError, dsa_abi_version, dsa_last_error, dsa_indexer_score,
+                  dsa_topk_workspace_bytes, dsa_topk, attention_args,
+                  dsa_attention_workspace_bytes, dsa_attention_decode,
+                  dsa_attention_prefill, default_softmax_scale, EXPORTS, LIB)
+
+__all__ = ["DsaError", "dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
+           "dsa_topk_workspace_bytes", "dsa_topk", "attention_args",
+           "dsa_attention_workspace_bytes", "dsa_attention_decode",
+           "dsa_attention_prefill", "default_softmax_scale", "EXPORTS", "LIB"]

@@ -1,0 +1,430 @@
+// Sparse GQA attention over the selected keys (ORT PR #33997 "Support FP16 KV
+// cache and FP16 query/key in DynamicSparseAttention<BFloat16> ...",
+// Description item 2: selected-only attention, grouped decode, FP16 cache
+// with BF16 activations, query read without a separate conversion kernel;
+// ORT PR #33802, Summary item 1: INT8 cache with per-token scales, split-K
+// decode, and follow-up #33847: a rising running maximum rescales the
+// accumulator by exp(old_max - new_max) and must not flush it to zero).
+//
+// gfx950 design.  A workgroup (4 waves) owns one (row, KV head g, key split).
+// Each wave walks 32-key tiles of the split's selected-index list.  The
+// logits are formed transposed, S^T = K . Q^T, with v_mfma_f32_16x16x32:
+//   * A operand = K rows: lane l loads a contiguous quarter of the row of key
+//     (l % 16) straight from HBM with 16-byte loads (the d <-> k-slot
+//     permutation is free because Q uses the same one);
+//   * B operand = Q^T: the R <= 16 query heads of group g (zero-padded),
+//     converted once to the MFMA type and kept in registers.
+// S^T leaves each lane with 4 keys of one head, which is exactly the B
+// operand layout of the next product, O^T = V^T . P^T: P never moves between
+// lanes.  V^T needs keys along the k-slot, so the wave stages its 32 V rows
+// in LDS and reads them back transposed.
+// Numerics: FP32 accumulation everywhere; P enters the PV product as a
+// hi/lo pair of 16-bit values (two MFMAs), keeping ~16 bits of each weight;
+// INT8 codes enter the MFMAs exactly and their per-token scales are applied
+// in FP32 (logit * k_scale, p * v_scale).  The online-softmax rescale keeps
+// FP32 subnormals (exp_keep_subnormal).
+// The 4 waves' (max, sum, O) states merge in LDS; with several key splits
+// the workgroup writes an unnormalised partial and attn_merge_kernel
+// combines the splits in a fixed order (deterministic).
+#include <type_traits>
+
+#include "dsa_device.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kTile = 32;
+
+struct AttnParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* indices;
+  const int32_t* kv_len;
+  void* out;
+  float* part;
+  int S, H_q, H_kv, L_cap, k, ratio, out_dtype, nsplit, kps;
+  float scale;
+};
+
+__device__ __forceinline__ void store_out(void* out, size_t i, float v, int dt) {
+  if (dt == kF32) ((float*)out)[i] = v;
+  else if (dt == kF16) ((_Float16*)out)[i] = (_Float16)v;
+  else ((__bf16*)out)[i] = (__bf16)v;
+}
+
+// N elements of T from global memory (N * sizeof(T) a multiple of 16).
+template <typename T, int N>
+__device__ __forceinline__ void load_elems(const T* src, T (&dst)[N]) {
+  constexpr int NV = N * (int)sizeof(T) / 16;
+  uint4 tmp[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) tmp[i] = ld_vec<uint4>((const char*)src + 16 * i);
+  __builtin_memcpy(dst, tmp, sizeof(dst));
+}
+
+template <typename To, typename From>
+__device__ __forceinline__ To cvt(From x) {
+  if constexpr (std::is_same<To, From>::value) return x;
+  else return from_f32<To>(to_f32(x));
+}
+
+template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+struct AttnCfg {
+  static constexpr bool kF32Path = std::is_same<KVT, float>::value;
+  static constexpr bool kInt8 = std::is_same<KVT, int8_t>::value;
+  static constexpr int kQuarter = D / 4;             // elements of a row per lane
+  static constexpr int kSteps = D / 32;              // QK K-steps (16-bit path)
+  static constexpr int kDTiles = D / 16;             // O^T tiles of 16 dims
+  static constexpr int kVPad = kF32Path ? 4 : 8;     // LDS row padding (elements)
+  static constexpr int kVStride = D + kVPad;
+  static constexpr size_t kVBytes = (size_t)kAttnWaves * kTile * kVStride * sizeof(MPV);
+  static constexpr size_t kMergeBytes = (size_t)kAttnWaves * 16 * (D + 2) * sizeof(float);
+  static constexpr size_t kLds = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+};
+
+template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
+  using Cfg = AttnCfg<D, QT, KVT, MQK, MPV>;
+  constexpr int Q4 = Cfg::kQuarter;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kLds];
+
+  const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
+  const int b = row / p.S, s = row % p.S;
+  int kvl = p.kv_len[b];
+  kvl = kvl < 0 ? 0 : (kvl > p.L_cap ? p.L_cap : kvl);
+  const int pos = kvl - p.S + s;
+  const int live = min(kvl, pos + 1);     // valid key indices are [0, live)
+  const int32_t* idx_row = p.indices + (size_t)row * p.k;
+  const int k0 = split * p.kps;
+  const int k1 = min(p.k, k0 + p.kps);
+
+  const int wave = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int g4 = l >> 4;        // lane group 0..3
+  const int c16 = l & 15;       // head column / key row within a half tile
+  const int R = p.ratio;
+  const bool head_ok = c16 < R;
+  const int h = g * R + (head_ok ? c16 : 0);
+
+  const size_t kv_row_stride = (size_t)p.H_kv * D;                  // elements per token
+  const KVT* kbase = (const KVT*)p.k_cache + (size_t)b * p.L_cap * kv_row_stride + (size_t)g * D;
+  const KVT* vbase = (const KVT*)p.v_cache + (size_t)b * p.L_cap * kv_row_stride + (size_t)g * D;
+  const float* ksc = Cfg::kInt8 ? p.k_scale + (size_t)b * p.L_cap * p.H_kv + g : nullptr;
+  const float* vsc = Cfg::kInt8 ? p.v_scale + (size_t)b * p.L_cap * p.H_kv + g : nullptr;
+
+  // ---- Q^T operand: lane holds head c16, dims [Q4*g4, Q4*g4 + Q4)
+  QT qraw[Q4];
+  {
+    const QT* qrow = (const QT*)p.q + ((size_t)row * p.H_q + h) * D + Q4 * g4;
+    load_elems<QT, Q4>(qrow, qraw);
+    if (!head_ok) {
+#pragma unroll
+      for (int i = 0; i < Q4; ++i) qraw[i] = cvt<QT>(0.0f);
+    }
+  }
+
+  MPV* vt = (MPV*)smem + (size_t)wave * kTile * Cfg::kVStride;
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  f32x4 o[Cfg::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] = f32x4{};
+
+  for (int t0 = k0 + kTile * wave; t0 < k1; t0 += kTile * kAttnWaves) {
+    // ---- this lane's two key rows (row c16 of each half tile)
+    const int ja = t0 + c16, jb = t0 + 16 + c16;
+    const int ia = ja < k1 ? idx_row[ja] : -1;
+    const int ib = jb < k1 ? idx_row[jb] : -1;
+    const bool va = ia >= 0 && ia < live;
+    const bool vb = ib >= 0 && ib < live;
+    const KVT* krow_a = kbase + (size_t)(va ? ia : 0) * kv_row_stride + Q4 * g4;
+    const KVT* krow_b = kbase + (size_t)(vb ? ib : 0) * kv_row_stride + Q4 * g4;
+    const KVT* vrow_a = vbase + (size_t)(va ? ia : 0) * kv_row_stride + Q4 * g4;
+    const KVT* vrow_b = vbase + (size_t)(vb ? ib : 0) * kv_row_stride + Q4 * g4;
+    KVT kra[Q4], krb[Q4], vra[Q4], vrb[Q4];
+    load_elems<KVT, Q4>(krow_a, kra);
+    load_elems<KVT, Q4>(krow_b, krb);
+    load_elems<KVT, Q4>(vrow_a, vra);
+    load_elems<KVT, Q4>(vrow_b, vrb);
+
+    // ---- V rows into this wave's LDS tile (converted to the PV operand type)
+    {
+      MPV va_c[Q4], vb_c[Q4];
+#pragma unroll
+      for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
+      constexpr int NV = Q4 * (int)sizeof(MPV) / 16;
+      uint4 ta[NV], tb[NV];
+      __builtin_memcpy(ta, va_c, sizeof(ta));
+      __builtin_memcpy(tb, vb_c, sizeof(tb));
+      uint4* da = (uint4*)(vt + (size_t)c16 * Cfg::kVStride + Q4 * g4);
+      uint4* db = (uint4*)(vt + (size_t)(16 + c16) * Cfg::kVStride + Q4 * g4);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) { da[i] = ta[i]; db[i] = tb[i]; }
+    }
+
+    // ---- S^T = K . Q^T for both halves
+    f32x4 sa = f32x4{}, sb = f32x4{};
+    if constexpr (Cfg::kF32Path) {
+#pragma unroll
+      for (int j = 0; j < Q4; ++j) {
+        sa = mfma16x16x4((float)kra[j], (float)qraw[j], sa);
+        sb = mfma16x16x4((float)krb[j], (float)qraw[j], sb);
+      }
+    } else {
+      using V8 = typename vec8<MQK>::type;
+#pragma unroll
+      for (int st = 0; st < Cfg::kSteps; ++st) {
+        V8 qa, ka, kb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qa[e] = cvt<MQK>(qraw[8 * st + e]);
+          ka[e] = cvt<MQK>(kra[8 * st + e]);
+          kb[e] = cvt<MQK>(krb[8 * st + e]);
+        }
+        sa = mfma16x16x32(ka, qa, sa);
+        sb = mfma16x16x32(kb, qa, sb);
+      }
+    }
+
+    // ---- logits of keys 4*g4+i (half a) and 16+4*g4+i (half b), head c16
+    float x[8];
+    float vs[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src = 4 * g4 + i;                 // lane holding that key row
+      const int ka_i = __shfl(ia, src, kWave);
+      const int kb_i = __shfl(ib, src, kWave);
+      const bool oka = __shfl((int)va, src, kWave) != 0;
+      const bool okb = __shfl((int)vb, src, kWave) != 0;
+      float fa = sa[i] * p.scale, fb = sb[i] * p.scale;
+      if constexpr (Cfg::kInt8) {
+        fa *= oka ? ksc[(size_t)ka_i * p.H_kv] : 0.0f;
+        fb *= okb ? ksc[(size_t)kb_i * p.H_kv] : 0.0f;
+        vs[i] = oka ? vsc[(size_t)ka_i * p.H_kv] : 0.0f;
+        vs[4 + i] = okb ? vsc[(size_t)kb_i * p.H_kv] : 0.0f;
+      }
+      x[i] = oka ? fa : -INFINITY;
+      x[4 + i] = okb ? fb : -INFINITY;
+    }
+
+    // ---- online softmax per head column (lanes c16, c16+16, c16+32, c16+48)
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_run == -INFINITY) ? 0.0f : exp_keep_subnormal(m_run - m_new);
+    float pv[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = (x[i] == -INFINITY) ? 0.0f : exp_keep_subnormal(x[i] - m_new);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] *= alpha;
+    if constexpr (Cfg::kInt8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] *= vs[i];
+    }
+
+    // V tile writes of this wave must land before its transposed reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- O^T += V^T . P^T
+    if constexpr (Cfg::kF32Path) {
+#pragma unroll
+      for (int dt = 0; dt < Cfg::kDTiles; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = (j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4);
+          const float a = (float)vt[(size_t)key * Cfg::kVStride + 16 * dt + c16];
+          o[dt] = mfma16x16x4(a, pv[j], o[dt]);
+        }
+      }
+    } else {
+      using V8 = typename vec8<MPV>::type;
+      V8 phi, plo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const MPV hi = from_f32<MPV>(pv[j]);
+        phi[j] = hi;
+        plo[j] = from_f32<MPV>(pv[j] - to_f32(hi));
+      }
+#pragma unroll
+      for (int dt = 0; dt < Cfg::kDTiles; ++dt) {
+        V8 a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = (j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4);
+          a[j] = vt[(size_t)key * Cfg::kVStride + 16 * dt + c16];
+        }
+        o[dt] = mfma16x16x32(a, phi, o[dt]);
+        o[dt] = mfma16x16x32(a, plo, o[dt]);
+      }
+    }
+    // Transposed reads must finish before the next tile overwrites the LDS.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the 4 waves' states in LDS
+  float l_col = l_run + __shfl_xor(l_run, 16, kWave);
+  l_col += __shfl_xor(l_col, 32, kWave);
+  __syncthreads();
+  float* mb = (float*)smem;                                  // [waves][16]
+  float* lb = mb + kAttnWaves * 16;                          // [waves][16]
+  float* ob = lb + kAttnWaves * 16;                          // [waves][16][D]
+  if (g4 == 0) {
+    mb[wave * 16 + c16] = m_run;
+    lb[wave * 16 + c16] = l_col;
+  }
+#pragma unroll
+  for (int dt = 0; dt < Cfg::kDTiles; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[((size_t)wave * 16 + c16) * D + 16 * dt + 4 * g4 + i] = o[dt][i];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < R * D; e += kAttnThreads) {
+    const int n = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mb[w * 16 + n]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = mb[w * 16 + n];
+        const float f = (mw == -INFINITY) ? 0.0f : exp_keep_subnormal(mw - M);
+        L += f * lb[w * 16 + n];
+        O += f * ob[((size_t)w * 16 + n) * D + d];
+      }
+    }
+    const size_t hrow = (size_t)row * p.H_q + g * R + n;
+    if (p.nsplit == 1) {
+      store_out(p.out, hrow * D + d, L > 0.0f ? O / L : 0.0f, p.out_dtype);
+    } else {
+      float* pml = p.part;
+      float* po = p.part + (size_t)2 * gridDim.z * p.H_q * p.nsplit;
+      po[(hrow * p.nsplit + split) * D + d] = O;
+      if (d == 0) {
+        pml[(hrow * p.nsplit + split) * 2 + 0] = M;
+        pml[(hrow * p.nsplit + split) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Combine the key splits of one (row, head): fixed order, exact rescale.
+template <int D>
+__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part, int rows_h,
+                                                        int nsplit, void* out, int out_dtype) {
+  const int hrow = blockIdx.x;
+  const int l = lane_id();
+  const float* pml = part;
+  const float* po = part + (size_t)2 * rows_h * nsplit;
+  float m = -INFINITY, lsum = 0.0f;
+  if (l < nsplit) {
+    m = pml[((size_t)hrow * nsplit + l) * 2 + 0];
+    lsum = pml[((size_t)hrow * nsplit + l) * 2 + 1];
+  }
+  float M = m;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+  const float f = (M == -INFINITY || m == -INFINITY) ? 0.0f : exp_keep_subnormal(m - M);
+  float L = f * lsum;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, kWave);
+  for (int d = l; d < D; d += kWave) {
+    float O = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float fs = __shfl(f, sp, kWave);
+      O += fs * po[((size_t)hrow * nsplit + sp) * D + d];
+    }
+    store_out(out, (size_t)hrow * D + d, L > 0.0f ? O / L : 0.0f, out_dtype);
+  }
+}
+
+template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+void launch_cfg(const AttnLaunch& a, hipStream_t st) {
+  AttnParams p;
+  p.q = a.q; p.k_cache = a.k_cache; p.v_cache = a.v_cache;
+  p.k_scale = a.k_scale; p.v_scale = a.v_scale;
+  p.indices = a.indices; p.kv_len = a.kv_len; p.out = a.out; p.part = a.part;
+  p.S = a.S; p.H_q = a.H_q; p.H_kv = a.H_kv; p.L_cap = a.L_cap; p.k = a.k;
+  p.ratio = a.H_q / a.H_kv; p.out_dtype = a.out_dtype;
+  p.nsplit = a.nsplit; p.kps = a.keys_per_split; p.scale = a.scale;
+  dim3 grid(a.nsplit, a.H_kv, a.B * a.S);
+  hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV>), grid, dim3(kAttnThreads), 0, st, p);
+  if (a.nsplit > 1) {
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.B * a.S * a.H_q), dim3(64), 0, st,
+                       (const float*)a.part, a.B * a.S * a.H_q, a.nsplit, a.out, a.out_dtype);
+  }
+}
+
+template <int D>
+void launch_d(const AttnLaunch& a, hipStream_t st) {
+  typedef _Float16 H;
+  typedef __bf16 BH;
+  if (a.kv_dtype == kF32) { launch_cfg<D, float, float, float, float>(a, st); return; }
+  if (a.q_dtype == kBF16) {
+    if (a.kv_dtype == kF16) launch_cfg<D, BH, H, H, H>(a, st);
+    else if (a.kv_dtype == kBF16) launch_cfg<D, BH, BH, BH, BH>(a, st);
+    else launch_cfg<D, BH, int8_t, BH, BH>(a, st);
+  } else {
+    if (a.kv_dtype == kF16) launch_cfg<D, H, H, H, H>(a, st);
+    else if (a.kv_dtype == kBF16) launch_cfg<D, H, BH, H, BH>(a, st);
+    else launch_cfg<D, H, int8_t, H, BH>(a, st);
+  }
+}
+
+}  // namespace
+
+void plan_attention(AttnLaunch& a, bool decode) {
+  if (!decode || a.k <= 0) {
+    a.nsplit = 1;
+    a.keys_per_split = a.k > 0 ? a.k : 1;
+    return;
+  }
+  // Aim for ~1024 workgroups; at least 128 keys (one tile per wave) per split,
+  // at most 64 splits (one merge lane per split).
+  const long long rows_kv = (long long)a.B * a.S * a.H_kv;
+  long long kps = (a.k * rows_kv + 1023) / 1024;
+  kps = ((kps + 127) / 128) * 128;
+  if (kps < 128) kps = 128;
+  long long ns = (a.k + kps - 1) / kps;
+  if (ns > 64) {
+    ns = 64;
+    kps = (a.k + 63) / 64;
+    kps = ((kps + kTile - 1) / kTile) * kTile;
+    ns = (a.k + kps - 1) / kps;
+  }
+  a.nsplit = (int)ns;
+  a.keys_per_split = (int)kps;
+}
+
+size_t attention_partials_bytes(const AttnLaunch& a) {
+  if (a.nsplit <= 1) return 0;
+  return (size_t)a.B * a.S * a.H_q * a.nsplit * (a.D + 2) * sizeof(float);
+}
+
+void launch_attention(const AttnLaunch& a, hipStream_t st) {
+  if (a.B * a.S == 0) return;
+  if (a.D == 64) launch_d<64>(a, st);
+  else launch_d<128>(a, st);
+}
+
+}  // namespace dsa

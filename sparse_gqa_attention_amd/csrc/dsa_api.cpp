@@ -1,0 +1,216 @@
+// C ABI of libdsa: argument validation, launch planning and error reporting.
+// Declarations and the contract of every entry point live in include/dsa.h.
+// Validation touches no HIP API, so every rejected call returns before any
+// device work is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+const char* dtype_name(int d) {
+  switch (d) {
+    case DSA_F32: return "F32";
+    case DSA_F16: return "F16";
+    case DSA_BF16: return "BF16";
+    case DSA_I8: return "I8";
+    default: return "unknown";
+  }
+}
+
+dsa_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(DSA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DSA_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return DSA_OK;
+}
+
+#define CHECK(expr)                    \
+  do {                                 \
+    dsa_status _s = (expr);            \
+    if (_s != DSA_OK) return _s;       \
+  } while (0)
+
+dsa_status hip_result(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ------------------------------------------------------------------ attention
+dsa_status validate_attention(const dsa_attention_args* a) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->B < 0 || a->S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", a->B, a->S);
+  if (a->k < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 0", a->k);
+  if (a->L_cap < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "L_cap=%d must be >= 1", a->L_cap);
+  if (a->max_kv_len < 0 || a->max_kv_len > a->L_cap)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", a->max_kv_len, a->L_cap);
+  if (a->H_q < 1 || a->H_kv < 1 || a->H_q % a->H_kv != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "H_q=%d must be a positive multiple of H_kv=%d", a->H_q, a->H_kv);
+  if (a->H_q / a->H_kv > 16)
+    return fail(DSA_ERR_UNSUPPORTED, "group ratio H_q/H_kv=%d exceeds 16", a->H_q / a->H_kv);
+  if (a->D != 64 && a->D != 128) return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d not in {64, 128}", a->D);
+  const int qd = a->q_dtype, kd = a->kv_dtype, od = a->out_dtype;
+  const bool f32_combo = qd == DSA_F32 && kd == DSA_F32 && od == DSA_F32;
+  const bool half_combo = (qd == DSA_F16 || qd == DSA_BF16) &&
+                          (kd == DSA_F16 || kd == DSA_BF16 || kd == DSA_I8) &&
+                          (od == DSA_F32 || od == DSA_F16 || od == DSA_BF16);
+  if (!f32_combo && !half_combo)
+    return fail(DSA_ERR_UNSUPPORTED, "dtype combination q=%s kv=%s out=%s is not supported",
+                dtype_name(qd), dtype_name(kd), dtype_name(od));
+  if (!std::isfinite(a->softmax_scale))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if ((long long)a->L_cap * a->H_kv * a->D >= (1LL << 40))
+    return fail(DSA_ERR_UNSUPPORTED, "cache too large");
+  if ((long long)a->B * a->S == 0) return DSA_OK;
+  CHECK(check_ptr(a->q, "q"));
+  CHECK(check_ptr(a->k_cache, "k_cache"));
+  CHECK(check_ptr(a->v_cache, "v_cache"));
+  CHECK(check_ptr(a->kv_len, "kv_len"));
+  CHECK(check_ptr(a->out, "out"));
+  if (a->k > 0) CHECK(check_ptr(a->indices, "indices"));
+  if (kd == DSA_I8) {
+    CHECK(check_ptr(a->k_scale, "k_scale"));
+    CHECK(check_ptr(a->v_scale, "v_scale"));
+  } else if (a->k_scale || a->v_scale) {
+    return fail(DSA_ERR_INVALID_ARGUMENT, "k_scale/v_scale must be NULL unless kv_dtype is I8");
+  }
+  return DSA_OK;
+}
+
+dsa::AttnLaunch make_attn(const dsa_attention_args* a, bool decode) {
+  dsa::AttnLaunch l{};
+  l.q = a->q; l.k_cache = a->k_cache; l.v_cache = a->v_cache;
+  l.k_scale = a->k_scale; l.v_scale = a->v_scale;
+  l.indices = a->indices; l.kv_len = a->kv_len; l.out = a->out;
+  l.q_dtype = a->q_dtype; l.kv_dtype = a->kv_dtype; l.out_dtype = a->out_dtype;
+  l.B = a->B; l.S = a->S; l.H_q = a->H_q; l.H_kv = a->H_kv; l.D = a->D;
+  l.L_cap = a->L_cap; l.k = a->k;
+  l.scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / std::sqrt((float)a->D);
+  dsa::plan_attention(l, decode);
+  return l;
+}
+
+dsa_status run_attention(const dsa_attention_args* a, void* ws, size_t ws_bytes, void* stream,
+                         bool decode) {
+  CHECK(validate_attention(a));
+  if ((long long)a->B * a->S == 0) return ok();
+  dsa::AttnLaunch l = make_attn(a, decode);
+  const size_t need = dsa::attention_partials_bytes(l);
+  if (need > 0) {
+    if (ws_bytes < need)
+      return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    CHECK(check_ptr(ws, "workspace"));
+    l.part = (float*)ws;
+  }
+  (void)hipGetLastError();
+  dsa::launch_attention(l, (hipStream_t)stream);
+  return hip_result(decode ? "dsa_attention_decode" : "dsa_attention_prefill");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* key_state,
+                             dsa_dtype idx_dtype, const int32_t* kv_len, int B, int S, int H_idx,
+                             int D_idx, int L_cap, int max_kv_len, float* scores, void* stream) {
+  if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
+  if (L_cap < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "L_cap=%d must be >= 1", L_cap);
+  if (max_kv_len < 0 || max_kv_len > L_cap)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
+  if (idx_dtype != DSA_BF16 && idx_dtype != DSA_F16)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype %s not in {BF16, F16}", dtype_name(idx_dtype));
+  if (H_idx < 1 || H_idx > 16) return fail(DSA_ERR_UNSUPPORTED, "H_idx=%d not in [1, 16]", H_idx);
+  if (D_idx != 32 && D_idx != 64 && D_idx != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "D_idx=%d not in {32, 64, 128}", D_idx);
+  if ((long long)B * S == 0 || max_kv_len == 0) return ok();
+  CHECK(check_ptr(q_idx, "q_idx"));
+  CHECK(check_ptr(w_idx, "w_idx"));
+  CHECK(check_ptr(key_state, "key_state"));
+  CHECK(check_ptr(kv_len, "kv_len"));
+  CHECK(check_ptr(scores, "scores"));
+  dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, max_kv_len);
+  l.q_idx = q_idx; l.w_idx = w_idx; l.key_state = key_state; l.kv_len = kv_len;
+  l.scores = scores; l.H = H_idx; l.L_cap = L_cap; l.bf16 = idx_dtype == DSA_BF16;
+  (void)hipGetLastError();
+  dsa::launch_indexer(l, (hipStream_t)stream);
+  return hip_result("dsa_indexer_score");
+}
+
+size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k) {
+  if (B <= 0 || S <= 0 || L_cap < 1 || k < 1 || k > L_cap || L_cap > (1 << 24)) return 0;
+  return dsa::plan_topk(B, S, L_cap, k).ws_bytes;
+}
+
+dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, int L_cap,
+                    int max_kv_len, int k, int32_t* indices, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
+  if (L_cap < 1 || L_cap > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "L_cap=%d not in [1, 2^24]", L_cap);
+  if (k < 1 || k > L_cap) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d not in [1, L_cap=%d]", k, L_cap);
+  if (max_kv_len < 0 || max_kv_len > L_cap)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
+  if ((long long)B * S == 0) return ok();
+  CHECK(check_ptr(scores, "scores"));
+  CHECK(check_ptr(kv_len, "kv_len"));
+  CHECK(check_ptr(indices, "indices"));
+  dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, k);
+  if (p.ws_bytes > 0) {
+    if (workspace_bytes < p.ws_bytes)
+      return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                  workspace_bytes, p.ws_bytes);
+    CHECK(check_ptr(workspace, "workspace"));
+  }
+  (void)hipGetLastError();
+  dsa::launch_topk(p, scores, kv_len, S, L_cap, k, indices, workspace, (hipStream_t)stream);
+  return hip_result("dsa_topk");
+}
+
+size_t dsa_attention_workspace_bytes(const dsa_attention_args* args, int is_decode) {
+  if (validate_attention(args) != DSA_OK) return 0;
+  if ((long long)args->B * args->S == 0) return 0;
+  return dsa::attention_partials_bytes(make_attn(args, is_decode != 0));
+}
+
+dsa_status dsa_attention_decode(const dsa_attention_args* args, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return run_attention(args, workspace, workspace_bytes, stream, true);
+}
+
+dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run_attention(args, workspace, workspace_bytes, stream, false);
+}
+
+}  // extern "C"

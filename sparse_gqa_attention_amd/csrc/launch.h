@@ -1,0 +1,68 @@
+// Internal host interface between the C-ABI layer (dsa_api.cpp) and the
+// kernel translation units.  Plans depend only on host-known arguments, so
+// workspace queries and launches always agree.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// ---------------------------------------------------------------- indexer
+struct IndexerLaunch {
+  const void* q_idx;
+  const float* w_idx;
+  const void* key_state;
+  const int32_t* kv_len;
+  float* scores;
+  int B, S, H, D_idx, L_cap;
+  bool bf16;
+  int pairs;        // token pairs per wave (1 or 2)
+  int tok_blocks;   // grid.y
+  int keys_per_wg;  // keys per workgroup
+  int key_blocks;   // grid.x
+};
+IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len);
+void launch_indexer(const IndexerLaunch& a, hipStream_t st);
+
+// ---------------------------------------------------------------- top-k
+struct TopkPlan {
+  bool multi;          // several workgroups per row (few long rows)
+  int rows;            // B*S
+  int chunk;           // keys per workgroup (multi)
+  int chunks;          // workgroups per row (multi)
+  int cap;             // candidate capacity (entries)
+  int words;           // bitmap words per row (multi, global)
+  size_t ws_bytes;     // workspace the plan needs
+  size_t lds_bytes;    // dynamic LDS of the row kernel (single)
+};
+TopkPlan plan_topk(int B, int S, int L_cap, int k);
+void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, int S,
+                 int L_cap, int k, int32_t* indices, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
+
+struct AttnLaunch {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* indices;
+  const int32_t* kv_len;
+  void* out;
+  float* part;        // decode partials (nsplit > 1), else null
+  int q_dtype, kv_dtype, out_dtype;
+  int B, S, H_q, H_kv, D, L_cap, k;
+  float scale;
+  int nsplit;         // key splits per (row, KV head)
+  int keys_per_split;
+};
+// nsplit/keys_per_split for the decode form; prefill uses nsplit = 1.
+void plan_attention(AttnLaunch& a, bool decode);
+size_t attention_partials_bytes(const AttnLaunch& a);
+void launch_attention(const AttnLaunch& a, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,150 @@
+"""The C-ABI library loads, exports every symbol include/dsa.h declares, and
+rejects invalid calls on the host before any device work (CPU only).
+
+Every call here fails validation, so no pointer is ever dereferenced and no
+kernel is launched; the fake addresses are never touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIBPATH = os.path.join(ROOT, "sparse_gqa_attention_amd", "libdsa.so")
+
+A16 = 0x100000          # a 16-byte-aligned fake address (never dereferenced)
+MIS = 0x100004          # misaligned fake address
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not os.path.exists(LIBPATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import sparse_gqa_attention_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_library_agree(dsa):
+    names = declared_functions()
+    assert len(names) == 8
+    lib = ctypes.CDLL(LIBPATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+    assert sorted(dsa.EXPORTS) == names
+    version = int(re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert dsa.dsa_abi_version() == version
+
+
+def _status(name):
+    return {"DSA_OK": 0, "INVALID": 1, "UNSUPPORTED": 2, "MISALIGNED": 3, "WS": 4}[name]
+
+
+def test_indexer_validation(dsa):
+    L = dsa.LIB
+    args = dict(q=A16, w=A16, ks=A16, dt=2, kv=A16, B=1, S=8, H=16, Di=64, Lc=4096, mx=4096, sc=A16)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dsa_indexer_score(a["q"], a["w"], a["ks"], a["dt"], a["kv"], a["B"], a["S"],
+                                   a["H"], a["Di"], a["Lc"], a["mx"], a["sc"], None)
+    assert call(H=17) == _status("UNSUPPORTED")
+    assert call(H=0) == _status("UNSUPPORTED")
+    assert call(Di=48) == _status("UNSUPPORTED")
+    assert call(dt=0) == _status("UNSUPPORTED")
+    assert "BF16" in dsa.dsa_last_error()
+    assert call(dt=3) == _status("UNSUPPORTED")
+    assert call(mx=4097) == _status("INVALID")
+    assert call(B=-1) == _status("INVALID")
+    assert call(q=None) == _status("INVALID")
+    assert "q_idx" in dsa.dsa_last_error()
+    assert call(ks=MIS) == _status("MISALIGNED")
+    assert call(sc=MIS) == _status("MISALIGNED")
+    # empty inputs are a no-op that touches nothing
+    assert call(B=0, q=None, w=None, ks=None, kv=None, sc=None) == 0
+    assert call(S=0, q=None) == 0
+    assert call(mx=0, q=None) == 0
+
+
+def test_topk_validation(dsa):
+    L = dsa.LIB
+    need = L.dsa_topk_workspace_bytes(1, 8, 32768, 2048)
+    assert need > 0                                      # few long rows: multi-workgroup plan
+    assert L.dsa_topk_workspace_bytes(1, 2048, 131072, 2048) == 0   # one workgroup per row
+    assert L.dsa_topk_workspace_bytes(1, 8, 32768, 2048) == need    # deterministic
+
+    def call(k=2048, Lc=32768, mx=32768, ws=A16, wsb=None, sc=A16, B=1, S=8, idx=A16):
+        return L.dsa_topk(sc, A16, B, S, Lc, mx, k, idx, ws, need if wsb is None else wsb, None)
+    assert call(k=0) == _status("INVALID")
+    assert call(k=32769) == _status("INVALID")
+    assert call(mx=40000) == _status("INVALID")
+    assert call(Lc=(1 << 24) + 1, mx=0) == _status("UNSUPPORTED")
+    assert call(wsb=need - 1) == _status("WS")
+    assert "needed" in dsa.dsa_last_error()
+    assert call(ws=None) == _status("INVALID")
+    assert call(ws=MIS) == _status("MISALIGNED")
+    assert call(sc=None) == _status("INVALID")
+    assert call(idx=MIS) == _status("MISALIGNED")
+    assert call(B=0, sc=None, idx=None, ws=None) == 0
+
+
+def _attn(dsa, **kw):
+    a = dsa.dsa.AttentionArgs()
+    base = dict(q=A16, q_dtype=2, k_cache=A16, v_cache=A16, kv_dtype=1, k_scale=None,
+                v_scale=None, indices=A16, k=2048, kv_len=A16, B=1, S=8, H_q=24, H_kv=2,
+                D=128, L_cap=32768, max_kv_len=32768, softmax_scale=0.0, out=A16, out_dtype=2)
+    base.update(kw)
+    for f, v in base.items():
+        setattr(a, f, v)
+    return a
+
+
+def test_attention_validation(dsa):
+    L = dsa.LIB
+    call = lambda a, ws=A16, wsb=1 << 30: L.dsa_attention_decode(ctypes.byref(a), ws, wsb, None)
+    bad = [
+        (dict(H_q=25), "INVALID"), (dict(H_kv=0), "INVALID"),
+        (dict(H_q=34, H_kv=2), "UNSUPPORTED"),           # ratio 17
+        (dict(D=96), "UNSUPPORTED"),
+        (dict(q_dtype=0), "UNSUPPORTED"),                 # F32 query with F16 cache
+        (dict(kv_dtype=0), "UNSUPPORTED"),
+        (dict(out_dtype=3), "UNSUPPORTED"),
+        (dict(kv_dtype=3), "INVALID"),                    # INT8 without scales
+        (dict(k_scale=A16, v_scale=A16), "INVALID"),      # scales with a float cache
+        (dict(k=-1), "INVALID"), (dict(max_kv_len=40000), "INVALID"),
+        (dict(softmax_scale=float("nan")), "INVALID"),
+        (dict(q=MIS), "MISALIGNED"), (dict(out=None), "INVALID"),
+        (dict(kv_dtype=3, k_scale=A16, v_scale=MIS), "MISALIGNED"),
+    ]
+    for kw, want in bad:
+        assert call(_attn(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
+    a = _attn(dsa)
+    need = L.dsa_attention_workspace_bytes(ctypes.byref(a), 1)
+    assert need > 0
+    assert L.dsa_attention_workspace_bytes(ctypes.byref(a), 0) == 0   # prefill: no workspace
+    assert call(a, wsb=need - 1) == _status("WS")
+    assert call(a, ws=None, wsb=need) == _status("INVALID")
+    assert call(_attn(dsa, B=0, q=None, out=None)) == 0
+
+
+def test_error_text_is_thread_local_and_cleared(dsa):
+    import threading
+    L = dsa.LIB
+    L.dsa_topk(None, None, 1, 1, 16, 16, 0, None, None, 0, None)
+    msg = dsa.dsa_last_error()
+    assert "k=0" in msg
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(dsa.dsa_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert L.dsa_topk(None, None, 0, 1, 16, 16, 4, None, None, 0, None) == 0
+    assert dsa.dsa_last_error() == ""

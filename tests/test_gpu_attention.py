@@ -1,0 +1,151 @@
+"""Sparse GQA attention on the GPU vs the FP64 oracle.
+
+Gate: relative RMSE <= 1e-3 and max |error| <= 4e-3 against the oracle
+rounded once to the output dtype; FP32 outputs must also reach 1e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_synth import INT8_DECODE_64K, SPEC_DECODE_32K, make_inputs, scaled, torch_dtype
+from gpu_util import DEV, dsa, run_attention, say, upload  # noqa: F401
+from parity import assert_output_close, output_errors
+
+pytestmark = pytest.mark.gpu
+
+
+def random_selection(rng, kv_len, S, k, L):
+    """Sorted random subsets of [0, pos] per row, -1 padded (a valid top-k output)."""
+    B = len(kv_len)
+    idx = np.full((B, S, k), -1, dtype=np.int32)
+    for b in range(B):
+        for s in range(S):
+            pos = kv_len[b] - S + s
+            n = max(0, min(k, pos + 1))
+            if n:
+                idx[b, s, :n] = np.sort(rng.choice(pos + 1, size=n, replace=False))
+    return torch.from_numpy(idx)
+
+
+# (q, kv, out, D, H_q, H_kv)
+COMBOS = [
+    ("f32", "f32", "f32", 64, 4, 1),
+    ("f32", "f32", "f32", 128, 8, 2),
+    ("bf16", "f16", "bf16", 128, 24, 2),
+    ("bf16", "bf16", "bf16", 128, 24, 2),
+    ("bf16", "i8", "bf16", 128, 48, 8),
+    ("f16", "f16", "f16", 64, 16, 4),
+    ("f16", "bf16", "f32", 128, 6, 6),
+    ("f16", "i8", "f16", 64, 16, 1),
+    ("bf16", "f16", "f32", 64, 12, 2),
+    ("bf16", "i8", "f32", 64, 10, 2),
+]
+
+
+def _run_case(dsa, combo, B, S, L, k, kv_len, decode, seed):
+    qd, kd, od, D, H_q, H_kv = combo
+    w = scaled(SPEC_DECODE_32K, B=B, S=S, L=L, H_q=H_q, H_kv=H_kv, D=D, q_dtype=qd,
+               kv_dtype=kd, out_dtype=od, k=k, H_idx=None, D_idx=None, seed=seed)
+    x = make_inputs(w, kv_len=kv_len)
+    idx = random_selection(np.random.default_rng(seed), x["kv_len"].tolist(), S, k, L)
+    g = upload(x)
+    out = run_attention(dsa, g, idx.to(DEV), torch_dtype(od), decode=decode)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], idx, x["kv_len"].tolist(),
+                                  k_scale=x["k_scale"], v_scale=x["v_scale"])
+    rel, mx = assert_output_close(out, ref, od, what=f"{combo} decode={decode}")
+    if od == "f32":
+        assert rel <= 1e-5, f"{combo}: FP32 output rel RMSE {rel:.2e}"
+    say(f"attention {combo} B={B} S={S} L={L} k={k} decode={decode}: rel={rel:.2e} max={mx:.2e}")
+    return out
+
+
+@pytest.mark.parametrize("decode", [True, False], ids=["decode", "prefill"])
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(map(str, c)))
+def test_attention_dtype_combos(dsa, combo, decode):
+    _run_case(dsa, combo, B=2, S=3, L=600, k=150, kv_len=[600, 421], decode=decode, seed=31)
+
+
+@pytest.mark.parametrize("decode", [True, False], ids=["decode", "prefill"])
+def test_attention_many_splits_and_short_rows(dsa, decode):
+    combo = ("bf16", "f16", "bf16", 128, 24, 2)
+    _run_case(dsa, combo, B=3, S=8, L=3000, k=1000, kv_len=[3000, 900, 40], decode=decode, seed=32)
+
+
+def test_attention_rising_max_with_huge_value_scale(dsa):
+    """Pages' worked example: logits 0 then 88 in a later tile/split, V scale 2^120."""
+    L, k, D = 200, 160, 64
+    q = torch.zeros((1, 1, 1, D), dtype=torch.bfloat16)
+    q[0, 0, 0, 0] = 1.0
+    kc = torch.zeros((1, L, 1, D), dtype=torch.int8)
+    vc = torch.zeros((1, L, 1, D), dtype=torch.int8)
+    kc[0, 150, 0, 0] = 88
+    vc[0, 0, 0, :] = 1
+    ks = torch.ones((1, L, 1), dtype=torch.float32)
+    vs = torch.full((1, L, 1), 2.0 ** 120, dtype=torch.float32)
+    want = 2.0 ** 120 * math.exp(-88) / (1 + math.exp(-88))
+    for order in ("low-first", "high-first"):
+        idx = torch.full((1, 1, k), -1, dtype=torch.int32)
+        a, b = (0, 150) if order == "low-first" else (150, 0)
+        idx[0, 0, 0], idx[0, 0, 140] = a, b        # different tiles and key splits
+        g = {"q": q.to(DEV), "k_cache": kc.to(DEV), "v_cache": vc.to(DEV),
+             "k_scale": ks.to(DEV), "v_scale": vs.to(DEV), "kv_len": torch.tensor([L], dtype=torch.int32, device=DEV)}
+        for decode in (True, False):
+            for od in (torch.bfloat16, torch.float32):
+                out = run_attention(dsa, g, idx.to(DEV), od, decode=decode, scale=1.0)
+                torch.cuda.synchronize()
+                got = out.float().cpu().numpy().ravel()
+                tol = 2 ** -8 if od == torch.bfloat16 else 1e-5
+                assert np.all(np.abs(got / want - 1) < tol), (order, decode, od, got[:4], want)
+
+
+def test_attention_rows_without_valid_keys_are_zero(dsa):
+    combo = ("bf16", "f16", "bf16", 128, 24, 2)
+    qd, kd, od, D, H_q, H_kv = combo
+    S, L, k = 4, 500, 64
+    w = scaled(SPEC_DECODE_32K, B=2, S=S, L=L, k=k, H_idx=None, D_idx=None, seed=33)
+    x = make_inputs(w, kv_len=[500, 2])          # b=1: rows s=0,1 have pos < 0
+    idx = torch.full((2, S, k), -1, dtype=torch.int32)
+    idx[0, 0, :3] = torch.tensor([499, 600, 497])   # all beyond pos(0,0)=496 or L
+    idx[1, 2, :2] = torch.tensor([0, 1])            # pos(1,2) = 0: only key 0 valid
+    g = upload(x)
+    for decode in (True, False):
+        out = run_attention(dsa, g, idx.to(DEV), torch.bfloat16, decode=decode).float().cpu()
+        assert torch.all(out[0, 0] == 0) and torch.all(out[0, 1] == 0)
+        assert torch.all(out[1, 0] == 0) and torch.all(out[1, 1] == 0)
+        ref = oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], idx, [500, 2])
+        assert_output_close(out, ref, "bf16", what=f"masked decode={decode}")
+
+
+def test_attention_decode_is_deterministic_and_matches_prefill(dsa):
+    w = SPEC_DECODE_32K
+    x = make_inputs(w)
+    idx = random_selection(np.random.default_rng(34), x["kv_len"].tolist(), w.S, w.k, w.L).to(DEV)
+    g = upload(x)
+    a = run_attention(dsa, g, idx, torch.bfloat16, decode=True)
+    b = run_attention(dsa, g, idx, torch.bfloat16, decode=True)
+    c = run_attention(dsa, g, idx, torch.bfloat16, decode=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], idx.cpu(), x["kv_len"].tolist())
+    for out, name in ((a, "decode"), (c, "prefill")):
+        rel, mx = assert_output_close(out, ref, "bf16", what=name)
+        say(f"spec_decode_32k {name}: rel={rel:.2e} max={mx:.2e}")
+
+
+def test_attention_int8_dense_batch_sampled(dsa):
+    w = INT8_DECODE_64K
+    x = make_inputs(w)
+    g = upload(x)
+    out = run_attention(dsa, g, g["indices"], torch.bfloat16, decode=True)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (7, 0)]
+    ref = oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], x["indices"],
+                                  x["kv_len"].tolist(), k_scale=x["k_scale"],
+                                  v_scale=x["v_scale"], rows=rows)
+    for b, s in rows:
+        rel, mx = assert_output_close(out[b, s], ref[b, s], "bf16", what=f"int8 row {b}")
+        say(f"int8_batched_decode_64k row {b}: rel={rel:.2e} max={mx:.2e}")

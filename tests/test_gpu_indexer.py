@@ -1,0 +1,72 @@
+"""Indexer scores on the GPU vs the FP64 oracle: bit-exact (integer inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_synth import (SPEC_DECODE_32K, TINY_DECODE, DECODE_256K, PREFILL_128K,
+                       make_inputs, scaled)
+from gpu_util import dsa, first_mismatch, run_indexer, say, upload  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+# (B, S, H_idx, D_idx, L, kv_len, idx dtype)
+SMALL = [
+    (1, 1, 4, 32, 1024, None, "bf16"),
+    (1, 8, 16, 64, 3000, None, "bf16"),            # ragged key tail
+    (2, 20, 16, 64, 2500, [2500, 1800], "bf16"),   # two token pairs per wave, ragged kv_len
+    (2, 3, 7, 128, 777, [777, 500], "f16"),
+    (1, 9, 16, 32, 1500, None, "f16"),
+    (3, 8, 16, 64, 5000, [5000, 8, 4000], "bf16"),  # kv_len == S
+    (1, 40, 12, 64, 700, None, "bf16"),
+]
+
+
+def _check(g_scores, x, S, what):
+    kv_len = x["kv_len"].tolist()
+    ref = oracle.indexer_scores(x["q_idx"], x["w_idx"], x["key_state"], kv_len, S)
+    got = g_scores.cpu().double().numpy()
+    B, _, L = got.shape
+    for b in range(B):
+        for s in range(S):
+            pos = kv_len[b] - S + s
+            a, r = got[b, s, :pos + 1], ref[b, s, :pos + 1]
+            assert np.array_equal(a, r), f"{what} b={b} s={s}: {first_mismatch(a, r)}"
+        assert np.all(np.isnan(got[b, :, kv_len[b]:])), f"{what}: wrote past kv_len"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}S{c[1]}H{c[2]}D{c[3]}L{c[4]}{c[6]}")
+def test_indexer_small_exact(dsa, case):
+    B, S, H, Di, L, kv, dt = case
+    say(f"indexer small {case}")
+    w = scaled(SPEC_DECODE_32K, B=B, S=S, H_idx=H, D_idx=Di, L=L, H_q=2, H_kv=1, D=64,
+               idx_dtype=dt, seed=1000 + L)
+    x = make_inputs(w, kv_len=kv)
+    g = upload(x)
+    scores = run_indexer(dsa, g, L)
+    torch.cuda.synchronize()
+    _check(scores, x, S, str(case))
+
+
+@pytest.mark.parametrize("wl", [TINY_DECODE, SPEC_DECODE_32K, DECODE_256K], ids=lambda w: w.name)
+def test_indexer_full_size_all_rows(dsa, wl):
+    say(f"indexer full {wl.name}")
+    x = make_inputs(wl)
+    scores = run_indexer(dsa, upload(x), wl.L)
+    torch.cuda.synchronize()
+    _check(scores, x, wl.S, wl.name)
+
+
+def test_indexer_prefill_128k_sampled_rows(dsa):
+    wl = PREFILL_128K
+    say("indexer full prefill_128k (sampled rows)")
+    x = make_inputs(wl)
+    scores = run_indexer(dsa, upload(x), wl.L)
+    torch.cuda.synchronize()
+    rows = [0, 1, 15, 16, 511, 1024, 2046, 2047]
+    got = scores[0, rows].cpu().double().numpy()
+    for i, s in enumerate(rows):
+        pos = wl.L - wl.S + s
+        ref = oracle.indexer_scores_row(x["q_idx"][0, s], x["w_idx"][0, s], x["key_state"][0], pos)
+        a, r = got[i, :pos + 1], ref[:pos + 1]
+        assert np.array_equal(a, r), f"row {s}: {first_mismatch(a, r)}"

@@ -1,0 +1,99 @@
+"""Top-k on the GPU vs the oracle's full stable sort: indices bit-exact.
+
+Score matrices are generated on the CPU and uploaded, so the GPU kernel and
+the oracle read the same FP32 values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_synth import indexer_like_scores, integer_scores
+from gpu_util import DEV, dsa, first_mismatch, run_topk, say  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(dsa, scores_cpu, kv_len, k, rows=None, what=""):
+    B, S, L = scores_cpu.shape
+    say(f"topk {what} B={B} S={S} L={L} k={k} ws={dsa.dsa_topk_workspace_bytes(B, S, L, k)}")
+    g_scores = scores_cpu.to(DEV)
+    g_kv = torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    idx = run_topk(dsa, g_scores, g_kv, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    rows = [(b, s) for b in range(B) for s in range(S)] if rows is None else rows
+    for b, s in rows:
+        pos = kv_len[b] - S + s
+        want = oracle.topk_row(scores_cpu[b, s], pos, k)
+        assert np.array_equal(got[b, s], want), f"{what} row ({b},{s}): {first_mismatch(got[b, s], want)}"
+    return got
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+@pytest.mark.parametrize("B,S,L,k", [(1, 8, 32768, 2048), (1, 300, 5000, 512), (2, 4, 20000, 100),
+                                     (1, 1, 1024, 128), (1, 8, 262144, 2048)])
+def test_topk_normal_floats(dsa, B, S, L, k):
+    sc = torch.from_numpy(rng(L + k).standard_normal(size=(B, S, L)).astype(np.float32))
+    _check(dsa, sc, [L] * B, k, what="normal")
+
+
+@pytest.mark.parametrize("B,S,L,k", [(1, 8, 32768, 2048), (1, 200, 3000, 256), (1, 8, 70000, 1000)])
+def test_topk_heavy_ties(dsa, B, S, L, k):
+    _check(dsa, integer_scores(rng(7), (B, S, L), -20, 20), [L] * B, k, what="ints[-20,20]")
+    _check(dsa, integer_scores(rng(8), (B, S, L), -1, 1), [L] * B, k, what="ints[-1,1]")
+
+
+@pytest.mark.parametrize("B,S,L,k", [(1, 8, 32768, 2048), (1, 200, 3000, 256), (1, 3, 50000, 4096)])
+def test_topk_tie_storm_takes_lowest_indices(dsa, B, S, L, k):
+    got = _check(dsa, torch.full((B, S, L), 3.0), [L] * B, k, what="tie storm")
+    assert np.array_equal(got[0, 0], np.arange(k))
+
+
+def test_topk_narrow_bin_forces_deep_descent(dsa):
+    # All keys share their top 11 bits: the first bin holds every key, so
+    # both plans must descend through all three radix levels.
+    r = rng(9)
+    for (B, S, L, k) in [(1, 8, 40000, 2048), (1, 150, 9000, 700)]:
+        base = r.integers(0, 1 << 16, size=(B, S, L))
+        sc = torch.from_numpy((1.0 + base.astype(np.float64) * 2.0 ** -23).astype(np.float32))
+        _check(dsa, sc, [L] * B, k, what="narrow")
+
+
+def test_topk_short_rows_and_ragged_lengths(dsa):
+    r = rng(10)
+    _check(dsa, torch.from_numpy(r.standard_normal((1, 4, 100)).astype(np.float32)), [100], 128,
+           what="k > n")
+    sc = torch.from_numpy(r.standard_normal((3, 8, 40000)).astype(np.float32))
+    got = _check(dsa, sc, [40000, 20000, 5], 1000, what="ragged multi")
+    assert np.all(got[2, :3] == -1)        # pos < 0: nothing to select
+    sc = torch.from_numpy(r.standard_normal((3, 50, 4000)).astype(np.float32))
+    _check(dsa, sc, [4000, 2500, 60], 300, what="ragged row")
+
+
+def test_topk_ignores_poison_beyond_position(dsa):
+    r = rng(11)
+    B, S, L, k = 1, 8, 30000, 2048
+    sc = torch.from_numpy(r.standard_normal((B, S, L)).astype(np.float32))
+    kv = 20000
+    for s in range(S):                          # +inf beyond each row's position
+        sc[0, s, kv - S + s + 1:] = float("inf")
+    _check(dsa, sc, [kv], k, what="poison")
+
+
+def test_topk_signed_zero_and_minus_inf(dsa):
+    r = rng(12)
+    for (B, S, L, k) in [(1, 8, 20000, 3000), (1, 130, 2000, 600)]:
+        choice = r.integers(0, 4, size=(B, S, L))
+        vals = np.array([0.0, -0.0, -np.inf, 1.0], dtype=np.float32)
+        sc = torch.from_numpy(vals[choice])
+        _check(dsa, sc, [L] * B, k, what="zeros/-inf")
+
+
+def test_topk_prefill_128k_shape(dsa):
+    sc = indexer_like_scores(rng(13), (1, 2048, 131072))
+    _check(dsa, sc, [131072], 2048, rows=[(0, s) for s in (0, 1, 500, 1023, 1024, 2047)],
+           what="prefill_128k-shaped")
