@@ -1,0 +1,250 @@
+"""Benchmark of the dynamic sparse GQA attention hot path on one MI355X.
+
+One step = the whole hot path (indexer score -> top-k -> sparse attention)
+run once per "layer" over N distinct layer buffer sets whose total footprint
+exceeds 1 GiB, so that no layer's key-state or KV cache is still resident in
+the 256 MB Infinity Cache when it is read again.  The reported value is the
+time per layer (microseconds): step time / N.
+
+Inputs are seeded and synthetic and already resident in HBM when the timed
+region starts.  HIP events on the launch stream time the whole region and,
+inside it, every call of the dominant stage; that stage's algorithmic bytes
+per call divided by its average duration is the roofline `achieved` figure.
+The CPU baseline times the FP64 oracle on the host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
+HBM_PEAK_GBPS = 8000.0
+ELT = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="spec_decode_32k")
+    p.add_argument("--layers", type=int, default=0, help="layer buffer sets (0: >= 1 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+def stage_bytes(w, kv_len):
+    """Bytes each stage's contract must move for one layer (each byte once)."""
+    B, S, k = w.B, w.S, w.k
+    rows_valid = []
+    for b in range(B):
+        for s in range(S):
+            pos = kv_len[b] - S + s
+            rows_valid.append(max(0, min(k, pos + 1)))
+    out = {}
+    if w.has_indexer:
+        key_state = sum(kv_len) * w.D_idx * ELT[w.idx_dtype]
+        q_idx = B * S * w.H_idx * w.D_idx * ELT[w.idx_dtype] + B * S * w.H_idx * 4
+        scores_w = B * S * w.L * 4
+        out["indexer"] = key_state + q_idx + scores_w
+        scores_r = sum(max(0, kv_len[b] - S + s + 1) for b in range(B) for s in range(S)) * 4
+        out["topk"] = scores_r + B * S * k * 4
+    row_bytes = w.H_kv * w.D * ELT[w.kv_dtype] * 2
+    if w.kv_dtype == "i8":
+        row_bytes += w.H_kv * 4 * 2
+    gathered = sum(rows_valid) * row_bytes
+    q = B * S * w.H_q * w.D * ELT[w.q_dtype]
+    o = B * S * w.H_q * w.D * ELT[w.out_dtype]
+    out["attention"] = gathered + q + o + B * S * k * 4
+    # Whole path without the score round trip (an artefact of the 4-call ABI).
+    path = out["attention"]
+    if w.has_indexer:
+        path += key_state + q_idx
+    out["path"] = path
+    return out
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, x, seconds):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    kv_len = x["kv_len"].tolist()
+    rows = [(b, s) for b in range(w.B) for s in range(w.S)]
+    if len(rows) > 16:
+        rows = rows[:: max(1, len(rows) // 16)][:16]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        idx = np.full((w.B, w.S, w.k), -1, dtype=np.int64)
+        for b, s in rows:
+            pos = kv_len[b] - w.S + s
+            if w.has_indexer:
+                sc = oracle.indexer_scores_row(x["q_idx"][b, s], x["w_idx"][b, s],
+                                               x["key_state"][b], pos)
+                idx[b, s] = oracle.topk_row(sc, pos, w.k)
+            else:
+                idx[b, s] = x["indices"][b, s].numpy()
+        oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], idx, kv_len,
+                                k_scale=x["k_scale"], v_scale=x["v_scale"], rows=rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    per_row = el / (reps * len(rows))
+    us_per_layer = per_row * w.B * w.S * 1e6
+    return {"value": round(us_per_layer, 1), "unit": "us/layer", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x {len(rows)} of the {w.B * w.S} query rows of one {w.name} layer "
+                      f"(FP64 scores, full-sort top-k, dense masked attention), scaled to "
+                      f"all {w.B * w.S} rows; {el:.1f} s of host time"}
+
+
+# ------------------------------------------------------------------ GPU bench
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs the "
+              f"hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_gqa_attention_amd as dsa
+    from dsa_synth import BY_NAME, make_inputs
+
+    w = BY_NAME[args.workload]
+    decode = w.name != "prefill_128k"
+    x = make_inputs(w)
+    kv_len = x["kv_len"].tolist()
+    dev = torch.device("cuda:0")
+    layer_bytes = sum(v.numel() * v.element_size() for v in x.values()
+                      if isinstance(v, torch.Tensor))
+    n_layers = args.layers or max(2, -(-(1 << 30) // layer_bytes))
+    layers = []
+    for _ in range(n_layers):
+        layers.append({kk: (v.to(dev) if isinstance(v, torch.Tensor) else v) for kk, v in x.items()})
+    B, S, L = w.B, w.S, w.L
+    scores = torch.empty((B, S, L), dtype=torch.float32, device=dev) if w.has_indexer else None
+    idx = torch.empty((B, S, w.k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, S, w.H_q, w.D), dtype={"f32": torch.float32, "f16": torch.float16,
+                                                  "bf16": torch.bfloat16}[w.out_dtype], device=dev)
+    topk_ws = None
+    if w.has_indexer:
+        nb = dsa.dsa_topk_workspace_bytes(B, S, L, w.k)
+        topk_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    g0 = layers[0]
+    a0 = dsa.attention_args(g0["q"], g0["k_cache"], g0["v_cache"], idx, g0["kv_len"], out,
+                            g0["k_scale"], g0["v_scale"])
+    attn_ws = torch.empty(max(dsa.dsa_attention_workspace_bytes(a0, decode), 16),
+                          dtype=torch.uint8, device=dev)
+    attn = dsa.dsa_attention_decode if decode else dsa.dsa_attention_prefill
+
+    def stage(name, g):
+        if name == "indexer":
+            dsa.dsa_indexer_score(g["q_idx"], g["w_idx"], g["key_state"], g["kv_len"], scores)
+        elif name == "topk":
+            dsa.dsa_topk(scores, g["kv_len"], w.k, idx, workspace=topk_ws)
+        else:
+            ind = idx if w.has_indexer else g["indices"]
+            attn(g["q"], g["k_cache"], g["v_cache"], ind, g["kv_len"], out,
+                 k_scale=g["k_scale"], v_scale=g["v_scale"], workspace=attn_ws)
+
+    stages = (["indexer", "topk"] if w.has_indexer else []) + ["attention"]
+
+    def layer_pass(g, ev=None, dom=None):
+        for st in stages:
+            if st == dom:
+                ev[0].record()
+                stage(st, g)
+                ev[1].record()
+            else:
+                stage(st, g)
+
+    # Calibration: per-stage durations (outside the timed region) pick the
+    # dominant stage.
+    for g in layers:
+        layer_pass(g)
+    torch.cuda.synchronize()
+    calib = {}
+    for st in stages:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            for g in layers:
+                stage(st, g)
+        e1.record()
+        torch.cuda.synchronize()
+        calib[st] = e0.elapsed_time(e1) * 1e3 / (reps * n_layers)
+    dominant = max(calib, key=calib.get)
+
+    for _ in range(args.warmup):
+        for g in layers:
+            layer_pass(g)
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    K = args.steps
+    dom_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K * n_layers)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    i = 0
+    for _ in range(K):
+        for g in layers:
+            layer_pass(g, dom_events[i], dominant)
+            i += 1
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / K
+    us_per_layer = ms_total * 1e3 / (K * n_layers)
+    dom_us = sum(a.elapsed_time(b) for a, b in dom_events) * 1e3 / len(dom_events)
+
+    sb = stage_bytes(w, kv_len)
+    dom_gbps = sb[dominant] / (dom_us * 1e-6) / 1e9
+    path_gbps = sb["path"] / (us_per_layer * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(us_per_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16", "i8": "i8", "f32": "f32"}[w.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "S": S, "L": L, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "D": w.D, "k": w.k, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
+                   "out_dtype": w.out_dtype, "indexer": (f"{w.H_idx}x{w.D_idx}"
+                                                         if w.has_indexer else None),
+                   "layers_per_step": n_layers, "attention_form": "decode" if decode else "prefill"},
+        "tokens_per_s": round(B * S / (us_per_layer * 1e-6), 1),
+        "path_hbm_gbps": round(path_gbps, 1),
+        "stage_us": {k2: round(v, 3) for k2, v in calib.items()},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "stage": dominant, "us_per_call": round(dom_us, 3),
+                     "bytes_per_call": sb[dominant]},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,7 +94,7 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx,
  *   workspace: at least dsa_topk_workspace_bytes(B, S, L_cap, k) bytes of
  *   device memory (may be NULL when that is 0); contents on entry are
  *   ignored, contents on return are unspecified.
- * Supported: 1 <= k <= L_cap <= 2^24.
+ * Supported: k >= 1 (k may exceed L_cap: the tail is -1), L_cap <= 2^24.
  */
 size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k);
 dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S,

@@ -328,33 +328,59 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   }
 }
 
-// Combine the key splits of one (row, head): fixed order, exact rescale.
+// Combine the key splits of one (row, head) in a fixed order (deterministic).
+// Thread t owns a float4 column chunk (t % (D/4)) and the splits
+// t / (D/4), + G, + 2G, ... (G = 256 / (D/4)); loads of all its splits are
+// independent and in flight together; the G partial sums meet in LDS.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part, int rows_h,
-                                                        int nsplit, void* out, int out_dtype) {
-  const int hrow = blockIdx.x;
-  const int l = lane_id();
-  const float* pml = part;
-  const float* po = part + (size_t)2 * rows_h * nsplit;
-  float m = -INFINITY, lsum = 0.0f;
-  if (l < nsplit) {
-    m = pml[((size_t)hrow * nsplit + l) * 2 + 0];
-    lsum = pml[((size_t)hrow * nsplit + l) * 2 + 1];
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
+    const float* __restrict__ part, int rows_h, int nsplit, void* out, int out_dtype) {
+  constexpr int C4 = D / 4;                 // float4 chunks per row
+  constexpr int G = kMergeThreads / C4;     // split groups
+  __shared__ float mm[64], ff[64], ll[64];
+  __shared__ __attribute__((aligned(16))) float4 acc[G][C4];
+  const int hrow = blockIdx.x, t = threadIdx.x;
+  const float* pml = part + (size_t)hrow * nsplit * 2;
+  const float4* po = (const float4*)(part + (size_t)2 * rows_h * nsplit) + (size_t)hrow * nsplit * C4;
+  if (t < nsplit) { mm[t] = pml[2 * t]; ll[t] = pml[2 * t + 1]; }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mm[sp]);
+  if (t < nsplit) ff[t] = (M == -INFINITY || mm[t] == -INFINITY) ? 0.0f : exp_keep_subnormal(mm[t] - M);
+  __syncthreads();
+  const int c = t % C4, g = t / C4;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sp = g;
+  for (; sp + G < nsplit; sp += 2 * G) {
+    const float4 a = po[(size_t)sp * C4 + c];
+    const float4 b = po[(size_t)(sp + G) * C4 + c];
+    const float fa = ff[sp], fb = ff[sp + G];
+    o.x += fa * a.x; o.y += fa * a.y; o.z += fa * a.z; o.w += fa * a.w;
+    o.x += fb * b.x; o.y += fb * b.y; o.z += fb * b.z; o.w += fb * b.w;
   }
-  float M = m;
+  if (sp < nsplit) {
+    const float4 a = po[(size_t)sp * C4 + c];
+    const float fa = ff[sp];
+    o.x += fa * a.x; o.y += fa * a.y; o.z += fa * a.z; o.w += fa * a.w;
+  }
+  acc[g][c] = o;
+  __syncthreads();
+  if (t < C4) {
+    float L = 0.0f;
+    for (int q = 0; q < nsplit; ++q) L += ff[q] * ll[q];
+    float4 r = acc[0][t];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-  const float f = (M == -INFINITY || m == -INFINITY) ? 0.0f : exp_keep_subnormal(m - M);
-  float L = f * lsum;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, kWave);
-  for (int d = l; d < D; d += kWave) {
-    float O = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float fs = __shfl(f, sp, kWave);
-      O += fs * po[((size_t)hrow * nsplit + sp) * D + d];
+    for (int q = 1; q < G; ++q) {
+      const float4 v = acc[q][t];
+      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }
-    store_out(out, (size_t)hrow * D + d, L > 0.0f ? O / L : 0.0f, out_dtype);
+    const size_t base = (size_t)hrow * D + 4 * t;
+    store_out(out, base + 0, L > 0.0f ? r.x / L : 0.0f, out_dtype);
+    store_out(out, base + 1, L > 0.0f ? r.y / L : 0.0f, out_dtype);
+    store_out(out, base + 2, L > 0.0f ? r.z / L : 0.0f, out_dtype);
+    store_out(out, base + 3, L > 0.0f ? r.w / L : 0.0f, out_dtype);
   }
 }
 
@@ -370,7 +396,7 @@ void launch_cfg(const AttnLaunch& a, hipStream_t st) {
   dim3 grid(a.nsplit, a.H_kv, a.B * a.S);
   hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV>), grid, dim3(kAttnThreads), 0, st, p);
   if (a.nsplit > 1) {
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.B * a.S * a.H_q), dim3(64), 0, st,
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.B * a.S * a.H_q), dim3(kMergeThreads), 0, st,
                        (const float*)a.part, a.B * a.S * a.H_q, a.nsplit, a.out, a.out_dtype);
   }
 }

@@ -168,7 +168,7 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* 
 }
 
 size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k) {
-  if (B <= 0 || S <= 0 || L_cap < 1 || k < 1 || k > L_cap || L_cap > (1 << 24)) return 0;
+  if (B <= 0 || S <= 0 || L_cap < 1 || k < 1 || L_cap > (1 << 24)) return 0;
   return dsa::plan_topk(B, S, L_cap, k).ws_bytes;
 }
 
@@ -178,7 +178,7 @@ dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, in
   if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
   if (L_cap < 1 || L_cap > (1 << 24))
     return fail(DSA_ERR_UNSUPPORTED, "L_cap=%d not in [1, 2^24]", L_cap);
-  if (k < 1 || k > L_cap) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d not in [1, L_cap=%d]", k, L_cap);
+  if (k < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
   if (max_kv_len < 0 || max_kv_len > L_cap)
     return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
   if ((long long)B * S == 0) return ok();

@@ -38,6 +38,14 @@ __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
 __device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Store that is coherent at device scope on its own (written through the
+// per-XCD L2), so that publishing it to other workgroups needs no L2
+// writeback -- only a wait for the store to complete (wait_vmem).
+__device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory operation of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------------------ conversions
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -102,13 +110,16 @@ __device__ __forceinline__ uint32_t wave_prefix_count(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive wave scan on DPP lane moves: four row_shr steps scan each
+// 16-lane row, then row_bcast:15 and row_bcast:31 carry the row totals.
+// Lanes without a source read `old` = 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, kWave);
-    if (l >= off) v += t;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 

@@ -28,14 +28,11 @@ void launch_indexer(const IndexerLaunch& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
 struct TopkPlan {
-  bool multi;          // several workgroups per row (few long rows)
+  int kind;            // resident / streaming (512 or 1024 threads) / multi
   int rows;            // B*S
-  int chunk;           // keys per workgroup (multi)
-  int chunks;          // workgroups per row (multi)
-  int cap;             // candidate capacity (entries)
-  int words;           // bitmap words per row (multi, global)
+  int chunk;           // keys per chunk workgroup (multi)
+  int chunks;          // chunk workgroups per row (multi)
   size_t ws_bytes;     // workspace the plan needs
-  size_t lds_bytes;    // dynamic LDS of the row kernel (single)
 };
 TopkPlan plan_topk(int B, int S, int L_cap, int k);
 void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, int S,

@@ -1,27 +1,41 @@
 // Per-query top-k with lowest-index tie-break (ORT PR #33802 "Optimize ...
 // for SM12x and 256K context", Summary item 2: radix histograms per key
-// chunk, a merge across up to 64+ chunks and an emit of the indices).
+// chunk, a merge across up to 64+ chunks and a final emit of the indices).
 //
-// Exact selection, any FP32 input.  Scores map to order-preserving u32 keys
-// (score_key).  A radix descent over the key bits -- levels of 11, 11 and 10
-// bits -- finds the bin holding the k-th largest key.  Keys above that bin
-// are certainly selected and go straight into a selection bitmap; keys in the
-// bin are collected as candidates (or, once the bin is a single key value,
-// marked in a tie bitmap).  The exact threshold T among the candidates is
-// found in LDS.  Finally both bitmaps are scanned in index order: the first
-// k - #{key > T} tie bits are kept (lowest indices win the tie) and the set
-// bits are written out in ascending order.  Bitmap words are produced with
-// wave ballots, one store per word, so ordering needs no sort at all.
+// Exact for any FP32 input.  Scores map to order-preserving u32 keys
+// (score_key); selection works on keys only.
 //
-// Two plans share these routines:
-//  * row plan -- one 1024-thread workgroup per row, everything in LDS; for
-//    many long rows (prefill: 2048 rows of 131072 keys).
-//  * multi plan -- a few long rows (speculative decode: 8 rows of up to
-//    262144 keys) spread over many workgroups per row.  K1 builds per-chunk
-//    histograms and merges them with device atomics; the last workgroup of a
-//    row to arrive picks the bin.  K2 fills the row's bitmaps and candidate
-//    list; its last arriver finishes the selection and emits.  No workgroup
-//    ever waits for another one.
+// 1. Threshold estimate.  A sample of the row (all of it when the row has at
+//    most 8192 keys, else 32 blocks of 256 consecutive keys spread over the
+//    row) goes through two radix levels (the top 11 + 11 key bits) to the
+//    bin of the key of rank r = ceil(1.2e + 4 sqrt(e)) + 8, where e = k *
+//    sample / n is the expected sample rank of the k-th largest key.  The
+//    bin's lower edge T_lo is at or below that key; every key >= T_lo is a
+//    candidate (about 1.2k + 4 sqrt(e) n/sample keys).
+// 2. Collection.  One pass over the row appends the candidates to a list.
+// 3. Exact selection on the list, in LDS: radix select of the k-th largest
+//    key T; when only some of the keys equal to T fit, the lowest indices
+//    win: one wave ranks up to 64 tied indices directly, more go through a
+//    radix select on the complemented index.  An entry is kept iff key > T
+//    or (key == T and index <= cut).  Exactly k entries.
+// 4. Ordered emission: the kept indices are set in an LDS bitmap one index
+//    segment at a time and written in ascending order by a block scan.
+// When the list holds fewer than k keys, overflows, or k itself exceeds its
+// capacity, an exact fallback selects from the whole row (three radix
+// passes) and emits from selection/tie bitmaps, carrying the tie count
+// across segments.  Every path computes the same, exact result.
+//
+// Plans (host-chosen from B*S and L_cap):
+//  * resident  -- few rows of <= 32768 keys (speculative decode at 32K): one
+//    1024-thread workgroup per row loads the row once into LDS (128 KB of
+//    keys) and does everything there.
+//  * streaming -- many rows (prefill: 2048 rows of 131072 keys): one
+//    512-thread workgroup per row reading the row ~1.06 times.
+//  * multi     -- few rows longer than 32768 keys (decode at 256K): KA (one
+//    workgroup per row) computes T_lo and resets the row's list counter, KB
+//    (many workgroups per row) collects with one list reservation per
+//    workgroup, KC (one workgroup per row) selects and emits.  Kernel
+//    boundaries order the three.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -30,17 +44,24 @@ namespace dsa {
 namespace {
 
 constexpr int kBins = 2048;
-constexpr int kRowThreads = 1024;
+constexpr int kSample = 8192;          // sampled keys (rows longer than this)
+constexpr int kSampleBlock = 256;      // consecutive keys per sample block
+constexpr int kSegWords = 2048;        // bitmap segment: 65536 indices
+constexpr int kSegBits = kSegWords * 32;
+constexpr int kResKeys = 32768;        // longest row the resident plan holds
+constexpr int kResCap = 4096;
+constexpr int kRowCap = 4096;
+constexpr int kMultiCap = 8192;
 constexpr int kChunkThreads = 256;
-constexpr int kRowCap = 4096;      // candidate capacity of the row plan
-constexpr int kMultiCap = 8192;    // candidate capacity per row of the multi plan
+constexpr int kChunkKeysPerThread = 8;
+
+enum PlanKind { kPlanStream512 = 0, kPlanResident = 1, kPlanMulti = 2 };
 
 // Radix levels: key bits [31:21], [20:10], [9:0].
 __device__ __forceinline__ int lvl_shift(int lvl) { return lvl == 0 ? 21 : (lvl == 1 ? 10 : 0); }
 __device__ __forceinline__ uint32_t lvl_digit(uint32_t key, int lvl) {
   return lvl == 0 ? (key >> 21) : (lvl == 1 ? ((key >> 10) & 0x7FFu) : (key & 0x3FFu));
 }
-// Does `key` share the bits already fixed (all bits above level lvl)?
 __device__ __forceinline__ bool lvl_match(uint32_t key, uint32_t prefix, int lvl) {
   return lvl == 0 ? true : (((key ^ prefix) >> (lvl == 1 ? 21 : 10)) == 0u);
 }
@@ -51,14 +72,36 @@ __device__ __forceinline__ int row_count(const int32_t* kv_len, int row, int S, 
   return n < 0 ? 0 : (n > L_cap ? L_cap : n);
 }
 
-// Find the bin holding the need-th largest key of a 2048-bin histogram.
-// Writes {bin, count of keys in higher bins} to out[0..1].  Block-wide.
+// Sample rank of the threshold and the row position of sample element i.
+__device__ __forceinline__ int sample_rank(int k, int n) {
+  const float e = (float)k * (float)kSample / (float)n;
+  const int r = (int)ceilf(1.2f * e + 4.0f * sqrtf(e)) + 8;
+  return r < kSample ? r : kSample;
+}
+__device__ __forceinline__ int sample_pos(int i, int n) {
+  constexpr int NB = kSample / kSampleBlock;
+  const int blk = i / kSampleBlock;
+  return (int)((long long)blk * (n - kSampleBlock) / (NB - 1)) + i % kSampleBlock;
+}
+
+// Shared-memory scratch of the block-wide helpers.
+struct Lds {
+  uint32_t* hist;      // [kBins]
+  uint32_t* scratch;   // [32]
+  uint32_t* misc;      // [16 + kTieSmall]: results, counters, tie indices at +16
+};
+constexpr int kTieSmall = 64;     // ties resolved by one wave without a radix pass
+constexpr int kMiscWords = 16 + kTieSmall;
+
+// The bin holding the need-th largest key of a 2048-bin histogram:
+// misc[0] = bin, misc[1] = keys in higher bins.  Block-wide.
 template <int NT>
 __device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* scratch,
-                           uint32_t* out) {
+                           uint32_t* misc) {
   constexpr int BPT = kBins / NT;
+  static_assert(BPT * NT == kBins, "block size must divide the bin count");
   const int t = threadIdx.x;
-  if (t == 0) { out[0] = 0; out[1] = 0; }   // ordered before the finder by the scan's barriers
+  if (t == 0) { misc[0] = 0; misc[1] = 0; }   // ordered before the finder by the scan's barriers
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) local += hist[kBins - 1 - (t * BPT + i)];
@@ -68,13 +111,38 @@ __device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* scratc
   for (int i = 0; i < BPT; ++i) {
     const int bin = kBins - 1 - (t * BPT + i);
     const uint32_t h = hist[bin];
-    if (before < need && need <= before + h) {
-      out[0] = (uint32_t)bin;
-      out[1] = before;
-    }
+    if (before < need && need <= before + h) { misc[0] = (uint32_t)bin; misc[1] = before; }
     before += h;
   }
   __syncthreads();
+}
+
+// Radix select over the keys get(i), i in [0, count), for which get returns
+// true.  With levels = 3: T = the need-th largest key exactly, take = how
+// many keys equal to T belong to the top `need`, eq = how many keys equal T.
+// With levels = 2 the low 10 bits of T are zero and T is a lower bound of
+// the need-th largest key (conservative threshold); take/eq then count the
+// keys sharing T's upper 22 bits.  Block-wide; 1 <= need <= number of keys.
+template <int NT, typename Get>
+__device__ void radix_select(Get get, int count, uint32_t need, const Lds& s, uint32_t& T,
+                             uint32_t& take, uint32_t& eq, int levels = 3) {
+  uint32_t prefix = 0;
+  for (int lvl = 0; lvl < levels; ++lvl) {
+    for (int i = threadIdx.x; i < kBins; i += NT) s.hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < count; i += NT) {
+      uint32_t key;
+      if (get(i, key) && lvl_match(key, prefix, lvl)) atomicAdd(&s.hist[lvl_digit(key, lvl)], 1u);
+    }
+    __syncthreads();
+    select_bin<NT>(s.hist, need, s.scratch, s.misc);
+    need -= s.misc[1];
+    eq = s.hist[s.misc[0]];
+    prefix |= s.misc[0] << lvl_shift(lvl);
+    __syncthreads();
+  }
+  T = prefix;
+  take = need;
 }
 
 // Keep the `m` lowest set bits of x.
@@ -88,10 +156,6 @@ __device__ __forceinline__ uint32_t keep_lowest_bits(uint32_t x, uint32_t m) {
   return r;
 }
 
-// Ordered emission from bitmaps.  Words [0, nw) of sel/tie; the first
-// `eq_take` tie bits (by index) join the selection; writes exactly the set
-// bits, ascending, to out.  Each thread owns a contiguous run of words and
-// reads them only through load_sel/load_tie.  Block-wide.
 __device__ __forceinline__ uint32_t kept_ties(uint32_t tw, uint32_t running, uint32_t eq_take) {
   const uint32_t c = __popc(tw);
   if (running >= eq_take) return 0u;
@@ -99,368 +163,547 @@ __device__ __forceinline__ uint32_t kept_ties(uint32_t tw, uint32_t running, uin
   return keep_lowest_bits(tw, eq_take - running);
 }
 
-template <int NT, typename LoadS, typename LoadT>
-__device__ void emit_bitmaps(int nw, uint32_t eq_take, LoadS load_sel, LoadT load_tie,
-                             int32_t* out, uint32_t k, uint32_t* scratch) {
+// Ordered emission of LDS bitmap words [0, nw) covering indices
+// word_base*32 + [0, 32*nw).  With a tie bitmap, the first eq_take tie bits
+// of the whole row (tie_run counts earlier ones) join the selection.
+// tie_run/out_run are block-uniform and advance by this segment's totals.
+// Never writes at or past k.  Block-wide.
+template <int NT>
+__device__ void emit_words(const uint32_t* sel, const uint32_t* tie, int nw, int word_base,
+                           uint32_t eq_take, uint32_t& tie_run, uint32_t& out_run, int32_t* out,
+                           uint32_t k, uint32_t* scratch) {
   const int t = threadIdx.x;
   const int wpt = (nw + NT - 1) / NT;
   const int w0 = min(t * wpt, nw), w1 = min(w0 + wpt, nw);
   uint32_t tcount = 0;
-  for (int w = w0; w < w1; ++w) tcount += __popc(load_tie(w));
-  uint32_t total;
-  const uint32_t tie_start = block_exclusive_scan<NT>(tcount, scratch, &total);
+  if (tie)
+    for (int w = w0; w < w1; ++w) tcount += __popc(tie[w]);
+  uint32_t tie_total;
+  const uint32_t tie_start = tie_run + block_exclusive_scan<NT>(tcount, scratch, &tie_total);
   uint32_t running = tie_start, fcount = 0;
   for (int w = w0; w < w1; ++w) {
-    const uint32_t tw = load_tie(w);
-    fcount += __popc(load_sel(w) | kept_ties(tw, running, eq_take));
+    const uint32_t tw = tie ? tie[w] : 0u;
+    fcount += __popc(sel[w] | kept_ties(tw, running, eq_take));
     running += __popc(tw);
   }
-  uint32_t pos = block_exclusive_scan<NT>(fcount, scratch, &total);
+  uint32_t out_total;
+  uint32_t pos = out_run + block_exclusive_scan<NT>(fcount, scratch, &out_total);
   running = tie_start;
   for (int w = w0; w < w1; ++w) {
-    const uint32_t tw = load_tie(w);
-    uint32_t f = load_sel(w) | kept_ties(tw, running, eq_take);
+    const uint32_t tw = tie ? tie[w] : 0u;
+    uint32_t f = sel[w] | kept_ties(tw, running, eq_take);
     running += __popc(tw);
     while (f) {
       const int bit = __ffs(f) - 1;
-      if (pos < k) out[pos] = w * 32 + bit;   // exactly k bits are set; never write past k
+      if (pos < k) out[pos] = (word_base + w) * 32 + bit;
       ++pos;
       f &= f - 1;
     }
   }
+  tie_run += tie_total;
+  out_run += out_total;
 }
 
-// ====================================================================== row plan
-// Dynamic LDS: hist[2048] | scratch[32] | misc[8] | sel[W] | tie[W] | ckey[cap] | cidx[cap]
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int words, int32_t* __restrict__ indices) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  uint32_t* hist = lds;
-  uint32_t* scratch = hist + kBins;
-  uint32_t* misc = scratch + 32;
-  uint32_t* sel = misc + 8;
-  uint32_t* tie = sel + words;
-  uint32_t* ckey = tie + words;
-  uint32_t* cidx = ckey + kRowCap;
+template <int NT>
+__device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
+  for (int i = threadIdx.x; i < k; i += NT) out[i] = i < n ? i : -1;
+}
 
-  const int row = blockIdx.x;
-  const int t = threadIdx.x;
+// Append index j (with its key) to an LDS list when `hit`: one slot
+// reservation per wave on the LDS counter *counter.
+__device__ __forceinline__ void list_append(bool hit, uint32_t key, uint32_t j, uint32_t* counter,
+                                            uint32_t* lkey, uint32_t* lidx, uint32_t cap) {
+  const uint64_t mk = __ballot(hit);
+  if (!mk) return;
+  uint32_t slot0 = 0;
+  if (lane_id() == 0) slot0 = atomicAdd(counter, (uint32_t)__popcll(mk));
+  slot0 = __shfl(slot0, 0, kWave);
+  const uint32_t slot = slot0 + wave_prefix_count(mk);
+  if (hit && slot < cap) {
+    if (lkey) lkey[slot] = key;
+    lidx[slot] = j;
+  }
+}
+
+// ---------------------------------------------------------------- steps 3-4
+// Exact selection from m candidates (key_of(i), idx_of(i)) that include every
+// key >= the k-th largest of the row; `bm` (kSegWords words of LDS, free for
+// this call) holds one bitmap segment of the ordered emission.
+template <int NT, typename KeyOf, typename IdxOf>
+__device__ void select_from_list(KeyOf key_of, IdxOf idx_of, int m, int n, int k, uint32_t* bm,
+                                 int32_t* out, const Lds& s) {
+  uint32_t T, take, eq;
+  radix_select<NT>([&](int i, uint32_t& key) { key = key_of(i); return true; }, m, (uint32_t)k,
+                   s, T, take, eq);
+  // Among the eq keys equal to T keep the `take` lowest indices.
+  uint32_t cut = 0xFFFFFFFFu;
+  if (take < eq) {
+    if (eq <= (uint32_t)kTieSmall) {
+      uint32_t* ties = s.misc + 16;
+      if (threadIdx.x == 0) s.misc[9] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < m; i += NT)
+        if (key_of(i) == T) ties[atomicAdd(&s.misc[9], 1u)] = idx_of(i);
+      __syncthreads();
+      if (threadIdx.x < kWave) {
+        const int l = threadIdx.x;
+        const uint32_t mine = l < (int)eq ? ties[l] : 0xFFFFFFFFu;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < eq; ++j) rank += ties[j] < mine ? 1u : 0u;
+        if (l < (int)eq && rank == take - 1) s.misc[10] = mine;
+      }
+      __syncthreads();
+      cut = s.misc[10];
+    } else {
+      // the take-th largest complemented index is the cut
+      uint32_t C, one, eq2;
+      radix_select<NT>([&](int i, uint32_t& key) { key = ~idx_of(i); return key_of(i) == T; }, m,
+                       take, s, C, one, eq2);
+      cut = ~C;
+    }
+  }
+  uint32_t tie_run = 0, out_run = 0;
+  for (int base = 0; base < n; base += kSegBits) {
+    const int nw = min(kSegWords, (n - base + 31) / 32);
+    for (int i = threadIdx.x; i < nw; i += NT) bm[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < m; i += NT) {
+      const uint32_t key = key_of(i), j = idx_of(i);
+      const bool keep = key > T || (key == T && j <= cut);
+      if (keep && j >= (uint32_t)base && j < (uint32_t)(base + kSegBits)) {
+        const uint32_t r = j - base;
+        atomicOr(&bm[r >> 5], 1u << (r & 31));
+      }
+    }
+    __syncthreads();
+    emit_words<NT>(bm, nullptr, nw, base / 32, 0, tie_run, out_run, out, (uint32_t)k, s.scratch);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- fallback
+// Exact top-k of a whole row of n keys key_at(j): three radix passes for T,
+// then one pass per index segment building selection/tie bitmaps (sel, tie:
+// kSegWords words of LDS each) with the tie count carried across segments.
+template <int NT, typename KeyAt>
+__device__ void select_exact_row(KeyAt key_at, int n, int k, uint32_t* sel, uint32_t* tie,
+                                 int32_t* out, const Lds& s) {
+  uint32_t T, take, eq;
+  radix_select<NT>([&](int i, uint32_t& key) { key = key_at(i); return true; }, n, (uint32_t)k,
+                   s, T, take, eq);
+  const int lane = lane_id();
+  uint32_t tie_run = 0, out_run = 0;
+  for (int base = 0; base < n; base += kSegBits) {
+    const int seg_n = min(kSegBits, n - base);
+    const int nw = (seg_n + 31) / 32;
+    const int span = ((seg_n + 63) / 64) * 64;
+    for (int r = threadIdx.x; r < span; r += NT) {
+      const bool valid = r < seg_n;
+      const uint32_t key = valid ? key_at(base + r) : 0u;
+      const uint64_t mg = __ballot(valid && key > T);
+      const uint64_t me = __ballot(valid && key == T);
+      const int w0 = (r - lane) >> 5;
+      if (lane == 0) { sel[w0] = (uint32_t)mg; tie[w0] = (uint32_t)me; }
+      if (lane == 32) { sel[w0 + 1] = (uint32_t)(mg >> 32); tie[w0 + 1] = (uint32_t)(me >> 32); }
+    }
+    __syncthreads();
+    emit_words<NT>(sel, tie, nw, base / 32, take, tie_run, out_run, out, (uint32_t)k, s.scratch);
+    __syncthreads();
+  }
+}
+
+// ====================================================================== resident plan
+// Dynamic LDS: row keys [kResKeys] | hist | scratch | misc | list indices [kResCap].
+constexpr int kResThreads = 1024;
+constexpr size_t kResLds = (size_t)(kResKeys + kBins + 32 + kMiscWords + kResCap) * 4;
+
+__global__ __launch_bounds__(kResThreads) void topk_resident_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
+    int k, int vec4, int32_t* __restrict__ indices) {
+  constexpr int NT = kResThreads;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  uint32_t* rowk = lds;
+  Lds s{lds + kResKeys, lds + kResKeys + kBins, lds + kResKeys + kBins + 32};
+  uint32_t* lidx = s.misc + kMiscWords;
+  const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
   int32_t* out = indices + (size_t)row * k;
-  if (n <= k) {
-    for (int i = t; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
-    return;
-  }
+  if (n <= k) { write_all<NT>(out, n, k); return; }
   const float* src = scores + (size_t)row * L_cap;
 
-  // ---- radix descent over the row until the bin is small or exact
-  uint32_t prefix = 0, need = (uint32_t)k, inbin = 0;
-  int lvl = 0;
-  bool exact = false;
-  while (true) {
-    for (int i = t; i < kBins; i += kRowThreads) hist[i] = 0;
+  // ---- the whole row into LDS, every load in flight before any store
+  if (vec4) {
+    constexpr int U = kResKeys / 4 / NT;
+    const int n4 = (n + 3) / 4;                 // 4*n4 <= L_cap since L_cap % 4 == 0
+    const float4* src4 = reinterpret_cast<const float4*>(src);
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = u * NT + t;
+      v[u] = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = u * NT + t;
+      if (i4 < n4) {
+        rowk[4 * i4 + 0] = score_key(v[u].x);
+        rowk[4 * i4 + 1] = score_key(v[u].y);
+        rowk[4 * i4 + 2] = score_key(v[u].z);
+        rowk[4 * i4 + 3] = score_key(v[u].w);
+      }
+    }
+  } else {
+    constexpr int U = 8;
+    for (int b0 = 0; b0 < n; b0 += U * NT) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = b0 + u * NT + t;
+        v[u] = j < n ? src[j] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = b0 + u * NT + t;
+        if (j < n) rowk[j] = score_key(v[u]);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (k <= kResCap) {
+    // ---- threshold from the sample (the row itself when short)
+    uint32_t T_lo, take, eq;
+    if (n <= kSample)
+      radix_select<NT>([&](int i, uint32_t& key) { key = rowk[i]; return true; }, n,
+                       (uint32_t)k, s, T_lo, take, eq, 2);
+    else
+      radix_select<NT>([&](int i, uint32_t& key) { key = rowk[sample_pos(i, n)]; return true; },
+                       kSample, (uint32_t)sample_rank(k, n), s, T_lo, take, eq, 2);
+    // ---- candidates (indices only: keys stay in the LDS row)
+    if (t == 0) s.misc[8] = 0;
     __syncthreads();
-    for (int j = t; j < n; j += kRowThreads) {
-      const uint32_t key = score_key(src[j]);
-      if (lvl_match(key, prefix, lvl)) atomicAdd(&hist[lvl_digit(key, lvl)], 1u);
+    for (int b0 = 0; b0 < n; b0 += NT) {
+      const int j = b0 + t;
+      const uint32_t key = j < n ? rowk[j] : 0u;
+      list_append(j < n && key >= T_lo, key, (uint32_t)j, &s.misc[8], nullptr, lidx, kResCap);
     }
     __syncthreads();
-    select_bin<kRowThreads>(hist, need, scratch, misc);
-    const uint32_t bin = misc[0];
-    need -= misc[1];
-    inbin = hist[bin];
-    prefix |= bin << lvl_shift(lvl);
-    ++lvl;
+    const int m = (int)s.misc[8];
     __syncthreads();
-    if (lvl == 3) { exact = true; break; }
-    if (inbin <= (uint32_t)kRowCap) break;
+    if (m >= k && m <= kResCap) {
+      select_from_list<NT>([&](int i) { return rowk[lidx[i]]; }, [&](int i) { return lidx[i]; },
+                           m, n, k, s.hist, out, s);
+      return;
+    }
   }
-
-  // ---- collect: bitmaps for the whole row, candidates of the bin into LDS
-  const int hi_shift = lvl_shift(lvl - 1);
-  const uint32_t hp = prefix >> hi_shift;
-  if (t == 0) misc[2] = 0;
-  __syncthreads();
+  // ---- exact fallback over the LDS row; sel/tie bitmaps in the hist area
+  // (n <= 32768 keys: 1024 words each).
+  uint32_t T, take, eq;
+  radix_select<NT>([&](int i, uint32_t& key) { key = rowk[i]; return true; }, n, (uint32_t)k, s,
+                   T, take, eq);
+  uint32_t* sel = s.hist;
+  uint32_t* tie = s.hist + kBins / 2;
   const int lane = lane_id();
-  const int span = ((n + kRowThreads - 1) / kRowThreads) * kRowThreads;
-  for (int base = 0; base < span; base += kRowThreads) {
-    const int j = base + t;
-    const bool valid = j < n;
-    const uint32_t key = valid ? score_key(src[j]) : 0u;
-    const uint32_t hk = key >> hi_shift;
-    const bool def = valid && hk > hp;
-    const bool eq = valid && hk == hp;
-    const uint64_t mdef = __ballot(def);
-    const uint64_t meq = __ballot(eq);
-    const int w0 = (j - lane) >> 5;
-    if (lane == 0) { sel[w0] = (uint32_t)mdef; tie[w0] = exact ? (uint32_t)meq : 0u; }
-    if (lane == 32) { sel[w0 + 1] = (uint32_t)(mdef >> 32); tie[w0 + 1] = exact ? (uint32_t)(meq >> 32) : 0u; }
-    if (!exact && meq) {
-      uint32_t base_slot = 0;
-      if (lane == 0) base_slot = atomicAdd(&misc[2], (uint32_t)__popcll(meq));
-      base_slot = __shfl(base_slot, 0, kWave);
-      if (eq) {
-        const uint32_t slot = base_slot + wave_prefix_count(meq);
-        ckey[slot] = key;
-        cidx[slot] = (uint32_t)j;
-      }
-    }
+  const int span = ((n + 63) / 64) * 64;
+  for (int r = t; r < span; r += NT) {
+    const bool valid = r < n;
+    const uint32_t key = valid ? rowk[r] : 0u;
+    const uint64_t mg = __ballot(valid && key > T);
+    const uint64_t me = __ballot(valid && key == T);
+    const int w0 = (r - lane) >> 5;
+    if (lane == 0) { sel[w0] = (uint32_t)mg; tie[w0] = (uint32_t)me; }
+    if (lane == 32) { sel[w0 + 1] = (uint32_t)(mg >> 32); tie[w0 + 1] = (uint32_t)(me >> 32); }
   }
   __syncthreads();
+  uint32_t tie_run = 0, out_run = 0;
+  emit_words<NT>(sel, tie, (n + 31) / 32, 0, take, tie_run, out_run, out, (uint32_t)k, s.scratch);
+}
 
-  if (!exact) {
-    // ---- finish the descent on the candidates held in LDS
-    const uint32_t nc = misc[2];
-    while (lvl < 3) {
-      for (int i = t; i < kBins; i += kRowThreads) hist[i] = 0;
-      __syncthreads();
-      for (uint32_t i = t; i < nc; i += kRowThreads) {
-        const uint32_t key = ckey[i];
-        if (lvl_match(key, prefix, lvl)) atomicAdd(&hist[lvl_digit(key, lvl)], 1u);
-      }
-      __syncthreads();
-      select_bin<kRowThreads>(hist, need, scratch, misc);
-      need -= misc[1];
-      prefix |= misc[0] << lvl_shift(lvl);
-      ++lvl;
-      __syncthreads();
+// ====================================================================== streaming plan
+// Dynamic LDS: hist | scratch | misc | region A (sample, then the list
+// keys+indices, or the fallback's sel/tie segments) | bitmap segment.
+template <int NT, int CAP>
+struct StreamCfg {
+  static constexpr int kRegionA = kSample > 2 * CAP ? kSample : 2 * CAP;
+  static constexpr size_t kLds = (size_t)(kBins + 32 + kMiscWords + kRegionA + kSegWords) * 4;
+  static_assert(kRegionA >= 2 * kSegWords, "fallback segments must fit region A");
+};
+
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void topk_stream_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
+    int k, int vec4, int32_t* __restrict__ indices) {
+  using Cfg = StreamCfg<NT, CAP>;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  Lds s{lds, lds + kBins, lds + kBins + 32};
+  uint32_t* regionA = lds + kBins + 32 + kMiscWords;
+  uint32_t* bm = regionA + Cfg::kRegionA;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int n = row_count(kv_len, row, S, L_cap);
+  int32_t* out = indices + (size_t)row * k;
+  if (n <= k) { write_all<NT>(out, n, k); return; }
+  const float* src = scores + (size_t)row * L_cap;
+
+  if (k <= CAP) {
+    // ---- sample into LDS (every load in flight first), threshold
+    uint32_t* sample = regionA;
+    const int cnt = n <= kSample ? n : kSample;
+    constexpr int U = kSample / NT;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * NT + t;
+      v[u] = i < cnt ? src[n <= kSample ? i : sample_pos(i, n)] : 0.0f;
     }
-    for (uint32_t i = t; i < nc; i += kRowThreads) {
-      const uint32_t key = ckey[i], j = cidx[i];
-      if (key > prefix) atomicOr(&sel[j >> 5], 1u << (j & 31));
-      else if (key == prefix) atomicOr(&tie[j >> 5], 1u << (j & 31));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * NT + t;
+      if (i < cnt) sample[i] = score_key(v[u]);
     }
     __syncthreads();
+    uint32_t T_lo, take, eq;
+    radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
+                     (uint32_t)(n <= kSample ? k : sample_rank(k, n)), s, T_lo, take, eq, 2);
+    // ---- one pass over the row: 16-byte loads, 4 per lane in flight
+    uint32_t* lkey = regionA;
+    uint32_t* lidx = regionA + CAP;
+    if (t == 0) s.misc[8] = 0;
+    __syncthreads();
+    int done = 0;
+    if (vec4) {
+      const float4* src4 = reinterpret_cast<const float4*>(src);
+      const int n4 = n / 4;
+      for (int b4 = 0; b4 < n4; b4 += 4 * NT) {
+        float4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i4 = b4 + u * NT + t;
+          q[u] = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i4 = b4 + u * NT + t;
+          const bool ok = i4 < n4;
+          const uint32_t k0 = score_key(q[u].x), k1 = score_key(q[u].y);
+          const uint32_t k2 = score_key(q[u].z), k3 = score_key(q[u].w);
+          list_append(ok && k0 >= T_lo, k0, 4 * i4 + 0, &s.misc[8], lkey, lidx, CAP);
+          list_append(ok && k1 >= T_lo, k1, 4 * i4 + 1, &s.misc[8], lkey, lidx, CAP);
+          list_append(ok && k2 >= T_lo, k2, 4 * i4 + 2, &s.misc[8], lkey, lidx, CAP);
+          list_append(ok && k3 >= T_lo, k3, 4 * i4 + 3, &s.misc[8], lkey, lidx, CAP);
+        }
+      }
+      done = 4 * n4;
+    }
+    for (int b0 = done; b0 < n; b0 += 4 * NT) {
+      float q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = b0 + u * NT + t;
+        q[u] = j < n ? src[j] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = b0 + u * NT + t;
+        const uint32_t key = score_key(q[u]);
+        list_append(j < n && key >= T_lo, key, (uint32_t)j, &s.misc[8], lkey, lidx, CAP);
+      }
+    }
+    __syncthreads();
+    const int m = (int)s.misc[8];
+    __syncthreads();
+    if (m >= k && m <= CAP) {
+      select_from_list<NT>([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, m, n,
+                           k, bm, out, s);
+      return;
+    }
   }
-
-  // ---- ordered emission
-  const int nw = (n + 31) / 32;
-  emit_bitmaps<kRowThreads>(
-      nw, need, [&](int w) { return sel[w]; }, [&](int w) { return tie[w]; }, out, (uint32_t)k,
-      scratch);
+  select_exact_row<NT>([&](int j) { return score_key(src[j]); }, n, k, regionA,
+                       regionA + kSegWords, out, s);
 }
 
 // ====================================================================== multi plan
+enum { kModeAll = 0, kModeList = 1, kModeExact = 2 };
+
 struct MultiWs {
-  uint32_t* ghist;   // [rows][2048]
-  uint32_t* ctr;     // [rows][4]: arrivals K1, arrivals K2, candidates, spare
-  uint32_t* state;   // [rows][4]: prefix, need, inbin, mode
-  uint32_t* ckey;    // [rows][cap]
-  uint32_t* cidx;    // [rows][cap]
-  uint32_t* sel;     // [rows][words]
-  uint32_t* tie;     // [rows][words]
+  uint32_t* state;   // [rows][4]: T_lo, mode, list count, spare
+  uint2* list;       // [rows][kMultiCap]: (key, index)
 };
 
-enum { kModeAll = 0, kModeCollect = 1, kModeRefine = 2 };
-
-__host__ __device__ inline MultiWs carve(void* ws, int rows, int words) {
+__host__ __device__ inline MultiWs carve(void* ws, int rows) {
   MultiWs m;
-  uint32_t* p = (uint32_t*)ws;
-  m.ghist = p; p += (size_t)rows * kBins;
-  m.ctr = p; p += (size_t)rows * 4;
-  m.state = p; p += (size_t)rows * 4;
-  m.ckey = p; p += (size_t)rows * kMultiCap;
-  m.cidx = p; p += (size_t)rows * kMultiCap;
-  m.sel = p; p += (size_t)rows * words;
-  m.tie = p; p += (size_t)rows * words;
+  m.state = (uint32_t*)ws;
+  m.list = (uint2*)((uint32_t*)ws + (size_t)rows * 4);
   return m;
 }
-__host__ inline size_t multi_ws_bytes(int rows, int words) {
-  return (size_t)rows * (kBins + 8 + 2 * (size_t)kMultiCap + 2 * (size_t)words) * 4;
+__host__ inline size_t multi_ws_bytes(int rows) {
+  return (size_t)rows * 4 * 4 + (size_t)rows * kMultiCap * sizeof(uint2);
 }
 
-// K0: clear histograms and counters (plain kernel, safe inside captured graphs).
-__global__ __launch_bounds__(kChunkThreads) void topk_clear_kernel(MultiWs m) {
-  const int row = blockIdx.x;
-  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) m.ghist[(size_t)row * kBins + i] = 0;
-  if (threadIdx.x < 4) m.ctr[row * 4 + threadIdx.x] = 0;
-}
+constexpr int kStateThreads = 1024;
+constexpr int kFinishThreads = 1024;
 
-// Arrive at a per-row counter after publishing this workgroup's global
-// writes; returns true in the last workgroup of the row (all threads).
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = (atomicAdd(counter, 1u) == expected - 1) ? 1u : 0u;
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// K1: chunk histograms of the top level, merged into the row histogram.
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_hist_kernel(
+// KA: threshold estimate and list reset, one workgroup per row.
+__global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int chunk, MultiWs m) {
+    int k, MultiWs m) {
+  constexpr int NT = kStateThreads;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t misc[8];
-  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  __shared__ uint32_t misc[kMiscWords];
+  __shared__ uint32_t sample[kSample];
+  Lds s{hist, scratch, misc};
+  const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
-  for (int i = t; i < kBins; i += kChunkThreads) hist[i] = 0;
-  __syncthreads();
-  if (n > k) {
-    const float* src = scores + (size_t)row * L_cap;
-    const int j1 = min((c + 1) * chunk, n);
-    for (int j = c * chunk + t; j < j1; j += kChunkThreads)
-      atomicAdd(&hist[score_key(src[j]) >> 21], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = m.ghist + (size_t)row * kBins;
-  for (int i = t; i < kBins; i += kChunkThreads)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
-  if (!arrive_last(&m.ctr[row * 4 + 0], gridDim.x, &misc[4])) return;
-
   uint32_t* st = m.state + row * 4;
-  if (n <= k) {
-    if (t == 0) { st[0] = 0; st[1] = 0; st[2] = 0; st[3] = kModeAll; }
-    return;
+  uint32_t mode = kModeAll, T_lo = 0;
+  if (n > k) {
+    if (k <= kMultiCap) {
+      const float* src = scores + (size_t)row * L_cap;
+      const int cnt = n <= kSample ? n : kSample;
+      constexpr int U = kSample / NT;
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = u * NT + t;
+        v[u] = i < cnt ? src[n <= kSample ? i : sample_pos(i, n)] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = u * NT + t;
+        if (i < cnt) sample[i] = score_key(v[u]);
+      }
+      __syncthreads();
+      uint32_t take, eq;
+      radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
+                       (uint32_t)(n <= kSample ? k : sample_rank(k, n)), s, T_lo, take, eq, 2);
+      mode = kModeList;
+    } else {
+      mode = kModeExact;
+    }
   }
-  for (int i = t; i < kBins; i += kChunkThreads) hist[i] = ld_coherent(&gh[i]);
+  if (t == 0) { st[0] = T_lo; st[1] = mode; st[2] = 0; st[3] = 0; }
+}
+
+// KB: candidates of one chunk appended to the row's list (one reservation).
+__global__ __launch_bounds__(kChunkThreads) void topk_collect_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
+    int chunk, MultiWs m) {
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t base_slot;
+  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  const uint32_t* st = m.state + row * 4;
+  if (st[1] != kModeList) return;
+  const uint32_t T_lo = st[0];
+  const int n = row_count(kv_len, row, S, L_cap);
+  const int j0 = c * chunk, j1 = min(j0 + chunk, n);
+  if (j0 >= j1) return;
+  const float* src = scores + (size_t)row * L_cap;
+  constexpr int U = kChunkKeysPerThread;    // chunk <= U * kChunkThreads
+  uint32_t key[U];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u * kChunkThreads + t;
+    key[u] = j < j1 ? score_key(src[j]) : 0u;
+    cnt += (j < j1 && key[u] >= T_lo) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<kChunkThreads>(cnt, scratch, &total);
+  if (total == 0) return;
+  if (t == 0) base_slot = atomicAdd(&m.state[row * 4 + 2], total);
   __syncthreads();
-  select_bin<kChunkThreads>(hist, (uint32_t)k, scratch, misc);
-  if (t == 0) {
-    const uint32_t bin = misc[0];
-    st[0] = bin << 21;
-    st[1] = (uint32_t)k - misc[1];
-    st[2] = hist[bin];
-    st[3] = hist[bin] <= (uint32_t)kMultiCap ? kModeCollect : kModeRefine;
+  pos += base_slot;
+  uint2* list = m.list + (size_t)row * kMultiCap;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u * kChunkThreads + t;
+    if (j < j1 && key[u] >= T_lo) {
+      if (pos < (uint32_t)kMultiCap) list[pos] = make_uint2(key[u], (uint32_t)j);
+      ++pos;
+    }
   }
 }
 
-// K2: bitmaps and candidates per chunk; the row's last arriver selects and emits.
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_collect_kernel(
+// KC: exact selection and ordered emission, one workgroup per row.
+// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | bitmap segment; the
+// fallback's sel/tie segments reuse the list area.
+constexpr size_t kFinishLds = (size_t)(2 * kMultiCap + kSegWords) * 4;
+static_assert(kMultiCap >= kSegWords, "fallback segments must fit the list area");
+
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int chunk, int words, MultiWs m, int32_t* __restrict__ indices) {
+    int k, MultiWs m, int32_t* __restrict__ indices) {
+  constexpr int NT = kFinishThreads;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t misc[8];
-  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x, lane = lane_id();
+  __shared__ uint32_t misc[kMiscWords];
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  Lds s{hist, scratch, misc};
+  uint32_t* lkey = dyn;
+  uint32_t* lidx = dyn + kMultiCap;
+  uint32_t* bm = dyn + 2 * kMultiCap;
+  const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
-  const uint32_t* st = m.state + row * 4;
-  const uint32_t mode = st[3];
-  uint32_t prefix = st[0];
-  uint32_t need = st[1];
-  const float* src = scores + (size_t)row * L_cap;
-  uint32_t* sel = m.sel + (size_t)row * words;
-  uint32_t* tie = m.tie + (size_t)row * words;
-  uint32_t* ckey = m.ckey + (size_t)row * kMultiCap;
-  uint32_t* cidx = m.cidx + (size_t)row * kMultiCap;
-  uint32_t* ncand = &m.ctr[row * 4 + 2];
-
-  if (mode != kModeAll) {
-    const uint32_t hp = prefix >> 21;
-    const int j_end = (c + 1) * chunk;    // chunk is a multiple of 64
-    for (int j = c * chunk + t; j < j_end; j += kChunkThreads) {
-      const bool valid = j < n;
-      const uint32_t key = valid ? score_key(src[j]) : 0u;
-      const uint32_t hk = key >> 21;
-      const bool def = valid && hk > hp;
-      const bool eq = valid && hk == hp;
-      const uint64_t mdef = __ballot(def);
-      const uint64_t meq = __ballot(eq);
-      const int w0 = (j - lane) >> 5;
-      if (lane == 0) { sel[w0] = (uint32_t)mdef; tie[w0] = 0u; }
-      if (lane == 32) { sel[w0 + 1] = (uint32_t)(mdef >> 32); tie[w0 + 1] = 0u; }
-      if (mode == kModeCollect && meq) {
-        uint32_t base_slot = 0;
-        if (lane == 0) base_slot = atomicAdd(ncand, (uint32_t)__popcll(meq));
-        base_slot = __shfl(base_slot, 0, kWave);
-        if (eq) {
-          const uint32_t slot = base_slot + wave_prefix_count(meq);
-          ckey[slot] = key;
-          cidx[slot] = (uint32_t)j;
-        }
-      }
-    }
-  }
-  if (!arrive_last(&m.ctr[row * 4 + 1], gridDim.x, &misc[4])) return;
-
   int32_t* out = indices + (size_t)row * k;
-  if (mode == kModeAll) {
-    for (int i = t; i < k; i += kChunkThreads) out[i] = i < n ? i : -1;
+  const uint32_t* st = m.state + row * 4;
+  const uint32_t mode = st[1];
+  if (mode == kModeAll) { write_all<NT>(out, n, k); return; }
+  const int cnt = (int)st[2];
+  const float* src = scores + (size_t)row * L_cap;
+  if (mode == kModeList && cnt >= k && cnt <= kMultiCap) {
+    const uint4* list4 = reinterpret_cast<const uint4*>(m.list + (size_t)row * kMultiCap);
+    constexpr int U = kMultiCap / 2 / NT;   // two entries per 16-byte load
+    uint4 e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i2 = u * NT + t;
+      e[u] = 2 * i2 < cnt ? list4[i2] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i2 = u * NT + t;
+      if (2 * i2 < cnt) { lkey[2 * i2] = e[u].x; lidx[2 * i2] = e[u].y; }
+      if (2 * i2 + 1 < cnt) { lkey[2 * i2 + 1] = e[u].z; lidx[2 * i2 + 1] = e[u].w; }
+    }
+    __syncthreads();
+    select_from_list<NT>([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, cnt, n,
+                         k, bm, out, s);
     return;
   }
-  int lvl = 1;
-  if (mode == kModeCollect) {
-    const uint32_t nc = ld_coherent(ncand);
-    while (lvl < 3) {
-      for (int i = t; i < kBins; i += kChunkThreads) hist[i] = 0;
-      __syncthreads();
-      for (uint32_t i = t; i < nc; i += kChunkThreads) {
-        const uint32_t key = ld_coherent(&ckey[i]);
-        if (lvl_match(key, prefix, lvl)) atomicAdd(&hist[lvl_digit(key, lvl)], 1u);
-      }
-      __syncthreads();
-      select_bin<kChunkThreads>(hist, need, scratch, misc);
-      need -= misc[1];
-      prefix |= misc[0] << lvl_shift(lvl);
-      ++lvl;
-      __syncthreads();
-    }
-    for (uint32_t i = t; i < nc; i += kChunkThreads) {
-      const uint32_t key = ld_coherent(&ckey[i]), j = ld_coherent(&cidx[i]);
-      if (key > prefix) atomicOr(&sel[j >> 5], 1u << (j & 31));
-      else if (key == prefix) atomicOr(&tie[j >> 5], 1u << (j & 31));
-    }
-  } else {
-    // Refine: the top bin is too full for the candidate list; descend over
-    // the whole row, then rebuild the row's bitmaps from the exact threshold.
-    while (lvl < 3) {
-      for (int i = t; i < kBins; i += kChunkThreads) hist[i] = 0;
-      __syncthreads();
-      for (int j = t; j < n; j += kChunkThreads) {
-        const uint32_t key = score_key(src[j]);
-        if (lvl_match(key, prefix, lvl)) atomicAdd(&hist[lvl_digit(key, lvl)], 1u);
-      }
-      __syncthreads();
-      select_bin<kChunkThreads>(hist, need, scratch, misc);
-      need -= misc[1];
-      prefix |= misc[0] << lvl_shift(lvl);
-      ++lvl;
-      __syncthreads();
-    }
-    const int span = ((n + 63) / 64) * 64;
-    for (int j = t; j < span; j += kChunkThreads) {
-      const bool valid = j < n;
-      const uint32_t key = valid ? score_key(src[j]) : 0u;
-      const uint64_t mdef = __ballot(valid && key > prefix);
-      const uint64_t meq = __ballot(valid && key == prefix);
-      const int w0 = (j - lane) >> 5;
-      if (lane == 0) { sel[w0] = (uint32_t)mdef; tie[w0] = (uint32_t)meq; }
-      if (lane == 32) { sel[w0 + 1] = (uint32_t)(mdef >> 32); tie[w0 + 1] = (uint32_t)(meq >> 32); }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  const int nw = (n + 31) / 32;
-  emit_bitmaps<kChunkThreads>(
-      nw, need, [&](int w) { return ld_coherent(&sel[w]); },
-      [&](int w) { return ld_coherent(&tie[w]); }, out, (uint32_t)k, scratch);
+  select_exact_row<NT>([&](int j) { return score_key(src[j]); }, n, k, dyn, dyn + kSegWords,
+                       out, s);
 }
+
+template <typename K>
+void opt_in_lds(K kernel, size_t bytes) {
+  (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes);
+}
+
+using Stream512 = StreamCfg<512, kRowCap>;
 
 }  // namespace
 
 TopkPlan plan_topk(int B, int S, int L_cap, int k) {
+  (void)k;
   TopkPlan p{};
   p.rows = B * S;
-  p.cap = kRowCap;
   const long long rows = p.rows;
-  p.multi = (rows < 128 && L_cap > 8192) || L_cap > 262144;
-  if (p.multi) {
+  if (rows >= 128) {
+    p.kind = kPlanStream512;
+  } else if (L_cap <= kResKeys) {
+    p.kind = kPlanResident;
+  } else {
+    p.kind = kPlanMulti;
+  }
+  if (p.kind == kPlanMulti) {
+    // ~1024 chunk workgroups in all, at most 8 keys per thread each.
     long long want = ((long long)L_cap * rows + 1023) / 1024;
-    int ch = 1024;
-    while (ch < want && ch < 16384) ch *= 2;
+    int ch = 256;
+    while (ch < want && ch < kChunkKeysPerThread * kChunkThreads) ch *= 2;
     p.chunk = ch;
     p.chunks = (L_cap + ch - 1) / ch;
-    p.words = (int)(((long long)p.chunks * ch) / 32);
-    p.cap = kMultiCap;
-    p.ws_bytes = multi_ws_bytes(p.rows, p.words);
-  } else {
-    p.words = ((L_cap + kRowThreads - 1) / kRowThreads) * kRowThreads / 32;
-    p.lds_bytes = (size_t)(kBins + 32 + 8 + 2 * p.words + 2 * kRowCap) * 4;
-    p.ws_bytes = 0;
+    p.ws_bytes = multi_ws_bytes(p.rows);
   }
   return p;
 }
@@ -468,24 +711,33 @@ TopkPlan plan_topk(int B, int S, int L_cap, int k) {
 void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, int S,
                  int L_cap, int k, int32_t* indices, void* ws, hipStream_t st) {
   if (p.rows == 0) return;
-  if (!p.multi) {
-    // The row plan may use more than the default 64 KiB of dynamic LDS.
-    static bool lds_opt_in = false;
-    if (!lds_opt_in) {
-      (void)hipFuncSetAttribute((const void*)topk_row_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      lds_opt_in = true;
-    }
-    hipLaunchKernelGGL(topk_row_kernel, dim3(p.rows), dim3(kRowThreads), p.lds_bytes, st,
-                       scores, kv_len, S, L_cap, k, p.words, indices);
-    return;
+  static bool lds_opt_in = false;
+  if (!lds_opt_in) {
+    opt_in_lds(topk_resident_kernel, kResLds);
+    opt_in_lds(topk_stream_kernel<512, kRowCap>, Stream512::kLds);
+    opt_in_lds(topk_finish_kernel, kFinishLds);
+    lds_opt_in = true;
   }
-  MultiWs m = carve(ws, p.rows, p.words);
-  hipLaunchKernelGGL(topk_clear_kernel, dim3(p.rows), dim3(kChunkThreads), 0, st, m);
-  hipLaunchKernelGGL(topk_chunk_hist_kernel, dim3(p.chunks, p.rows), dim3(kChunkThreads), 0, st,
-                     scores, kv_len, S, L_cap, k, p.chunk, m);
-  hipLaunchKernelGGL(topk_chunk_collect_kernel, dim3(p.chunks, p.rows), dim3(kChunkThreads), 0,
-                     st, scores, kv_len, S, L_cap, k, p.chunk, p.words, m, indices);
+  const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
+  switch (p.kind) {
+    case kPlanStream512:
+      hipLaunchKernelGGL((topk_stream_kernel<512, kRowCap>), dim3(p.rows), dim3(512),
+                         Stream512::kLds, st, scores, kv_len, S, L_cap, k, vec4, indices);
+      return;
+    case kPlanResident:
+      hipLaunchKernelGGL(topk_resident_kernel, dim3(p.rows), dim3(kResThreads), kResLds, st,
+                         scores, kv_len, S, L_cap, k, vec4, indices);
+      return;
+    default: {
+      MultiWs m = carve(ws, p.rows);
+      hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.rows), dim3(kStateThreads), 0, st, scores,
+                         kv_len, S, L_cap, k, m);
+      hipLaunchKernelGGL(topk_collect_kernel, dim3(p.chunks, p.rows), dim3(kChunkThreads), 0, st,
+                         scores, kv_len, S, L_cap, p.chunk, m);
+      hipLaunchKernelGGL(topk_finish_kernel, dim3(p.rows), dim3(kFinishThreads), kFinishLds, st,
+                         scores, kv_len, S, L_cap, k, m, indices);
+    }
+  }
 }
 
 }  // namespace dsa

@@ -76,16 +76,18 @@ def test_indexer_validation(dsa):
 
 def test_topk_validation(dsa):
     L = dsa.LIB
-    need = L.dsa_topk_workspace_bytes(1, 8, 32768, 2048)
-    assert need > 0                                      # few long rows: multi-workgroup plan
-    assert L.dsa_topk_workspace_bytes(1, 2048, 131072, 2048) == 0   # one workgroup per row
-    assert L.dsa_topk_workspace_bytes(1, 8, 32768, 2048) == need    # deterministic
+    LC = 1 << 20
+    need = L.dsa_topk_workspace_bytes(1, 8, LC, 2048)
+    assert need > 0                                             # few very long rows: multi plan
+    assert L.dsa_topk_workspace_bytes(1, 8, 32768, 2048) == 0     # one workgroup per row
+    assert L.dsa_topk_workspace_bytes(1, 2048, 131072, 2048) == 0
+    assert L.dsa_topk_workspace_bytes(1, 8, LC, 2048) == need     # deterministic
 
-    def call(k=2048, Lc=32768, mx=32768, ws=A16, wsb=None, sc=A16, B=1, S=8, idx=A16):
+    def call(k=2048, Lc=LC, mx=LC, ws=A16, wsb=None, sc=A16, B=1, S=8, idx=A16):
         return L.dsa_topk(sc, A16, B, S, Lc, mx, k, idx, ws, need if wsb is None else wsb, None)
     assert call(k=0) == _status("INVALID")
-    assert call(k=32769) == _status("INVALID")
-    assert call(mx=40000) == _status("INVALID")
+    assert call(k=-5) == _status("INVALID")
+    assert call(mx=LC + 1) == _status("INVALID")
     assert call(Lc=(1 << 24) + 1, mx=0) == _status("UNSUPPORTED")
     assert call(wsb=need - 1) == _status("WS")
     assert "needed" in dsa.dsa_last_error()

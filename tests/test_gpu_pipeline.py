@@ -56,7 +56,7 @@ def test_pipeline_full_size(dsa, wl):
     got = out.cpu()
     sel_got = torch.stack([got[b, s] for b, s in rows])
     sel_ref = np.stack([ref[b, s] for b, s in rows])
-    rel, mx = assert_output_close(sel_got, sel_ref, wl.out_dtype, what=wl.name)
+    rel, mx = assert_output_close(sel_got, sel_ref, wl.out_dtype, what=wl.name, strict=True)
     if wl.out_dtype == "f32":
         assert rel <= 1e-5
     say(f"pipeline {wl.name}: rows={len(rows)} rel={rel:.2e} max={mx:.2e}")

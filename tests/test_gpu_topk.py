@@ -97,3 +97,43 @@ def test_topk_prefill_128k_shape(dsa):
     sc = indexer_like_scores(rng(13), (1, 2048, 131072))
     _check(dsa, sc, [131072], 2048, rows=[(0, s) for s in (0, 1, 500, 1023, 1024, 2047)],
            what="prefill_128k-shaped")
+
+
+def test_topk_k_beyond_list_capacity_uses_exact_fallback(dsa):
+    r = rng(14)
+    # row plan (many rows) and multi plan (few long rows), k above the list capacity
+    _check(dsa, integer_scores(r, (1, 130, 12000), -50, 50), [12000], 5000, what="row k>cap")
+    _check(dsa, torch.from_numpy(r.standard_normal((1, 4, 40000)).astype(np.float32)), [40000],
+           9000, what="multi k>cap")
+
+
+def _sample_positions(n, sample=8192, block=256):
+    nb = sample // block
+    return np.concatenate([np.arange(b * (n - block) // (nb - 1), b * (n - block) // (nb - 1) + block)
+                           for b in range(nb)])
+
+
+def test_topk_sample_heavy_rows_use_exact_fallback(dsa):
+    # White-box: large scores exactly at the keys the threshold sample reads,
+    # so fewer than k keys reach the estimated threshold and the exact
+    # fallback must produce the result.
+    r = rng(15)
+    for (B, S, L, k) in [(1, 8, 40000, 2048), (1, 130, 40000, 2048)]:
+        sc = r.integers(-100, 100, size=(B, S, L)).astype(np.float32)
+        for s in range(S):
+            n = L - S + s + 1
+            pos = _sample_positions(n)
+            sc[0, s, pos] = 1000.0 + r.integers(0, 50, size=pos.shape[0])
+        _check(dsa, torch.from_numpy(sc), [L], k, what="sample-heavy")
+
+
+def test_topk_very_long_rows_multi_plan(dsa):
+    # Rows above 512K keys with few rows use several workgroups per row.
+    r = rng(16)
+    L = 600000
+    _check(dsa, torch.from_numpy(r.standard_normal((1, 3, L)).astype(np.float32)), [L], 2048,
+           what="multi normal")
+    _check(dsa, integer_scores(r, (1, 2, L), -30, 30), [L, ], 2048, what="multi ties")
+    _check(dsa, torch.full((1, 2, L), -1.5), [L], 3000, what="multi tie storm")
+    _check(dsa, torch.from_numpy(r.standard_normal((2, 1, L)).astype(np.float32)), [L, 1000],
+           9000, what="multi k>cap ragged")
