@@ -7,9 +7,12 @@ the 256 MB Infinity Cache when it is read again.  The reported value is the
 time per layer (microseconds): step time / N.
 
 Inputs are seeded and synthetic and already resident in HBM when the timed
-region starts.  HIP events on the launch stream time the whole region and,
-inside it, every call of the dominant stage; that stage's algorithmic bytes
-per call divided by its average duration is the roofline `achieved` figure.
+region starts.  By default one step is captured as a HIP graph (through
+torch.cuda.CUDAGraph) and replayed, as a decode step is in a serving loop;
+--eager times plain launches.  HIP events on the launch stream time K step
+replays, then K replays of a graph of each stage alone; the stage with the
+longest time is the dominant one, and its algorithmic bytes per call divided
+by its average duration is the roofline `achieved` figure.
 The CPU baseline times the FP64 oracle on the host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -36,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="spec_decode_32k")
     p.add_argument("--layers", type=int, default=0, help="layer buffer sets (0: >= 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches instead of HIP-graph replays")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
 
@@ -129,7 +134,7 @@ def main():
     dev = torch.device("cuda:0")
     layer_bytes = sum(v.numel() * v.element_size() for v in x.values()
                       if isinstance(v, torch.Tensor))
-    n_layers = args.layers or max(2, -(-(1 << 30) // layer_bytes))
+    n_layers = args.layers or min(512, max(2, -(-(1 << 30) // layer_bytes)))
     layers = []
     for _ in range(n_layers):
         layers.append({kk: (v.to(dev) if isinstance(v, torch.Tensor) else v) for kk, v in x.items()})
@@ -161,57 +166,68 @@ def main():
 
     stages = (["indexer", "topk"] if w.has_indexer else []) + ["attention"]
 
-    def layer_pass(g, ev=None, dom=None):
+    def layer_pass(g):
         for st in stages:
-            if st == dom:
-                ev[0].record()
-                stage(st, g)
-                ev[1].record()
-            else:
-                stage(st, g)
+            stage(st, g)
 
-    # Calibration: per-stage durations (outside the timed region) pick the
-    # dominant stage.
-    for g in layers:
-        layer_pass(g)
-    torch.cuda.synchronize()
-    calib = {}
-    for st in stages:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 3
-        e0.record()
-        for _ in range(reps):
-            for g in layers:
-                stage(st, g)
-        e1.record()
-        torch.cuda.synchronize()
-        calib[st] = e0.elapsed_time(e1) * 1e3 / (reps * n_layers)
-    dominant = max(calib, key=calib.get)
-
-    for _ in range(args.warmup):
+    def step():
         for g in layers:
             layer_pass(g)
-    torch.cuda.synchronize()
 
-    # ---- timed region
+    stage_fns = {st: (lambda st=st: [stage(st, g) for g in layers]) for st in stages}
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
     K = args.steps
-    dom_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(K * n_layers)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    i = 0
-    for _ in range(K):
-        for g in layers:
-            layer_pass(g, dom_events[i], dominant)
-            i += 1
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / K
-    us_per_layer = ms_total * 1e3 / (K * n_layers)
-    dom_us = sum(a.elapsed_time(b) for a, b in dom_events) * 1e3 / len(dom_events)
 
+    def timed(fn, reps):
+        """Average ms per fn() over `reps` calls, HIP events on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    mode = "eager"
+    run_step, run_stage = step, dict(stage_fns)
+    if not args.eager:
+        # One step (every layer, every stage) captured as a HIP graph and
+        # replayed; each stage alone (over every layer) is a graph of its own.
+        try:
+            s_cap = torch.cuda.Stream()
+            s_cap.wait_stream(torch.cuda.current_stream())
+            graphs = {}
+            with torch.cuda.stream(s_cap):
+                for name, fn in [("step", step)] + list(stage_fns.items()):
+                    fn()                                   # warm-up on the capture stream
+                    torch.cuda.synchronize()
+                    gph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gph, stream=s_cap):
+                        fn()
+                    graphs[name] = gph
+            torch.cuda.current_stream().wait_stream(s_cap)
+            torch.cuda.synchronize()
+            run_step = graphs["step"].replay
+            run_stage = {st: graphs[st].replay for st in stages}
+            for _ in range(3):
+                run_step()
+            torch.cuda.synchronize()
+            mode = "hip_graph"
+        except Exception as ex:     # capture unsupported here: time eager launches
+            print(f"graph capture failed ({ex}); timing eager launches", file=sys.stderr)
+            run_step, run_stage = step, dict(stage_fns)
+
+    # ---- timed region: K steps, then K replays of each stage alone
+    ms_per_step = timed(run_step, K)
+    us_per_layer = ms_per_step * 1e3 / n_layers
+    stage_us = {st: timed(run_stage[st], K) * 1e3 / n_layers for st in stages}
+    dominant = max(stage_us, key=stage_us.get)
+    dom_us = stage_us[dominant]
+    eager_us = timed(step, max(3, K // 5)) * 1e3 / n_layers if mode != "eager" else us_per_layer
     sb = stage_bytes(w, kv_len)
     dom_gbps = sb[dominant] / (dom_us * 1e-6) / 1e9
     path_gbps = sb["path"] / (us_per_layer * 1e-6) / 1e9
@@ -234,11 +250,14 @@ def main():
                                                          if w.has_indexer else None),
                    "layers_per_step": n_layers, "attention_form": "decode" if decode else "prefill"},
         "tokens_per_s": round(B * S / (us_per_layer * 1e-6), 1),
+        "launch_mode": mode,
+        "eager_us_per_layer": round(eager_us, 3),
         "path_hbm_gbps": round(path_gbps, 1),
-        "stage_us": {k2: round(v, 3) for k2, v in calib.items()},
+        "stage_us": {k2: round(v, 3) for k2, v in stage_us.items()},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "stage": dominant, "us_per_call": round(dom_us, 3),
+                     "timing": f"{mode} replays of the {dominant} stage over all layers",
                      "bytes_per_call": sb[dominant]},
     }
     if not args.no_cpu_baseline:

@@ -59,6 +59,24 @@ __device__ __forceinline__ void store_out(void* out, size_t i, float v, int dt) 
   else ((__bf16*)out)[i] = (__bf16)v;
 }
 
+// out[i .. i+3] = O / L (0 where L == 0), rounded to the output dtype.
+__device__ __forceinline__ void store_out4(void* out, size_t i, f32x4 O, float L, int dt) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = L > 0.0f ? O[e] / L : 0.0f;
+  if (dt == kF32) {
+    *reinterpret_cast<f32x4*>((float*)out + i) = r;
+  } else if (dt == kF16) {
+    typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+    h4 v = {(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+    *reinterpret_cast<h4*>((_Float16*)out + i) = v;
+  } else {
+    typedef __attribute__((ext_vector_type(4))) __bf16 b4;
+    b4 v = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+    *reinterpret_cast<b4*>((__bf16*)out + i) = v;
+  }
+}
+
 // N elements of T from global memory (N * sizeof(T) a multiple of 16).
 template <typename T, int N>
 __device__ __forceinline__ void load_elems(const T* src, T (&dst)[N]) {
@@ -85,7 +103,9 @@ struct AttnCfg {
   static constexpr int kVPad = kF32Path ? 4 : 8;     // LDS row padding (elements)
   static constexpr int kVStride = D + kVPad;
   static constexpr size_t kVBytes = (size_t)kAttnWaves * kTile * kVStride * sizeof(MPV);
-  static constexpr size_t kMergeBytes = (size_t)kAttnWaves * 16 * (D + 2) * sizeof(float);
+  static constexpr int kOStride = D + 4;              // padded O^T row (floats) in the merge
+  static constexpr size_t kMergeBytes =
+      ((size_t)kAttnWaves * 16 * kOStride + 4 * kAttnWaves * 16 + 2 * 16) * sizeof(float);
   static constexpr size_t kLds = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
 };
 
@@ -109,6 +129,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const int l = lane_id();
   const int g4 = l >> 4;        // lane group 0..3
   const int c16 = l & 15;       // head column / key row within a half tile
+  // This lane's key-list entries of the wave's first tile, fetched right
+  // away so that their latency overlaps the kv_len and query loads.
+  int next_a = -1, next_b = -1;
+  {
+    const int ja = k0 + kTile * wave + c16, jb = ja + 16;
+    if (ja < k1) next_a = idx_row[ja];
+    if (jb < k1) next_b = idx_row[jb];
+  }
   const int R = p.ratio;
   const bool head_ok = c16 < R;
   const int h = g * R + (head_ok ? c16 : 0);
@@ -138,10 +166,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] = f32x4{};
 
   for (int t0 = k0 + kTile * wave; t0 < k1; t0 += kTile * kAttnWaves) {
-    // ---- this lane's two key rows (row c16 of each half tile)
-    const int ja = t0 + c16, jb = t0 + 16 + c16;
-    const int ia = ja < k1 ? idx_row[ja] : -1;
-    const int ib = jb < k1 ? idx_row[jb] : -1;
+    // ---- this lane's two key rows (row c16 of each half tile); fetch the
+    // entries of the wave's next tile now, they are needed one tile later.
+    const int ia = next_a, ib = next_b;
+    {
+      const int ja = t0 + kTile * kAttnWaves + c16, jb = ja + 16;
+      next_a = ja < k1 ? idx_row[ja] : -1;
+      next_b = jb < k1 ? idx_row[jb] : -1;
+    }
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
     const KVT* krow_a = kbase + (size_t)(va ? ia : 0) * kv_row_stride + Q4 * g4;
@@ -285,43 +317,54 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   float l_col = l_run + __shfl_xor(l_run, 16, kWave);
   l_col += __shfl_xor(l_col, 32, kWave);
   __syncthreads();
-  float* mb = (float*)smem;                                  // [waves][16]
+  constexpr int OS = Cfg::kOStride;
+  float* ob = (float*)smem;                                  // [waves][16][OS]
+  float* mb = ob + kAttnWaves * 16 * OS;                     // [waves][16]
   float* lb = mb + kAttnWaves * 16;                          // [waves][16]
-  float* ob = lb + kAttnWaves * 16;                          // [waves][16][D]
+  float* fb = lb + kAttnWaves * 16;                          // [waves][16] rescale factors
+  float* hb = fb + kAttnWaves * 16;                          // [16] L, [16] M
   if (g4 == 0) {
     mb[wave * 16 + c16] = m_run;
     lb[wave * 16 + c16] = l_col;
   }
 #pragma unroll
   for (int dt = 0; dt < Cfg::kDTiles; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ob[((size_t)wave * 16 + c16) * D + 16 * dt + 4 * g4 + i] = o[dt][i];
+    *reinterpret_cast<f32x4*>(&ob[((size_t)wave * 16 + c16) * OS + 16 * dt + 4 * g4]) = o[dt];
   __syncthreads();
-
-  for (int e = threadIdx.x; e < R * D; e += kAttnThreads) {
-    const int n = e / D, d = e % D;
+  if (threadIdx.x < 16) {
+    const int n = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mb[w * 16 + n]);
-    float L = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
+    float L = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = mb[w * 16 + n];
-        const float f = (mw == -INFINITY) ? 0.0f : exp_keep_subnormal(mw - M);
-        L += f * lb[w * 16 + n];
-        O += f * ob[((size_t)w * 16 + n) * D + d];
-      }
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float mw = mb[w * 16 + n];
+      const float f = (mw == -INFINITY) ? 0.0f : exp_keep_subnormal(mw - M);
+      fb[w * 16 + n] = f;
+      L += f * lb[w * 16 + n];
     }
+    hb[n] = L;
+    hb[16 + n] = M;
+  }
+  __syncthreads();
+  constexpr int C4 = D / 4;
+  for (int e = threadIdx.x; e < R * C4; e += kAttnThreads) {
+    const int n = e / C4, c = e % C4;
+    f32x4 O = f32x4{};
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w)
+      O += fb[w * 16 + n] * *reinterpret_cast<const f32x4*>(&ob[((size_t)w * 16 + n) * OS + 4 * c]);
+    const float L = hb[n];
     const size_t hrow = (size_t)row * p.H_q + g * R + n;
     if (p.nsplit == 1) {
-      store_out(p.out, hrow * D + d, L > 0.0f ? O / L : 0.0f, p.out_dtype);
+      store_out4(p.out, hrow * D + 4 * c, O, L, p.out_dtype);
     } else {
       float* pml = p.part;
       float* po = p.part + (size_t)2 * gridDim.z * p.H_q * p.nsplit;
-      po[(hrow * p.nsplit + split) * D + d] = O;
-      if (d == 0) {
-        pml[(hrow * p.nsplit + split) * 2 + 0] = M;
+      *reinterpret_cast<f32x4*>(&po[(hrow * p.nsplit + split) * D + 4 * c]) = O;
+      if (c == 0) {
+        pml[(hrow * p.nsplit + split) * 2 + 0] = hb[16 + n];
         pml[(hrow * p.nsplit + split) * 2 + 1] = L;
       }
     }

@@ -129,29 +129,27 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return v;
 }
 
-// Block-wide exclusive scan of one u32 per thread.  `scratch` holds at least
-// NT/64 + 1 words of LDS.  Returns the exclusive prefix; *total gets the sum.
-// Contains barriers: every thread of the block must call it.
+// Block-wide exclusive scan of one u32 per thread; *total gets the sum.
+// `scratch` holds NT/64 words of LDS.  One barrier: the caller must not let
+// any thread reuse the same scratch words before a later barrier (every
+// thread reads all of them after the one inside).
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
                                                          uint32_t* total) {
   constexpr int NW = NT / kWave;
   const int w = threadIdx.x / kWave, l = lane_id();
-  uint32_t inc = wave_inclusive_scan(v);
-  __syncthreads();
+  const uint32_t inc = wave_inclusive_scan(v);
   if (l == kWave - 1) scratch[w] = inc;
   __syncthreads();
-  if (w == 0) {
-    uint32_t x = (l < NW) ? scratch[l] : 0u;
-    uint32_t xi = wave_inclusive_scan(x);
-    if (l < NW) scratch[l] = xi - x;
-    if (l == NW - 1) scratch[NW] = xi;
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t x = scratch[i];
+    before += i < w ? x : 0u;
+    tot += x;
   }
-  __syncthreads();
-  uint32_t res = scratch[w] + inc - v;
-  *total = scratch[NW];
-  __syncthreads();
-  return res;
+  *total = tot;
+  return before + inc - v;
 }
 
 }  // namespace dsa

@@ -5,9 +5,10 @@
 // Exact for any FP32 input.  Scores map to order-preserving u32 keys
 // (score_key); selection works on keys only.
 //
-// 1. Threshold estimate.  A sample of the row (all of it when the row has at
-//    most 8192 keys, else 32 blocks of 256 consecutive keys spread over the
-//    row) goes through two radix levels (the top 11 + 11 key bits) to the
+// 1. Threshold estimate.  A sample of the row (all of it when the row is
+//    short, else blocks of 256 consecutive keys spread evenly over the row:
+//    2048 keys for an LDS-resident row, 8192 when streaming, 4096 in the
+//    multi plan) goes through two radix levels (the top 11 + 11 key bits) to the
 //    bin of the key of rank r = ceil(1.2e + 4 sqrt(e)) + 8, where e = k *
 //    sample / n is the expected sample rank of the k-th largest key.  The
 //    bin's lower edge T_lo is at or below that key; every key >= T_lo is a
@@ -50,8 +51,10 @@ constexpr int kSegWords = 2048;        // bitmap segment: 65536 indices
 constexpr int kSegBits = kSegWords * 32;
 constexpr int kResKeys = 32768;        // longest row the resident plan holds
 constexpr int kResCap = 4096;
+constexpr int kResSample = 2048;       // sample of a resident row (already in LDS)
 constexpr int kRowCap = 4096;
 constexpr int kMultiCap = 8192;
+constexpr int kMultiSample = 4096;     // sample of the threshold kernel
 constexpr int kChunkThreads = 256;
 constexpr int kChunkKeysPerThread = 8;
 
@@ -72,16 +75,18 @@ __device__ __forceinline__ int row_count(const int32_t* kv_len, int row, int S, 
   return n < 0 ? 0 : (n > L_cap ? L_cap : n);
 }
 
-// Sample rank of the threshold and the row position of sample element i.
-__device__ __forceinline__ int sample_rank(int k, int n) {
-  const float e = (float)k * (float)kSample / (float)n;
+// Sample rank of the threshold and the row position of sample element i,
+// for a sample of `ns` keys (ns a multiple of kSampleBlock) of a row of n > ns.
+__device__ __forceinline__ int sample_rank(int k, int n, int ns) {
+  const float e = (float)k * (float)ns / (float)n;
   const int r = (int)ceilf(1.2f * e + 4.0f * sqrtf(e)) + 8;
-  return r < kSample ? r : kSample;
+  return r < ns ? r : ns;
 }
+template <int NS>
 __device__ __forceinline__ int sample_pos(int i, int n) {
-  constexpr int NB = kSample / kSampleBlock;
+  constexpr int NB = NS / kSampleBlock;             // <= 32 blocks, n < 2^24: no overflow
   const int blk = i / kSampleBlock;
-  return (int)((long long)blk * (n - kSampleBlock) / (NB - 1)) + i % kSampleBlock;
+  return (int)((uint32_t)(blk * (n - kSampleBlock)) / (uint32_t)(NB - 1)) + i % kSampleBlock;
 }
 
 // Shared-memory scratch of the block-wide helpers.
@@ -130,9 +135,11 @@ __device__ void radix_select(Get get, int count, uint32_t need, const Lds& s, ui
   for (int lvl = 0; lvl < levels; ++lvl) {
     for (int i = threadIdx.x; i < kBins; i += NT) s.hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < count; i += NT) {
-      uint32_t key;
-      if (get(i, key) && lvl_match(key, prefix, lvl)) atomicAdd(&s.hist[lvl_digit(key, lvl)], 1u);
+    for (int i0 = 0; i0 < count; i0 += NT) {
+      const int i = i0 + threadIdx.x;
+      uint32_t key = 0;
+      const bool in = i < count && get(i, key) && lvl_match(key, prefix, lvl);
+      if (in) atomicAdd(&s.hist[lvl_digit(key, lvl)], 1u);
     }
     __syncthreads();
     select_bin<NT>(s.hist, need, s.scratch, s.misc);
@@ -187,7 +194,7 @@ __device__ void emit_words(const uint32_t* sel, const uint32_t* tie, int nw, int
     running += __popc(tw);
   }
   uint32_t out_total;
-  uint32_t pos = out_run + block_exclusive_scan<NT>(fcount, scratch, &out_total);
+  uint32_t pos = out_run + block_exclusive_scan<NT>(fcount, scratch + 16, &out_total);
   running = tie_start;
   for (int w = w0; w < w1; ++w) {
     const uint32_t tw = tie ? tie[w] : 0u;
@@ -209,20 +216,15 @@ __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
   for (int i = threadIdx.x; i < k; i += NT) out[i] = i < n ? i : -1;
 }
 
-// Append index j (with its key) to an LDS list when `hit`: one slot
-// reservation per wave on the LDS counter *counter.
-__device__ __forceinline__ void list_append(bool hit, uint32_t key, uint32_t j, uint32_t* counter,
-                                            uint32_t* lkey, uint32_t* lidx, uint32_t cap) {
-  const uint64_t mk = __ballot(hit);
-  if (!mk) return;
-  uint32_t slot0 = 0;
-  if (lane_id() == 0) slot0 = atomicAdd(counter, (uint32_t)__popcll(mk));
-  slot0 = __shfl(slot0, 0, kWave);
-  const uint32_t slot = slot0 + wave_prefix_count(mk);
-  if (hit && slot < cap) {
-    if (lkey) lkey[slot] = key;
-    lidx[slot] = j;
-  }
+// Reserve `cnt` consecutive list slots per lane with one LDS atomic per
+// wave; returns this lane's first slot.
+__device__ __forceinline__ uint32_t wave_reserve(uint32_t cnt, uint32_t* counter) {
+  const uint32_t inc = wave_inclusive_scan(cnt);
+  const uint32_t total = (uint32_t)__shfl((int)inc, kWave - 1, kWave);
+  uint32_t base = 0;
+  if (lane_id() == kWave - 1 && total) base = atomicAdd(counter, total);
+  base = (uint32_t)__shfl((int)base, kWave - 1, kWave);
+  return base + inc - cnt;
 }
 
 // ---------------------------------------------------------------- steps 3-4
@@ -317,10 +319,10 @@ __device__ void select_exact_row(KeyAt key_at, int n, int k, uint32_t* sel, uint
 constexpr int kResThreads = 1024;
 constexpr size_t kResLds = (size_t)(kResKeys + kBins + 32 + kMiscWords + kResCap) * 4;
 
-__global__ __launch_bounds__(kResThreads) void topk_resident_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_resident_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
     int k, int vec4, int32_t* __restrict__ indices) {
-  constexpr int NT = kResThreads;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* rowk = lds;
   Lds s{lds + kResKeys, lds + kResKeys + kBins, lds + kResKeys + kBins + 32};
@@ -373,26 +375,60 @@ __global__ __launch_bounds__(kResThreads) void topk_resident_kernel(
   if (k <= kResCap) {
     // ---- threshold from the sample (the row itself when short)
     uint32_t T_lo, take, eq;
-    if (n <= kSample)
+    if (n <= kResSample)
       radix_select<NT>([&](int i, uint32_t& key) { key = rowk[i]; return true; }, n,
                        (uint32_t)k, s, T_lo, take, eq, 2);
     else
-      radix_select<NT>([&](int i, uint32_t& key) { key = rowk[sample_pos(i, n)]; return true; },
-                       kSample, (uint32_t)sample_rank(k, n), s, T_lo, take, eq, 2);
-    // ---- candidates (indices only: keys stay in the LDS row)
+      radix_select<NT>(
+          [&](int i, uint32_t& key) { key = rowk[sample_pos<kResSample>(i, n)]; return true; },
+          kResSample, (uint32_t)sample_rank(k, n, kResSample), s, T_lo, take, eq, 2);
+    // ---- candidates.  Each lane reads its keys 4 at a time (16-byte LDS
+    // reads), keeps a hit mask (one bit per key), reserves its slots with one atomic
+    // per wave and writes its indices; list order is irrelevant.
+    constexpr int R4 = kResKeys / 4 / NT;       // 16-byte groups per lane
+    static_assert(R4 * 4 <= 64, "hit mask holds one bit per key of a lane");
     if (t == 0) s.misc[8] = 0;
     __syncthreads();
-    for (int b0 = 0; b0 < n; b0 += NT) {
-      const int j = b0 + t;
-      const uint32_t key = j < n ? rowk[j] : 0u;
-      list_append(j < n && key >= T_lo, key, (uint32_t)j, &s.misc[8], nullptr, lidx, kResCap);
+    const uint4* row4 = reinterpret_cast<const uint4*>(rowk);
+    uint64_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < R4; ++i) {
+      const int g = i * NT + t;                 // keys 4g .. 4g+3
+      if (4 * g < n) {
+        const uint4 q = row4[g];
+        mask |= (uint64_t)(q.x >= T_lo && 4 * g + 0 < n) << (4 * i + 0);
+        mask |= (uint64_t)(q.y >= T_lo && 4 * g + 1 < n) << (4 * i + 1);
+        mask |= (uint64_t)(q.z >= T_lo && 4 * g + 2 < n) << (4 * i + 2);
+        mask |= (uint64_t)(q.w >= T_lo && 4 * g + 3 < n) << (4 * i + 3);
+      }
+    }
+    uint32_t slot = wave_reserve((uint32_t)__popcll(mask), &s.misc[8]);
+    for (uint64_t mm = mask; mm; mm &= mm - 1) {
+      const int b = __ffsll((unsigned long long)mm) - 1;
+      if (slot < (uint32_t)kResCap) lidx[slot] = (uint32_t)(4 * ((b >> 2) * NT + t) + (b & 3));
+      ++slot;
     }
     __syncthreads();
     const int m = (int)s.misc[8];
-    __syncthreads();
     if (m >= k && m <= kResCap) {
-      select_from_list<NT>([&](int i) { return rowk[lidx[i]]; }, [&](int i) { return lidx[i]; },
-                           m, n, k, s.hist, out, s);
+      // The row is no longer needed beyond the candidates' keys: gather them
+      // into a compact key array at the front of the row area.
+      constexpr int MU = kResCap / NT;
+      uint32_t kk[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int i = u * NT + t;
+        kk[u] = i < m ? rowk[lidx[i]] : 0u;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int i = u * NT + t;
+        if (i < m) rowk[i] = kk[u];
+      }
+      __syncthreads();
+      select_from_list<NT>([&](int i) { return rowk[i]; }, [&](int i) { return lidx[i]; }, m, n,
+                           k, s.hist, out, s);
       return;
     }
   }
@@ -453,7 +489,7 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = u * NT + t;
-      v[u] = i < cnt ? src[n <= kSample ? i : sample_pos(i, n)] : 0.0f;
+      v[u] = i < cnt ? src[n <= kSample ? i : sample_pos<kSample>(i, n)] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -463,12 +499,25 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
     __syncthreads();
     uint32_t T_lo, take, eq;
     radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
-                     (uint32_t)(n <= kSample ? k : sample_rank(k, n)), s, T_lo, take, eq, 2);
+                     (uint32_t)(n <= kSample ? k : sample_rank(k, n, kSample)), s, T_lo, take,
+                     eq, 2);
     // ---- one pass over the row: 16-byte loads, 4 per lane in flight
     uint32_t* lkey = regionA;
     uint32_t* lidx = regionA + CAP;
     if (t == 0) s.misc[8] = 0;
     __syncthreads();
+    // 16 keys per lane per step (4 x 16-byte loads in flight); lanes count
+    // their hits and one LDS reservation per wave places them.
+    auto place = [&](const uint32_t* kk, const int* jj, int nk) {
+      uint32_t hits = 0;
+      for (int e = 0; e < nk; ++e) hits += (jj[e] >= 0 && kk[e] >= T_lo) ? 1u : 0u;
+      uint32_t slot = wave_reserve(hits, &s.misc[8]);
+      for (int e = 0; e < nk; ++e)
+        if (jj[e] >= 0 && kk[e] >= T_lo) {
+          if (slot < (uint32_t)CAP) { lkey[slot] = kk[e]; lidx[slot] = (uint32_t)jj[e]; }
+          ++slot;
+        }
+    };
     int done = 0;
     if (vec4) {
       const float4* src4 = reinterpret_cast<const float4*>(src);
@@ -478,35 +527,35 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i4 = b4 + u * NT + t;
-          q[u] = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          q[u] = i4 < n4 ? src4[i4] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
+        uint32_t kk[16];
+        int jj[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i4 = b4 + u * NT + t;
           const bool ok = i4 < n4;
-          const uint32_t k0 = score_key(q[u].x), k1 = score_key(q[u].y);
-          const uint32_t k2 = score_key(q[u].z), k3 = score_key(q[u].w);
-          list_append(ok && k0 >= T_lo, k0, 4 * i4 + 0, &s.misc[8], lkey, lidx, CAP);
-          list_append(ok && k1 >= T_lo, k1, 4 * i4 + 1, &s.misc[8], lkey, lidx, CAP);
-          list_append(ok && k2 >= T_lo, k2, 4 * i4 + 2, &s.misc[8], lkey, lidx, CAP);
-          list_append(ok && k3 >= T_lo, k3, 4 * i4 + 3, &s.misc[8], lkey, lidx, CAP);
+          kk[4 * u + 0] = ok ? score_key(q[u].x) : 0u;
+          kk[4 * u + 1] = ok ? score_key(q[u].y) : 0u;
+          kk[4 * u + 2] = ok ? score_key(q[u].z) : 0u;
+          kk[4 * u + 3] = ok ? score_key(q[u].w) : 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) jj[4 * u + e] = ok ? 4 * i4 + e : -1;
         }
+        place(kk, jj, 16);
       }
       done = 4 * n4;
     }
     for (int b0 = done; b0 < n; b0 += 4 * NT) {
-      float q[4];
+      uint32_t kk[4];
+      int jj[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = b0 + u * NT + t;
-        q[u] = j < n ? src[j] : 0.0f;
+        kk[u] = j < n ? score_key(src[j]) : 0u;
+        jj[u] = j < n ? j : -1;
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = b0 + u * NT + t;
-        const uint32_t key = score_key(q[u]);
-        list_append(j < n && key >= T_lo, key, (uint32_t)j, &s.misc[8], lkey, lidx, CAP);
-      }
+      place(kk, jj, 4);
     }
     __syncthreads();
     const int m = (int)s.misc[8];
@@ -550,7 +599,7 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t misc[kMiscWords];
-  __shared__ uint32_t sample[kSample];
+  __shared__ uint32_t sample[kMultiSample];
   Lds s{hist, scratch, misc};
   const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
@@ -559,13 +608,13 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
   if (n > k) {
     if (k <= kMultiCap) {
       const float* src = scores + (size_t)row * L_cap;
-      const int cnt = n <= kSample ? n : kSample;
-      constexpr int U = kSample / NT;
+      const int cnt = n <= kMultiSample ? n : kMultiSample;
+      constexpr int U = kMultiSample / NT;
       float v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = u * NT + t;
-        v[u] = i < cnt ? src[n <= kSample ? i : sample_pos(i, n)] : 0.0f;
+        v[u] = i < cnt ? src[n <= kMultiSample ? i : sample_pos<kMultiSample>(i, n)] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -575,7 +624,8 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
       __syncthreads();
       uint32_t take, eq;
       radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
-                       (uint32_t)(n <= kSample ? k : sample_rank(k, n)), s, T_lo, take, eq, 2);
+                       (uint32_t)(n <= kMultiSample ? k : sample_rank(k, n, kMultiSample)), s,
+                       T_lo, take, eq, 2);
       mode = kModeList;
     } else {
       mode = kModeExact;
@@ -713,7 +763,7 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   if (p.rows == 0) return;
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
-    opt_in_lds(topk_resident_kernel, kResLds);
+    opt_in_lds(topk_resident_kernel<kResThreads>, kResLds);
     opt_in_lds(topk_stream_kernel<512, kRowCap>, Stream512::kLds);
     opt_in_lds(topk_finish_kernel, kFinishLds);
     lds_opt_in = true;
@@ -725,7 +775,7 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
                          Stream512::kLds, st, scores, kv_len, S, L_cap, k, vec4, indices);
       return;
     case kPlanResident:
-      hipLaunchKernelGGL(topk_resident_kernel, dim3(p.rows), dim3(kResThreads), kResLds, st,
+      hipLaunchKernelGGL((topk_resident_kernel<kResThreads>), dim3(p.rows), dim3(kResThreads), kResLds, st,
                          scores, kv_len, S, L_cap, k, vec4, indices);
       return;
     default: {

@@ -113,27 +113,17 @@ def _sample_positions(n, sample=8192, block=256):
                            for b in range(nb)])
 
 
-def test_topk_sample_heavy_rows_use_exact_fallback(dsa):
+@pytest.mark.parametrize("B,S,L,k,sample", [(1, 8, 30000, 2048, 2048),     # LDS-resident rows
+                                            (1, 8, 40000, 2048, 4096),     # multi plan
+                                            (1, 130, 40000, 2048, 8192)])  # streaming rows
+def test_topk_sample_heavy_rows_use_exact_fallback(dsa, B, S, L, k, sample):
     # White-box: large scores exactly at the keys the threshold sample reads,
     # so fewer than k keys reach the estimated threshold and the exact
     # fallback must produce the result.
     r = rng(15)
-    for (B, S, L, k) in [(1, 8, 40000, 2048), (1, 130, 40000, 2048)]:
-        sc = r.integers(-100, 100, size=(B, S, L)).astype(np.float32)
-        for s in range(S):
-            n = L - S + s + 1
-            pos = _sample_positions(n)
-            sc[0, s, pos] = 1000.0 + r.integers(0, 50, size=pos.shape[0])
-        _check(dsa, torch.from_numpy(sc), [L], k, what="sample-heavy")
-
-
-def test_topk_very_long_rows_multi_plan(dsa):
-    # Rows above 512K keys with few rows use several workgroups per row.
-    r = rng(16)
-    L = 600000
-    _check(dsa, torch.from_numpy(r.standard_normal((1, 3, L)).astype(np.float32)), [L], 2048,
-           what="multi normal")
-    _check(dsa, integer_scores(r, (1, 2, L), -30, 30), [L, ], 2048, what="multi ties")
-    _check(dsa, torch.full((1, 2, L), -1.5), [L], 3000, what="multi tie storm")
-    _check(dsa, torch.from_numpy(r.standard_normal((2, 1, L)).astype(np.float32)), [L, 1000],
-           9000, what="multi k>cap ragged")
+    sc = r.integers(-100, 100, size=(B, S, L)).astype(np.float32)
+    for s in range(S):
+        n = L - S + s + 1
+        pos = _sample_positions(n, sample)
+        sc[0, s, pos] = 1000.0 + r.integers(0, 50, size=pos.shape[0])
+    _check(dsa, torch.from_numpy(sc), [L], k, what=f"sample-heavy/{sample}")
