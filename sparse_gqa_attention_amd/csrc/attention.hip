@@ -38,6 +38,8 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kTile = 32;
+// Running-maximum slack of the online softmax, in nats (see the tile loop).
+constexpr float kLazyNats = 8.0f;
 
 struct AttnParams {
   const void* q;
@@ -87,6 +89,18 @@ __device__ __forceinline__ void load_elems(const T* src, T (&dst)[N]) {
   __builtin_memcpy(dst, tmp, sizeof(dst));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4 (in that order).  p must be 8-byte aligned.
+template <typename T>
+__device__ __forceinline__ s16x4 ds_read_tr16x4(const T* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(p));
+}
+
 template <typename To, typename From>
 __device__ __forceinline__ To cvt(From x) {
   if constexpr (std::is_same<To, From>::value) return x;
@@ -100,13 +114,18 @@ struct AttnCfg {
   static constexpr int kQuarter = D / 4;             // elements of a row per lane
   static constexpr int kSteps = D / 32;              // QK K-steps (16-bit path)
   static constexpr int kDTiles = D / 16;             // O^T tiles of 16 dims
-  static constexpr int kVPad = kF32Path ? 4 : 8;     // LDS row padding (elements)
+  // LDS row padding (elements).  16-bit rows are padded by 32 bytes so that
+  // the 16 lanes of a transposing read (4 keys x 4 eight-byte chunks) hit
+  // distinct banks.
+  static constexpr int kVPad = kF32Path ? 4 : 16;
   static constexpr int kVStride = D + kVPad;
   static constexpr size_t kVBytes = (size_t)kAttnWaves * kTile * kVStride * sizeof(MPV);
+  static constexpr size_t kSclBytes = kInt8 ? (size_t)kAttnWaves * 64 * sizeof(float) : 0;
   static constexpr int kOStride = D + 4;              // padded O^T row (floats) in the merge
   static constexpr size_t kMergeBytes =
       ((size_t)kAttnWaves * 16 * kOStride + 4 * kAttnWaves * 16 + 2 * 16) * sizeof(float);
-  static constexpr size_t kLds = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+  static constexpr size_t kLds =
+      kVBytes + kSclBytes > kMergeBytes ? kVBytes + kSclBytes : kMergeBytes;
 };
 
 template <int D, typename QT, typename KVT, typename MQK, typename MPV>
@@ -159,6 +178,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   }
 
   MPV* vt = (MPV*)smem + (size_t)wave * kTile * Cfg::kVStride;
+  // INT8: per-key (softmax_scale * k_scale) for the 32 keys, then v_scale.
+  float* scl = (float*)(smem + Cfg::kVBytes) + wave * 64;
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x4 o[Cfg::kDTiles];
@@ -185,21 +206,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     load_elems<KVT, Q4>(krow_b, krb);
     load_elems<KVT, Q4>(vrow_a, vra);
     load_elems<KVT, Q4>(vrow_b, vrb);
-
-    // ---- V rows into this wave's LDS tile (converted to the PV operand type)
-    {
-      MPV va_c[Q4], vb_c[Q4];
-#pragma unroll
-      for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
-      constexpr int NV = Q4 * (int)sizeof(MPV) / 16;
-      uint4 ta[NV], tb[NV];
-      __builtin_memcpy(ta, va_c, sizeof(ta));
-      __builtin_memcpy(tb, vb_c, sizeof(tb));
-      uint4* da = (uint4*)(vt + (size_t)c16 * Cfg::kVStride + Q4 * g4);
-      uint4* db = (uint4*)(vt + (size_t)(16 + c16) * Cfg::kVStride + Q4 * g4);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) { da[i] = ta[i]; db[i] = tb[i]; }
+    // INT8: lane l fetches one scale of key (l % 32): k_scale for l < 32,
+    // v_scale above (lane l holds that key's index as ia or ib).
+    float my_scale = 0.0f;
+    if constexpr (Cfg::kInt8) {
+      const int si = (l & 16) ? ib : ia;
+      const bool sok = (l & 16) ? vb : va;
+      const float* sp = (l < 32) ? ksc : vsc;
+      if (sok) my_scale = sp[(size_t)si * p.H_kv];
     }
+    // Validity of keys 4*g4 + i (half a) and 16 + 4*g4 + i (half b): lanes
+    // 0..15 hold rows 0..15 of each half.
+    const uint32_t bits_a = ((uint32_t)__ballot(va) >> (4 * g4)) & 0xFu;
+    const uint32_t bits_b = ((uint32_t)__ballot(vb) >> (4 * g4)) & 0xFu;
 
     // ---- S^T = K . Q^T for both halves
     f32x4 sa = f32x4{}, sb = f32x4{};
@@ -225,55 +244,76 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       }
     }
 
+    // ---- V rows into this wave's LDS tile (converted to the PV operand type)
+    {
+      MPV va_c[Q4], vb_c[Q4];
+#pragma unroll
+      for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
+      constexpr int NV = Q4 * (int)sizeof(MPV) / 16;
+      uint4 ta[NV], tb[NV];
+      __builtin_memcpy(ta, va_c, sizeof(ta));
+      __builtin_memcpy(tb, vb_c, sizeof(tb));
+      uint4* da = (uint4*)(vt + (size_t)c16 * Cfg::kVStride + Q4 * g4);
+      uint4* db = (uint4*)(vt + (size_t)(16 + c16) * Cfg::kVStride + Q4 * g4);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) { da[i] = ta[i]; db[i] = tb[i]; }
+    }
+    if constexpr (Cfg::kInt8) scl[l] = (l < 32) ? my_scale * p.scale : my_scale;
+    // This wave's LDS writes must land before its reads below.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
     // ---- logits of keys 4*g4+i (half a) and 16+4*g4+i (half b), head c16
     float x[8];
-    float vs[8];
+    f32x4 vs_a, vs_b;
+    if constexpr (Cfg::kInt8) {
+      const f32x4 ks_a = *reinterpret_cast<const f32x4*>(scl + 4 * g4);
+      const f32x4 ks_b = *reinterpret_cast<const f32x4*>(scl + 16 + 4 * g4);
+      vs_a = *reinterpret_cast<const f32x4*>(scl + 32 + 4 * g4);
+      vs_b = *reinterpret_cast<const f32x4*>(scl + 48 + 4 * g4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int src = 4 * g4 + i;                 // lane holding that key row
-      const int ka_i = __shfl(ia, src, kWave);
-      const int kb_i = __shfl(ib, src, kWave);
-      const bool oka = __shfl((int)va, src, kWave) != 0;
-      const bool okb = __shfl((int)vb, src, kWave) != 0;
-      float fa = sa[i] * p.scale, fb = sb[i] * p.scale;
-      if constexpr (Cfg::kInt8) {
-        fa *= oka ? ksc[(size_t)ka_i * p.H_kv] : 0.0f;
-        fb *= okb ? ksc[(size_t)kb_i * p.H_kv] : 0.0f;
-        vs[i] = oka ? vsc[(size_t)ka_i * p.H_kv] : 0.0f;
-        vs[4 + i] = okb ? vsc[(size_t)kb_i * p.H_kv] : 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        x[i] = ((bits_a >> i) & 1u) ? sa[i] * ks_a[i] : -INFINITY;
+        x[4 + i] = ((bits_b >> i) & 1u) ? sb[i] * ks_b[i] : -INFINITY;
       }
-      x[i] = oka ? fa : -INFINITY;
-      x[4 + i] = okb ? fb : -INFINITY;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = ((bits_a >> i) & 1u) ? sa[i] * p.scale : -INFINITY;
+        x[4 + i] = ((bits_b >> i) & 1u) ? sb[i] * p.scale : -INFINITY;
+      }
     }
 
-    // ---- online softmax per head column (lanes c16, c16+16, c16+32, c16+48)
-    float tmax = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    // ---- online softmax per head column (lanes c16, c16+16, c16+32, c16+48).
+    // The reference maximum only moves when a tile's maximum exceeds it by
+    // more than kLazyNats, so most tiles skip the O rescale; weights are
+    // then at most e^kLazyNats, and the final O / L is unchanged.
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp_keep_subnormal(m_run - m_new);
+    const bool grow = tmax > m_run + kLazyNats;      // also the first valid key (m_run = -inf)
+    if (__ballot(grow) != 0) {                       // wave-uniform branch
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.0f : exp_keep_subnormal(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
     float pv[8];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = (x[i] == -INFINITY) ? 0.0f : exp_keep_subnormal(x[i] - m_new);
+      pv[i] = (x[i] == -INFINITY) ? 0.0f : exp_keep_subnormal(x[i] - m_run);
       psum += pv[i];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] *= alpha;
+    l_run += psum;
     if constexpr (Cfg::kInt8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] *= vs[i];
+      for (int i = 0; i < 4; ++i) { pv[i] *= vs_a[i]; pv[4 + i] *= vs_b[i]; }
     }
-
-    // V tile writes of this wave must land before its transposed reads.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- O^T += V^T . P^T
     if constexpr (Cfg::kF32Path) {
@@ -295,19 +335,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
         phi[j] = hi;
         plo[j] = from_f32<MPV>(pv[j] - to_f32(hi));
       }
+      // A operand (V^T, dims x keys) by transposing LDS reads: lane
+      // 16*g4 + 4*e + c addresses dims [4c, 4c+4) of key 4*g4 + e, and the
+      // read hands lane 16*g4 + n the dim-n element of keys 4*g4 + 0..3.
+      const MPV* tr_a = vt + (size_t)(4 * g4 + (c16 >> 2)) * Cfg::kVStride + 4 * (c16 & 3);
+      const MPV* tr_b = tr_a + 16 * Cfg::kVStride;
 #pragma unroll
       for (int dt = 0; dt < Cfg::kDTiles; ++dt) {
-        V8 a;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = (j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4);
-          a[j] = vt[(size_t)key * Cfg::kVStride + 16 * dt + c16];
-        }
+        const s16x4 lo = ds_read_tr16x4(tr_a + 16 * dt);
+        const s16x4 hi = ds_read_tr16x4(tr_b + 16 * dt);
+        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = mfma16x16x32(a, phi, o[dt]);
         o[dt] = mfma16x16x32(a, plo, o[dt]);
       }
     }
-    // Transposed reads must finish before the next tile overwrites the LDS.
+    // Reads of this tile must finish before the next tile overwrites the LDS.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -80,7 +80,7 @@ template <> struct vec8<_Float16> { typedef f16x8 type; };
 template <> struct vec8<__bf16> { typedef bf16x8 type; };
 
 // ------------------------------------------------------------------ exp
-// e^x for x <= 0 (and -inf), keeping FP32 subnormal results: a rise of the
+// e^x for x <= ~88 (and -inf), keeping FP32 subnormal results: a rise of the
 // running maximum by ~88 nats must leave e^-88 (~6e-39, subnormal) intact,
 // not flush it to zero.  2^y = 2^(y - n) * 2^n with n = floor(y): the
 // hardware exp2 only sees y - n in [0, 1) and ldexp produces the subnormal.

@@ -7,16 +7,24 @@
 // gfx950 design.  One v_mfma_f32_32x32x16 tile has 32 rows = two query
 // tokens x 16 indexer heads (fewer heads are zero-padded) and 32 columns =
 // 32 keys, so the per-head contraction is a dense MFMA and the weighted head
-// reduction reads straight out of the accumulator: each lane holds 8 heads of
-// one token for one key, multiplies them by the head weights, and one
-// cross-half exchange (lane l <-> l^32) completes the 16-head sum.  Lanes
-// 0..31 then hold token t0's scores for 32 consecutive keys and lanes 32..63
-// token t1's: one coalesced 128-byte store per half wave.
+// reduction reads straight out of the accumulator: rows are ordered so that
+// each lane holds all 16 heads of one token for one key and multiplies them
+// by the head weights in registers.  Lanes 0..31 then hold token t0's scores
+// for 32 consecutive keys and lanes 32..63 token t1's: one coalesced
+// 128-byte store per half wave.
 //
-// A workgroup (4 waves) owns a run of keys and 8*PAIRS query tokens; each
-// 64-key tile of key_state is staged once in LDS (16-byte chunks XOR-swizzled
-// by row so that the B-operand reads of 32 different keys hit different
-// banks) and read by all waves.  Query operands stay in registers.
+// A workgroup owns a run of up to KR keys and 2*PAIRS*WAVES query tokens (8
+// at decode, 32 at prefill).  The whole key run is copied into LDS once, by
+// direct global->LDS loads (16-byte chunks XOR-swizzled by row so that the
+// B-operand reads of different keys hit different banks), and every wave
+// multiplies its token pairs against all of it.  After that copy the
+// workgroup issues no vector-memory loads, only score stores: on gfx9 one
+// in-order counter tracks loads and stores alike, so a load issued behind
+// stores (a prefetch of the next key tile) would wait for those stores to be
+// acknowledged.  Query operands and head weights stay in registers.  Token
+// blocks are the fastest grid dimension and the XCD-aware renumbering below
+// keeps the workgroups sharing a key run on one XCD, so each key-state run is
+// fetched from HBM about once.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -24,32 +32,56 @@ namespace dsa {
 
 namespace {
 
-constexpr int kIdxThreads = 256;
-constexpr int kIdxTile = 64;   // keys staged in LDS per step
-
 template <typename T, int DI>
 struct IdxTraits {
   static constexpr int kSteps = DI / 16;        // K-steps of the 32x32x16 MFMA
   static constexpr int kChunks = DI / 8;        // 16-byte chunks per key row
-  static constexpr int kSwz = kChunks < 8 ? kChunks - 1 : 7;
+  // Stored position of 16-byte chunk c of run row r is c ^ swz(r).  A
+  // 128-bit LDS read by 16 lanes (rows r0..r0+15, one logical chunk) then
+  // touches 16 distinct 16-byte bank groups of a 256-byte bank window, and
+  // any 8 consecutive lanes touch 8 distinct groups of a 128-byte window.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (kChunks == 16) return r & 15;
+    else if constexpr (kChunks == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+  }
 };
 
-template <typename T, int DI, int PAIRS>
-__global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T, int DI, int PAIRS, int WAVES, int KR>
+__global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void indexer_score_kernel(
     const T* __restrict__ q_idx, const float* __restrict__ w_idx,
     const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
     int S, int H, int L_cap, int keys_per_wg, float* __restrict__ scores) {
   using Tr = IdxTraits<T, DI>;
   using V8 = typename vec8<T>::type;
-  constexpr int kTokPerWg = 8 * PAIRS;
-  __shared__ __attribute__((aligned(16))) uint4 tile[kIdxTile * Tr::kChunks];
+  constexpr int NT = WAVES * kWave;
+  constexpr int kTokPerWg = 2 * PAIRS * WAVES;
+  __shared__ __attribute__((aligned(16))) uint4 run[KR * Tr::kChunks];
 
-  const int b = blockIdx.z;
+  // Workgroups are handed to the 8 XCDs round-robin by linear id.  Renumber
+  // so that each XCD owns a contiguous range of (token block, key run, batch)
+  // tiles in token-fastest order: the token blocks that share a key run then
+  // run on one XCD and read it through that XCD's L2.
+  int tx = blockIdx.x, ty = blockIdx.y, tz = blockIdx.z;
+  {
+    const int nx = gridDim.x, nxy = gridDim.x * gridDim.y;
+    const int total = nxy * gridDim.z;
+    if ((total & 7) == 0) {
+      const int lin = blockIdx.x + nx * blockIdx.y + nxy * blockIdx.z;
+      const int logical = (lin & 7) * (total >> 3) + (lin >> 3);
+      tz = logical / nxy;
+      ty = (logical - tz * nxy) / nx;
+      tx = logical - tz * nxy - ty * nx;
+    }
+  }
+  const int b = tz;
   int kvl = kv_len[b];
   kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
-  const int j_begin = blockIdx.x * keys_per_wg;
+  const int j_begin = ty * keys_per_wg;
   const int j_end = min(j_begin + keys_per_wg, kvl);
-  const int s_first = blockIdx.y * kTokPerWg;
+  const int s_first = tx * kTokPerWg;
   // Keys beyond the last position of this block's tokens are never selected.
   const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
   if (j_begin >= j_end || j_begin > last_pos) return;
@@ -59,14 +91,34 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(
   const int half = l >> 5;     // 0: lanes 0..31, 1: lanes 32..63
   const int col = l & 31;
 
-  // A operands: row m = l%32 -> token (m/16), head m%16; k = 16*step + 8*half.
+  // ---- key run -> LDS.  Slot q holds chunk (q % kChunks) ^ swz(r) of
+  // run row r = q / kChunks; a wave fills 64 consecutive slots per load.
+  // Rows are rounded up to whole 32-key chunks; rows past the run repeat its
+  // last row (their scores are never stored).
+  {
+    const T* ks_b = key_state + (size_t)b * L_cap * DI;
+    const int nvec = ((j_end - j_begin + 31) & ~31) * Tr::kChunks;   // multiple of 64
+    for (int q0 = wave * kWave; q0 < nvec; q0 += NT) {
+      const int q = q0 + l;
+      const int r = q / Tr::kChunks, c = q % Tr::kChunks;
+      const int j = min(j_begin + r, j_end - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(ks_b + (size_t)j * DI + 8 * (c ^ Tr::swz(r))),
+                                       (lds_void*)(run + q0), 16, 0, 0);
+    }
+  }
+
+  // MFMA row m <-> token (m/4)%2 of the pair, head 4*(m/8) + m%4.  With the
+  // 32x32 accumulator layout (element v of lane l is row 8*(v/4) + 4*(l/32)
+  // + v%4) every lane then holds all 16 heads of one token, token l/32, as
+  // elements v = head.  A operand: lane l supplies row l%32, k = 16*step +
+  // 8*(l/32).
   V8 a[PAIRS][Tr::kSteps];
   float wv[PAIRS][16];
 #pragma unroll
   for (int p = 0; p < PAIRS; ++p) {
     const int s0 = s_first + wave * 2 * PAIRS + 2 * p;
     {
-      const int s = s0 + (col >> 4), h = col & 15;
+      const int s = s0 + ((col >> 2) & 1), h = 4 * (col >> 3) + (col & 3);
       const bool ok = (s < S) && (h < H);
       const T* src = q_idx + ((size_t)(b * S + (ok ? s : 0)) * H + (ok ? h : 0)) * DI;
 #pragma unroll
@@ -75,74 +127,79 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(
         a[p][st] = __builtin_bit_cast(V8, raw);
       }
     }
-    // Weights for the 16 accumulator elements of this lane:
-    // element v <-> row m = 8*(v/4) + 4*half + v%4.
+    const int s = s0 + half;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * half + (v & 3);
-      const int s = s0 + (m >> 4), h = m & 15;
-      wv[p][v] = (s < S && h < H) ? w_idx[(size_t)(b * S + s) * H + h] : 0.0f;
-    }
+    for (int v = 0; v < 16; ++v)
+      wv[p][v] = (s < S && v < H) ? w_idx[(size_t)(b * S + s) * H + v] : 0.0f;
   }
+  // Score row of each pair's token for this lane (lanes 0..31: t0, 32..63: t1).
+  float* srow[PAIRS];
+  bool s_ok[PAIRS];
+#pragma unroll
+  for (int p = 0; p < PAIRS; ++p) {
+    const int s = s_first + wave * 2 * PAIRS + 2 * p + half;
+    s_ok[p] = s < S;
+    srow[p] = scores + ((size_t)b * S + (s_ok[p] ? s : 0)) * L_cap + col;
+  }
+  wait_vmem();              // this wave's share of the run has landed in LDS
+  __syncthreads();          // ... and every other wave's
 
-  const T* ks_b = key_state + (size_t)b * L_cap * DI;
-  for (int j0 = j_begin; j0 < j_end; j0 += kIdxTile) {
-    // Stage key_state[j0 .. j0+63] (zero rows past j_end) into swizzled LDS.
-    for (int c = threadIdx.x; c < kIdxTile * Tr::kChunks; c += kIdxThreads) {
-      const int r = c / Tr::kChunks, ch = c % Tr::kChunks;
-      const int j = j0 + r;
-      uint4 v = (j < j_end) ? ld_vec<uint4>(ks_b + (size_t)j * DI + 8 * ch)
-                            : make_uint4(0, 0, 0, 0);
-      tile[r * Tr::kChunks + (ch ^ (r & Tr::kSwz))] = v;
+#pragma unroll 2
+  for (int jc = j_begin; jc < j_end; jc += 32) {
+    const int r = jc - j_begin + col;      // this lane's run row (B column n = col)
+    f32x16 acc[PAIRS];
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) acc[p] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st) {
+      const int ch = 2 * st + half;
+      V8 bop = __builtin_bit_cast(V8, run[r * Tr::kChunks + (ch ^ Tr::swz(r))]);
+#pragma unroll
+      for (int p = 0; p < PAIRS; ++p) acc[p] = mfma32x32x16(a[p][st], bop, acc[p]);
     }
-    __syncthreads();
+    const bool key_ok = jc + col < j_end;
 #pragma unroll
-    for (int ct = 0; ct < kIdxTile / 32; ++ct) {
-      const int r = ct * 32 + col;     // this lane's key row (B column n = col)
-      f32x16 acc[PAIRS];
+    for (int p = 0; p < PAIRS; ++p) {
+      // sum over the 16 heads (two chains of 8, then one add)
+      float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
-      for (int p = 0; p < PAIRS; ++p) acc[p] = f32x16{};
+      for (int v = 0; v < 8; ++v) part0 += wv[p][v] * acc[p][v];
 #pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) {
-        const int ch = 2 * st + half;
-        V8 bop = __builtin_bit_cast(V8, tile[r * Tr::kChunks + (ch ^ (r & Tr::kSwz))]);
-#pragma unroll
-        for (int p = 0; p < PAIRS; ++p) acc[p] = mfma32x32x16(a[p][st], bop, acc[p]);
-      }
-      const int j = j0 + ct * 32 + col;
-#pragma unroll
-      for (int p = 0; p < PAIRS; ++p) {
-        float part0 = 0.0f, part1 = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) part0 += wv[p][v] * acc[p][v];
-#pragma unroll
-        for (int v = 8; v < 16; ++v) part1 += wv[p][v] * acc[p][v];
-        // Lane l keeps token (half) and adds the other half's partial of it.
-        const float mine = half ? part1 : part0;
-        const float give = half ? part0 : part1;
-        const float total = mine + __shfl_xor(give, 32, kWave);
-        const int s = s_first + wave * 2 * PAIRS + 2 * p + half;
-        if (s < S && j < j_end) scores[((size_t)b * S + s) * L_cap + j] = total;
-      }
+      for (int v = 8; v < 16; ++v) part1 += wv[p][v] * acc[p][v];
+      const float total = part0 + part1;
+      if (s_ok[p] && key_ok) srow[p][jc] = total;
     }
-    __syncthreads();
   }
 }
 
-template <typename T, int DI, int PAIRS>
+template <typename T, int DI, int PAIRS, int WAVES, int KR>
 void launch_idx(const IndexerLaunch& a, hipStream_t st) {
-  dim3 grid(a.key_blocks, a.tok_blocks, a.B);
-  hipLaunchKernelGGL((indexer_score_kernel<T, DI, PAIRS>), grid, dim3(kIdxThreads), 0, st,
-                     (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
+  dim3 grid(a.tok_blocks, a.key_blocks, a.B);
+  hipLaunchKernelGGL((indexer_score_kernel<T, DI, PAIRS, WAVES, KR>), grid, dim3(WAVES * kWave), 0,
+                     st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
                      a.L_cap, a.keys_per_wg, a.scores);
 }
 
-template <typename T, int PAIRS>
+// Largest key run a workgroup keeps in LDS: 64 KB at prefill (two
+// workgroups per CU), 32 KB at decode.
+template <int DI> constexpr int kPrefillRun = 65536 / (2 * DI);
+template <int DI> constexpr int kDecodeRun = 32768 / (2 * DI);
+
+template <typename T, bool PREFILL>
 void launch_idx_d(const IndexerLaunch& a, hipStream_t st) {
   switch (a.D_idx) {
-    case 32: launch_idx<T, 32, PAIRS>(a, st); break;
-    case 64: launch_idx<T, 64, PAIRS>(a, st); break;
-    default: launch_idx<T, 128, PAIRS>(a, st); break;
+    case 32:
+      if (PREFILL) launch_idx<T, 32, 2, 8, kPrefillRun<32>>(a, st);
+      else launch_idx<T, 32, 1, 4, kDecodeRun<32>>(a, st);
+      break;
+    case 64:
+      if (PREFILL) launch_idx<T, 64, 2, 8, kPrefillRun<64>>(a, st);
+      else launch_idx<T, 64, 1, 4, kDecodeRun<64>>(a, st);
+      break;
+    default:   // one token pair per wave keeps the 128-dim operands in registers
+      if (PREFILL) launch_idx<T, 128, 1, 8, kPrefillRun<128>>(a, st);
+      else launch_idx<T, 128, 1, 4, kDecodeRun<128>>(a, st);
+      break;
   }
 }
 
@@ -153,24 +210,33 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
   a.B = B;
   a.S = S;
   a.D_idx = D_idx;
-  a.pairs = S > 8 ? 2 : 1;
-  const int tok_per_wg = 8 * a.pairs;
+  // Decode (S <= 8): 4 waves x 1 token pair.  Prefill: 8 waves x 2 pairs
+  // (1 pair for D_idx = 128), 32 tokens sharing every key run.
+  const bool prefill = S > 8;
+  a.prefill = prefill;
+  a.pairs = prefill && D_idx < 128 ? 2 : 1;
+  a.waves = prefill ? 8 : 4;
+  a.tile = (prefill ? 65536 : 32768) / (2 * D_idx);   // key-run capacity (LDS)
+  const int tok_per_wg = 2 * a.pairs * a.waves;
   a.tok_blocks = (S + tok_per_wg - 1) / tok_per_wg;
-  // Aim for ~1024 workgroups (4 per CU), 64..1024 keys each.
-  long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
-  int kpw = kIdxTile;
-  while (kpw < want && kpw < 1024) kpw *= 2;
-  a.keys_per_wg = kpw;
-  a.key_blocks = (max_kv_len + kpw - 1) / kpw;
+  // Aim for ~1024 workgroups (4 per CU); runs are whole 32-key chunks and
+  // fit the LDS capacity.
+  const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
+  long long kpw = ((want + 31) / 32) * 32;
+  if (kpw < 32) kpw = 32;
+  if (kpw > a.tile) kpw = a.tile;
+  a.keys_per_wg = (int)kpw;
+  a.key_blocks = (int)((max_kv_len + kpw - 1) / kpw);
   return a;
 }
 
 void launch_indexer(const IndexerLaunch& a, hipStream_t st) {
   if (a.key_blocks == 0 || a.tok_blocks == 0 || a.B == 0) return;
+  const bool prefill = a.prefill;
   if (a.bf16) {
-    if (a.pairs == 2) launch_idx_d<__bf16, 2>(a, st); else launch_idx_d<__bf16, 1>(a, st);
+    if (prefill) launch_idx_d<__bf16, true>(a, st); else launch_idx_d<__bf16, false>(a, st);
   } else {
-    if (a.pairs == 2) launch_idx_d<_Float16, 2>(a, st); else launch_idx_d<_Float16, 1>(a, st);
+    if (prefill) launch_idx_d<_Float16, true>(a, st); else launch_idx_d<_Float16, false>(a, st);
   }
 }
 

@@ -19,6 +19,8 @@ SMALL = [
     (1, 9, 16, 32, 1500, None, "f16"),
     (3, 8, 16, 64, 5000, [5000, 8, 4000], "bf16"),  # kv_len == S
     (1, 40, 12, 64, 700, None, "bf16"),
+    (1, 40, 16, 128, 900, None, "bf16"),          # prefill form, one token pair per wave
+    (2, 33, 5, 32, 1300, [1300, 1000], "f16"),    # prefill form, D_idx 32, ragged kv_len
 ]
 
 
