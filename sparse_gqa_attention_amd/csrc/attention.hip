@@ -510,11 +510,13 @@ void plan_attention(AttnLaunch& a, bool decode) {
     a.keys_per_split = a.k > 0 ? a.k : 1;
     return;
   }
-  // Aim for ~1024 workgroups; at least 128 keys (one tile per wave) per split,
-  // at most 64 splits (one merge lane per split).
+  // Aim for ~3072 workgroups: a whole number of dispatch rounds whether the
+  // kernel fits 3 or 4 workgroups per CU (3072 = 256 CUs x 3 x 4), so no
+  // round runs partly empty.  At least 128 keys (one tile per wave) per
+  // split, whole 32-key tiles, at most 64 splits (one merge lane per split).
   const long long rows_kv = (long long)a.B * a.S * a.H_kv;
-  long long kps = (a.k * rows_kv + 1023) / 1024;
-  kps = ((kps + 127) / 128) * 128;
+  long long kps = (a.k * rows_kv + 3071) / 3072;
+  kps = ((kps + kTile - 1) / kTile) * kTile;
   if (kps < 128) kps = 128;
   long long ns = (a.k + kps - 1) / kps;
   if (ns > 64) {
