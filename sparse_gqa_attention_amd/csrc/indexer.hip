@@ -117,20 +117,35 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void indexer_sco
 #pragma unroll
   for (int p = 0; p < PAIRS; ++p) {
     const int s0 = s_first + wave * 2 * PAIRS + 2 * p;
+    // Loads are unconditional from clamped addresses (no per-load branch);
+    // rows and heads out of range are zeroed afterwards.
     {
       const int s = s0 + ((col >> 2) & 1), h = 4 * (col >> 3) + (col & 3);
       const bool ok = (s < S) && (h < H);
-      const T* src = q_idx + ((size_t)(b * S + (ok ? s : 0)) * H + (ok ? h : 0)) * DI;
+      const T* src = q_idx + ((size_t)(b * S + min(s, S - 1)) * H + min(h, H - 1)) * DI;
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st) {
-        uint4 raw = ok ? ld_vec<uint4>(src + 16 * st + 8 * half) : make_uint4(0, 0, 0, 0);
+        uint4 raw = ld_vec<uint4>(src + 16 * st + 8 * half);
+        if (!ok) raw = make_uint4(0, 0, 0, 0);
         a[p][st] = __builtin_bit_cast(V8, raw);
       }
     }
     const int s = s0 + half;
+    const float* wrow = w_idx + (size_t)(b * S + min(s, S - 1)) * H;
+    if (H == 16) {                       // 64-byte aligned row: four 16-byte loads
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const f32x4 w4 = ld_vec<f32x4>(wrow + 4 * v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[p][4 * v4 + e] = w4[e];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) wv[p][v] = wrow[min(v, H - 1)];
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      wv[p][v] = (s < S && v < H) ? w_idx[(size_t)(b * S + s) * H + v] : 0.0f;
+      if (s >= S || v >= H) wv[p][v] = 0.0f;
   }
   // Score row of each pair's token for this lane (lanes 0..31: t0, 32..63: t1).
   float* srow[PAIRS];
