@@ -34,12 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "42c9938abb9b1784",
-    "spec_decode_32k": {"indexer": 5442335, "topk": 1416790, "attention": 16396799 + 1699642},
-    "decode_256k": {"indexer": 42142727, "topk": 227555 + 8795060 + 524358,
-                    "attention": 18617554 + 1699630},
-    "prefill_128k": {"indexer": 1772830243, "topk": 1156495606, "attention": 2395496552},
-    "int8_batched_decode_64k": {"attention": 1117615029 + 3346028},
+    "sources": "85f31d24df1d7c22",
+    "spec_decode_32k": {"indexer": 5431027, "topk": 1416774, "attention": 16382615 + 1700646},
+    "decode_256k": {"indexer": 42127818, "topk": 227301 + 8795785 + 524361, "attention": 18599302 + 1700666},
+    "prefill_128k": {"indexer": 2187158527, "topk": 1156417558, "attention": 2386535726},
+    "int8_batched_decode_64k": {"attention": 1149192037 + 9736040},
 }
 
 
@@ -96,6 +95,15 @@ def stage_bytes(w, kv_len):
     q = B * S * w.H_q * w.D * ELT[w.q_dtype]
     o = B * S * w.H_q * w.D * ELT[w.out_dtype]
     out["attention"] = gathered + q + o + B * S * k * 4
+    # KV-cache append of the step's S new tokens (measured separately, not
+    # part of the path below): new K/V and indexer keys read, cache rows written.
+    new_elt = ELT[w.kv_dtype] if w.kv_dtype != "i8" else ELT[w.q_dtype]
+    app = B * S * w.H_kv * w.D * (new_elt + ELT[w.kv_dtype]) * 2
+    if w.kv_dtype == "i8":
+        app += B * S * w.H_kv * 4 * 2
+    if w.has_indexer:
+        app += B * S * w.D_idx * ELT[w.idx_dtype] * 2
+    out["cache_append"] = app
     # Whole path without the score round trip (an artefact of the 4-call ABI).
     path = out["attention"]
     if w.has_indexer:
@@ -152,7 +160,7 @@ def main():
         sys.exit(2)
     import torch
     import sparse_gqa_attention_amd as dsa
-    from dsa_synth import BY_NAME, make_inputs
+    from dsa_synth import BY_NAME, make_inputs, make_new_tokens
 
     w = BY_NAME[args.workload]
     decode = w.name != "prefill_128k"
@@ -193,6 +201,19 @@ def main():
 
     stages = (["indexer", "topk"] if w.has_indexer else []) + ["attention"]
 
+    # KV-cache append of the step's new tokens (timed on its own; the path's
+    # step keeps the three stages above).
+    new_dtype = w.kv_dtype if w.kv_dtype != "i8" else w.q_dtype
+    nt = {kk: v.to(dev) for kk, v in make_new_tokens(B, S, w.H_kv, w.D, new_dtype,
+                                                      D_idx=w.D_idx or 64,
+                                                      idx_dtype=w.idx_dtype or "bf16").items()}
+
+    def append_stage(g):
+        dsa.dsa_cache_append(nt["k_new"], nt["v_new"], g["k_cache"], g["v_cache"], g["kv_len"],
+                             k_scale=g["k_scale"], v_scale=g["v_scale"],
+                             key_state_new=nt["key_state_new"] if w.has_indexer else None,
+                             key_state=g["key_state"] if w.has_indexer else None)
+
     def layer_pass(g):
         for st in stages:
             stage(st, g)
@@ -202,6 +223,7 @@ def main():
             layer_pass(g)
 
     stage_fns = {st: (lambda st=st: [stage(st, g) for g in layers]) for st in stages}
+    extra_fns = {"cache_append": lambda: [append_stage(g) for g in layers]}
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -238,7 +260,7 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     mode = "eager"
-    run_step, run_stage = step, dict(stage_fns)
+    run_step, run_stage = step, dict(stage_fns, **extra_fns)
     if not args.eager:
         # One step (every layer, every stage) captured as a HIP graph and
         # replayed; each stage alone (over every layer) is a graph of its own.
@@ -247,7 +269,7 @@ def main():
             s_cap.wait_stream(torch.cuda.current_stream())
             graphs = {}
             with torch.cuda.stream(s_cap):
-                for name, fn in [("step", step)] + list(stage_fns.items()):
+                for name, fn in [("step", step)] + list(stage_fns.items()) + list(extra_fns.items()):
                     fn()                                   # warm-up on the capture stream
                     torch.cuda.synchronize()
                     gph = torch.cuda.CUDAGraph()
@@ -257,19 +279,20 @@ def main():
             torch.cuda.current_stream().wait_stream(s_cap)
             torch.cuda.synchronize()
             run_step = graphs["step"].replay
-            run_stage = {st: graphs[st].replay for st in stages}
+            run_stage = {st: graphs[st].replay for st in list(stages) + list(extra_fns)}
             for _ in range(3):
                 run_step()
             torch.cuda.synchronize()
             mode = "hip_graph"
         except Exception as ex:     # capture unsupported here: time eager launches
             print(f"graph capture failed ({ex}); timing eager launches", file=sys.stderr)
-            run_step, run_stage = step, dict(stage_fns)
+            run_step, run_stage = step, dict(stage_fns, **extra_fns)
 
     # ---- timed region: K steps, then K replays of each stage alone
     ms_per_step = timed(run_step, K)
     us_per_layer = ms_per_step * 1e3 / n_layers
     stage_us = {st: timed(run_stage[st], K) * 1e3 / n_layers for st in stages}
+    extra_us = {st: timed(run_stage[st], K) * 1e3 / n_layers for st in extra_fns}
     dominant = max(stage_us, key=stage_us.get)
     dom_us = stage_us[dominant]
     eager_us = timed(step, max(3, K // 5)) * 1e3 / n_layers if mode != "eager" else us_per_layer
@@ -307,6 +330,10 @@ def main():
                      "traffic": traffic, "stage": dominant, "us_per_call": round(dom_us, 3),
                      "timing": f"{mode} replays of the {dominant} stage over all layers",
                      "bytes_per_call": sb[dominant]},
+        "extra_stages": {st: {"us_per_call": round(v, 3), "bytes_per_call": sb[st],
+                              "hbm_gbps": round(sb[st] / (v * 1e-6) / 1e9, 1),
+                              "note": "KV-cache append of the step's new tokens; not in value"}
+                         for st, v in extra_us.items()},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

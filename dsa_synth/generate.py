@@ -95,3 +95,42 @@ def indexer_like_scores(rng, shape, sigma=2100.0):
     """
     x = np.rint(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma))
     return torch.from_numpy(x.astype(np.float32))
+
+
+def make_append_inputs(B, S, H_kv, D, L_cap, new_dtype, kv_dtype, kv_len, D_idx=64,
+                       idx_dtype="bf16", seed=0, scale=1.0):
+    """Inputs of one KV-cache append: pre-filled caches plus the new tokens.
+
+    Draw order: k_cache, v_cache, (k_scale, v_scale), key_state, k_new, v_new,
+    key_state_new.  Caches hold generator values (N(0,1) or INT8 codes with
+    scales in [0.005, 0.05)); new K/V are N(0,1)*scale in new_dtype; indexer
+    keys are integers in [-8, 8].  kv_len is the post-append length list.
+    """
+    rng = np.random.default_rng(seed)
+    out = {}
+    if kv_dtype == "i8":
+        out["k_cache"] = torch.from_numpy(rng.integers(-127, 128, (B, L_cap, H_kv, D), dtype=np.int8))
+        out["v_cache"] = torch.from_numpy(rng.integers(-127, 128, (B, L_cap, H_kv, D), dtype=np.int8))
+        out["k_scale"] = torch.from_numpy(rng.uniform(0.005, 0.05, (B, L_cap, H_kv)).astype(np.float32))
+        out["v_scale"] = torch.from_numpy(rng.uniform(0.005, 0.05, (B, L_cap, H_kv)).astype(np.float32))
+    else:
+        out["k_cache"] = _normal(rng, (B, L_cap, H_kv, D), kv_dtype)
+        out["v_cache"] = _normal(rng, (B, L_cap, H_kv, D), kv_dtype)
+        out["k_scale"] = out["v_scale"] = None
+    out["key_state"] = _int_uniform(rng, -8, 8, (B, L_cap, D_idx), idx_dtype)
+    kn = rng.standard_normal(size=(B, S, H_kv, D), dtype=np.float32) * np.float32(scale)
+    vn = rng.standard_normal(size=(B, S, H_kv, D), dtype=np.float32) * np.float32(scale)
+    out["k_new"] = torch.from_numpy(kn).to(_TORCH[new_dtype])
+    out["v_new"] = torch.from_numpy(vn).to(_TORCH[new_dtype])
+    out["key_state_new"] = _int_uniform(rng, -8, 8, (B, S, D_idx), idx_dtype)
+    out["kv_len"] = torch.tensor(list(kv_len), dtype=torch.int32)
+    return out
+
+
+def make_new_tokens(B, S, H_kv, D, new_dtype, D_idx=64, idx_dtype="bf16", seed=0):
+    """New K/V rows [B, S, H_kv, D] (N(0,1) in new_dtype) and indexer keys
+    [B, S, D_idx] (integers in [-8, 8]) for one append step."""
+    rng = np.random.default_rng(seed)
+    return {"k_new": _normal(rng, (B, S, H_kv, D), new_dtype),
+            "v_new": _normal(rng, (B, S, H_kv, D), new_dtype),
+            "key_state_new": _int_uniform(rng, -8, 8, (B, S, D_idx), idx_dtype)}

@@ -152,6 +152,41 @@ dsa_status dsa_attention_decode(const dsa_attention_args* args, void* workspace,
 dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * KV-cache append (ORT PR #33997, file table: cache writes precede the
+ * attention kernels; ORT PR #33802, Summary item 1: an INT8 KV cache with one
+ * FP32 scale per token per KV head).  Writes the S new tokens of every
+ * sequence into the caches: token s of sequence b goes to position
+ * pos = kv_len[b] - S + s, where kv_len is the length AFTER the append (the
+ * same kv_len the indexer, top-k and attention calls of that step take);
+ * tokens with pos outside [0, L_cap) are skipped.
+ *   k_new, v_new    [B, S, H_kv, D]      new_dtype (F32, F16 or BF16)
+ *   k_cache, v_cache [B, L_cap, H_kv, D] kv_dtype (F32, F16, BF16 or I8)
+ *   k_scale, v_scale [B, L_cap, H_kv]    FP32, written for DSA_I8, NULL
+ *                                        otherwise
+ *   key_state_new   [B, S, D_idx]        idx_dtype (F16 or BF16), copied to
+ *   key_state       [B, L_cap, D_idx]    idx_dtype; both NULL to skip
+ *   kv_len          [B]                  int32, device
+ * Float caches store each value rounded once to nearest-even.  An INT8 cache
+ * stores, per (token, KV head) row x of D values, in FP32 arithmetic:
+ *   scale = amax / 127 with amax = max_d |x_d|, and
+ *   code_d = clamp(rint(x_d / scale), -127, 127)   (ties to even),
+ * both quotients correctly rounded; an all-zero row stores scale 0 and zero
+ * codes.  Non-finite inputs are not supported.
+ * Supported: D in {64, 128}; D_idx in {32, 64, 128}; an F32 cache needs F32
+ * new values.  Rows written by one call must not overlap (unique positions).
+ */
+typedef struct {
+  const void* k_new;  const void* v_new;  int32_t new_dtype;
+  void* k_cache;      void* v_cache;      int32_t kv_dtype;
+  float* k_scale;     float* v_scale;
+  const void* key_state_new; void* key_state; int32_t idx_dtype;
+  const int32_t* kv_len;
+  int32_t B, S, H_kv, D, D_idx, L_cap;
+} dsa_cache_append_args;
+
+dsa_status dsa_cache_append(const dsa_cache_append_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

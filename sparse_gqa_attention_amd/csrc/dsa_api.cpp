@@ -213,4 +213,52 @@ dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace
   return run_attention(args, workspace, workspace_bytes, stream, false);
 }
 
+dsa_status dsa_cache_append(const dsa_cache_append_args* a, void* stream) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->B < 0 || a->S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", a->B, a->S);
+  if (a->L_cap < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "L_cap=%d must be >= 1", a->L_cap);
+  if (a->H_kv < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "H_kv=%d must be >= 1", a->H_kv);
+  if (a->D != 64 && a->D != 128) return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d not in {64, 128}", a->D);
+  const int nd = a->new_dtype, kd = a->kv_dtype;
+  if (nd != DSA_F32 && nd != DSA_F16 && nd != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "new K/V dtype %s not in {F32, F16, BF16}", dtype_name(nd));
+  if (kd != DSA_F32 && kd != DSA_F16 && kd != DSA_BF16 && kd != DSA_I8)
+    return fail(DSA_ERR_UNSUPPORTED, "cache dtype %s unsupported", dtype_name(kd));
+  if (kd == DSA_F32 && nd != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "an F32 cache needs F32 new values, got %s", dtype_name(nd));
+  const bool has_ks = a->key_state != nullptr || a->key_state_new != nullptr;
+  if (has_ks) {
+    if (a->D_idx != 32 && a->D_idx != 64 && a->D_idx != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "indexer dim D_idx=%d not in {32, 64, 128}", a->D_idx);
+    if (a->idx_dtype != DSA_F16 && a->idx_dtype != DSA_BF16)
+      return fail(DSA_ERR_UNSUPPORTED, "key-state dtype %s not in {F16, BF16}", dtype_name(a->idx_dtype));
+  }
+  if ((long long)a->B * a->S == 0) return ok();
+  CHECK(check_ptr(a->k_new, "k_new"));
+  CHECK(check_ptr(a->v_new, "v_new"));
+  CHECK(check_ptr(a->k_cache, "k_cache"));
+  CHECK(check_ptr(a->v_cache, "v_cache"));
+  CHECK(check_ptr(a->kv_len, "kv_len"));
+  if (kd == DSA_I8) {
+    CHECK(check_ptr(a->k_scale, "k_scale"));
+    CHECK(check_ptr(a->v_scale, "v_scale"));
+  } else if (a->k_scale || a->v_scale) {
+    return fail(DSA_ERR_INVALID_ARGUMENT, "k_scale/v_scale must be NULL for a %s cache", dtype_name(kd));
+  }
+  if (has_ks) {
+    CHECK(check_ptr(a->key_state_new, "key_state_new"));
+    CHECK(check_ptr(a->key_state, "key_state"));
+  }
+  dsa::CacheAppendLaunch l{};
+  l.k_new = a->k_new; l.v_new = a->v_new; l.k_cache = a->k_cache; l.v_cache = a->v_cache;
+  l.k_scale = a->k_scale; l.v_scale = a->v_scale;
+  l.key_state_new = has_ks ? a->key_state_new : nullptr;
+  l.key_state = has_ks ? a->key_state : nullptr;
+  l.kv_len = a->kv_len; l.new_dtype = nd; l.kv_dtype = kd;
+  l.B = a->B; l.S = a->S; l.H_kv = a->H_kv; l.D = a->D; l.D_idx = a->D_idx; l.L_cap = a->L_cap;
+  (void)hipGetLastError();
+  dsa::launch_cache_append(l, (hipStream_t)stream);
+  return hip_result("dsa_cache_append");
+}
+
 }  // extern "C"

@@ -65,4 +65,20 @@ void plan_attention(AttnLaunch& a, bool decode);
 size_t attention_partials_bytes(const AttnLaunch& a);
 void launch_attention(const AttnLaunch& a, hipStream_t st);
 
+// ---------------------------------------------------------------- cache append
+struct CacheAppendLaunch {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  const void* key_state_new;
+  void* key_state;          // null: no key-state rows
+  const int32_t* kv_len;
+  int new_dtype, kv_dtype;
+  int B, S, H_kv, D, D_idx, L_cap;
+};
+void launch_cache_append(const CacheAppendLaunch& a, hipStream_t st);
+
 }  // namespace dsa

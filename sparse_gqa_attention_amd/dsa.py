@@ -22,7 +22,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
 
 EXPORTS = ("dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "dsa_attention_workspace_bytes",
-           "dsa_attention_decode", "dsa_attention_prefill")
+           "dsa_attention_decode", "dsa_attention_prefill", "dsa_cache_append")
 
 
 class DsaError(RuntimeError):
@@ -43,6 +43,18 @@ class AttentionArgs(ctypes.Structure):
                 ("H_kv", ctypes.c_int32), ("D", ctypes.c_int32), ("L_cap", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32)]
+
+
+class CacheAppendArgs(ctypes.Structure):
+    """Mirror of dsa_cache_append_args."""
+    _fields_ = [("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("new_dtype", ctypes.c_int32),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("kv_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("key_state_new", ctypes.c_void_p), ("key_state", ctypes.c_void_p),
+                ("idx_dtype", ctypes.c_int32),
+                ("kv_len", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("D_idx", ctypes.c_int32), ("L_cap", ctypes.c_int32)]
 
 
 def _load():
@@ -67,6 +79,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = i32
         f.argtypes = [ctypes.POINTER(AttentionArgs), vp, sz, vp]
+    lib.dsa_cache_append.restype = i32
+    lib.dsa_cache_append.argtypes = [ctypes.POINTER(CacheAppendArgs), vp]
     return lib
 
 
@@ -189,3 +203,31 @@ def dsa_attention_prefill(q, k_cache, v_cache, indices, kv_len, out, k_scale=Non
 
 def default_softmax_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# ------------------------------------------------------------------ cache append
+def cache_append_args(k_new, v_new, k_cache, v_cache, kv_len, k_scale=None, v_scale=None,
+                      key_state_new=None, key_state=None):
+    B, S, H_kv, D = k_new.shape
+    a = CacheAppendArgs()
+    a.k_new, a.v_new, a.new_dtype = k_new.data_ptr(), v_new.data_ptr(), _DTYPE_CODE[k_new.dtype]
+    a.k_cache, a.v_cache, a.kv_dtype = k_cache.data_ptr(), v_cache.data_ptr(), _DTYPE_CODE[k_cache.dtype]
+    a.k_scale = None if k_scale is None else k_scale.data_ptr()
+    a.v_scale = None if v_scale is None else v_scale.data_ptr()
+    if key_state is not None:
+        a.key_state_new, a.key_state = key_state_new.data_ptr(), key_state.data_ptr()
+        a.idx_dtype, a.D_idx = _DTYPE_CODE[key_state.dtype], key_state.shape[-1]
+    a.kv_len = kv_len.data_ptr()
+    a.B, a.S, a.H_kv, a.D, a.L_cap = B, S, H_kv, D, k_cache.shape[1]
+    return a
+
+
+def dsa_cache_append(k_new, v_new, k_cache, v_cache, kv_len, k_scale=None, v_scale=None,
+                     key_state_new=None, key_state=None, stream=None):
+    """Write the S new tokens at kv_len[b] - S + s (INT8 caches: quantised); see include/dsa.h."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (kv_len, "kv_len")):
+        _gpu(t, n)
+    a = cache_append_args(k_new, v_new, k_cache, v_cache, kv_len, k_scale, v_scale,
+                          key_state_new, key_state)
+    _check(LIB.dsa_cache_append(ctypes.byref(a), _stream(stream)))

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_and_library_agree(dsa):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     lib = ctypes.CDLL(LIBPATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -135,6 +135,38 @@ def test_attention_validation(dsa):
     assert call(a, wsb=need - 1) == _status("WS")
     assert call(a, ws=None, wsb=need) == _status("INVALID")
     assert call(_attn(dsa, B=0, q=None, out=None)) == 0
+
+
+def _append(dsa, **kw):
+    a = dsa.dsa.CacheAppendArgs()
+    base = dict(k_new=A16, v_new=A16, new_dtype=2, k_cache=A16, v_cache=A16, kv_dtype=3,
+                k_scale=A16, v_scale=A16, key_state_new=A16, key_state=A16, idx_dtype=2,
+                kv_len=A16, B=8, S=1, H_kv=8, D=128, D_idx=64, L_cap=65536)
+    base.update(kw)
+    for f, v in base.items():
+        setattr(a, f, v)
+    return a
+
+
+def test_cache_append_validation(dsa):
+    L = dsa.LIB
+    call = lambda a: L.dsa_cache_append(ctypes.byref(a), None)
+    bad = [
+        (dict(D=96), "UNSUPPORTED"), (dict(H_kv=0), "INVALID"), (dict(L_cap=0), "INVALID"),
+        (dict(B=-1), "INVALID"),
+        (dict(new_dtype=3), "UNSUPPORTED"),                # INT8 new values
+        (dict(kv_dtype=0), "UNSUPPORTED"),                 # F32 cache from BF16 values
+        (dict(kv_dtype=5), "UNSUPPORTED"),
+        (dict(kv_dtype=1), "INVALID"),                     # scales with a float cache
+        (dict(k_scale=None), "INVALID"),                   # INT8 cache without scales
+        (dict(v_scale=MIS), "MISALIGNED"),
+        (dict(D_idx=48), "UNSUPPORTED"), (dict(idx_dtype=0), "UNSUPPORTED"),
+        (dict(key_state=None), "INVALID"),                 # key-state source without target
+        (dict(k_new=MIS), "MISALIGNED"), (dict(kv_len=None), "INVALID"),
+    ]
+    for kw, want in bad:
+        assert call(_append(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
+    assert call(_append(dsa, S=0, k_new=None, v_new=None)) == 0   # nothing to append
 
 
 def test_error_text_is_thread_local_and_cleared(dsa):
