@@ -163,7 +163,8 @@ def main():
     from dsa_synth import BY_NAME, make_inputs, make_new_tokens
 
     w = BY_NAME[args.workload]
-    decode = w.name != "prefill_128k"
+    decode = w.decode_form
+    mx = w.max_kv_len          # runtime capacity bound that sizes the launch grids
     x = make_inputs(w)
     kv_len = x["kv_len"].tolist()
     dev = torch.device("cuda:0")
@@ -184,20 +185,21 @@ def main():
         topk_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     g0 = layers[0]
     a0 = dsa.attention_args(g0["q"], g0["k_cache"], g0["v_cache"], idx, g0["kv_len"], out,
-                            g0["k_scale"], g0["v_scale"])
+                            g0["k_scale"], g0["v_scale"], max_kv_len=w.max_kv_len)
     attn_ws = torch.empty(max(dsa.dsa_attention_workspace_bytes(a0, decode), 16),
                           dtype=torch.uint8, device=dev)
     attn = dsa.dsa_attention_decode if decode else dsa.dsa_attention_prefill
 
     def stage(name, g):
         if name == "indexer":
-            dsa.dsa_indexer_score(g["q_idx"], g["w_idx"], g["key_state"], g["kv_len"], scores)
+            dsa.dsa_indexer_score(g["q_idx"], g["w_idx"], g["key_state"], g["kv_len"], scores,
+                                  max_kv_len=mx)
         elif name == "topk":
-            dsa.dsa_topk(scores, g["kv_len"], w.k, idx, workspace=topk_ws)
+            dsa.dsa_topk(scores, g["kv_len"], w.k, idx, workspace=topk_ws, max_kv_len=mx)
         else:
             ind = idx if w.has_indexer else g["indices"]
             attn(g["q"], g["k_cache"], g["v_cache"], ind, g["kv_len"], out,
-                 k_scale=g["k_scale"], v_scale=g["v_scale"], workspace=attn_ws)
+                 k_scale=g["k_scale"], v_scale=g["v_scale"], workspace=attn_ws, max_kv_len=mx)
 
     stages = (["indexer", "topk"] if w.has_indexer else []) + ["attention"]
 
@@ -319,7 +321,9 @@ def main():
                    "D": w.D, "k": w.k, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
                    "out_dtype": w.out_dtype, "indexer": (f"{w.H_idx}x{w.D_idx}"
                                                          if w.has_indexer else None),
-                   "layers_per_step": n_layers, "attention_form": "decode" if decode else "prefill"},
+                   "layers_per_step": n_layers, "attention_form": "decode" if decode else "prefill",
+                   "kv_len": kv_len if w.kv_len is not None else "L for every sequence",
+                   "max_kv_len": mx},
         "tokens_per_s": round(B * S / (us_per_layer * 1e-6), 1),
         "launch_mode": mode,
         "eager_us_per_layer": round(eager_us, 3),

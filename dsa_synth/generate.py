@@ -73,7 +73,7 @@ def make_inputs(w: Workload, seed=None, kv_len=None):
         out["k_scale"] = None
         out["v_scale"] = None
     if kv_len is None:
-        kv_len = [L] * B
+        kv_len = w.live_lengths
     out["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)
     if not w.has_indexer:
         # Dense selection: every cached key of the row, in ascending order.

@@ -29,7 +29,22 @@ class Workload:
     H_idx: Optional[int] = None   # indexer heads (None: no indexer, dense selection)
     D_idx: Optional[int] = None   # indexer dim
     idx_dtype: str = "bf16"
+    kv_len: Optional[tuple] = None   # per-sequence live length (None: every sequence full)
     note: str = field(default="", compare=False)
+
+    @property
+    def live_lengths(self):
+        return list(self.kv_len) if self.kv_len is not None else [self.L] * self.B
+
+    @property
+    def max_kv_len(self) -> int:
+        """Runtime capacity bound handed to the launches (<= L, the cache capacity)."""
+        return max(self.live_lengths)
+
+    @property
+    def decode_form(self) -> bool:
+        """Split-K decode attention for short query runs, prefill form otherwise."""
+        return self.S <= 16
 
     @property
     def has_indexer(self) -> bool:
@@ -69,8 +84,23 @@ DECODE_256K = Workload(
     q_dtype="bf16", kv_dtype="f16", out_dtype="bf16", k=2048, H_idx=16, D_idx=64,
     note="8 tokens at 262136..262143, FP16 KV, 128 chunks of 2048 keys")
 
+RAGGED_DECODE_256K = Workload(
+    name="ragged_decode_256k", seed=6, B=4, S=8, L=262144, H_q=24, H_kv=2, D=128,
+    q_dtype="bf16", kv_dtype="f16", out_dtype="bf16", k=2048, H_idx=16, D_idx=64,
+    kv_len=(200000, 70001, 9000, 131072),
+    note="4 sequences of different live lengths in a 256K-capacity cache; launches sized "
+         "by the runtime bound max(kv_len) = 200000")
+
+RAGGED_PREFILL_64K = Workload(
+    name="ragged_prefill_64k", seed=7, B=3, S=512, L=65536, H_q=24, H_kv=2, D=128,
+    q_dtype="bf16", kv_dtype="bf16", out_dtype="bf16", k=2048, H_idx=16, D_idx=64,
+    kv_len=(65536, 20000, 512),
+    note="512-token prefill chunks of 3 sequences: after 65024 and 19488 cached tokens, and "
+         "a fresh sequence (kv_len == S)")
+
 ALL = (TINY_DECODE, SPEC_DECODE_32K, PREFILL_128K, INT8_DECODE_64K, DECODE_256K)
-BY_NAME = {w.name: w for w in ALL}
+RAGGED = (RAGGED_DECODE_256K, RAGGED_PREFILL_64K)
+BY_NAME = {w.name: w for w in ALL + RAGGED}
 
 
 def scaled(w: Workload, **overrides) -> Workload:

@@ -29,27 +29,29 @@ def upload(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
-def run_indexer(dsa, g, L):
+def run_indexer(dsa, g, L, max_kv_len=None):
     q = g["q_idx"]
     B, S = q.shape[0], q.shape[1]
     scores = torch.full((B, S, L), float("nan"), dtype=torch.float32, device=DEV)
-    dsa.dsa_indexer_score(q, g["w_idx"], g["key_state"], g["kv_len"], scores)
+    dsa.dsa_indexer_score(q, g["w_idx"], g["key_state"], g["kv_len"], scores,
+                          max_kv_len=max_kv_len)
     return scores
 
 
-def run_topk(dsa, scores, kv_len, k):
+def run_topk(dsa, scores, kv_len, k, max_kv_len=None):
     B, S, _ = scores.shape
     idx = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
-    dsa.dsa_topk(scores, kv_len, k, idx)
+    dsa.dsa_topk(scores, kv_len, k, idx, max_kv_len=max_kv_len)
     return idx
 
 
-def run_attention(dsa, g, indices, out_dtype, decode=True, scale=0.0):
+def run_attention(dsa, g, indices, out_dtype, decode=True, scale=0.0, max_kv_len=None):
     q = g["q"]
     out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
     fn = dsa.dsa_attention_decode if decode else dsa.dsa_attention_prefill
     fn(q, g["k_cache"], g["v_cache"], indices, g["kv_len"], out,
-       k_scale=g.get("k_scale"), v_scale=g.get("v_scale"), softmax_scale=scale)
+       k_scale=g.get("k_scale"), v_scale=g.get("v_scale"), softmax_scale=scale,
+       max_kv_len=max_kv_len)
     return out
 
 

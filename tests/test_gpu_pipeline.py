@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from dsa_synth import ALL, make_inputs, torch_dtype
+from dsa_synth import ALL, RAGGED, make_inputs, torch_dtype
 from gpu_util import (DEV, dsa, first_mismatch, run_attention, run_indexer,  # noqa: F401
                       run_topk, say, upload)
 from parity import assert_output_close
@@ -20,22 +20,27 @@ SAMPLE_ROWS = {
     "prefill_128k": [(0, 0), (0, 1), (0, 777), (0, 1024), (0, 2047)],
     "int8_batched_decode_64k": [(0, 0), (5, 0)],
     "decode_256k": None,
+    # ragged batches: rows of every sequence, including the first token of a
+    # fresh sequence (one candidate key) and sequences far below capacity
+    "ragged_decode_256k": [(0, 0), (0, 7), (1, 3), (2, 0), (2, 7), (3, 5)],
+    "ragged_prefill_64k": [(0, 0), (0, 511), (1, 100), (1, 511), (2, 0), (2, 1), (2, 511)],
 }
 
 
-@pytest.mark.parametrize("wl", ALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", ALL + RAGGED, ids=lambda w: w.name)
 def test_pipeline_full_size(dsa, wl):
-    say(f"pipeline {wl.name}")
+    say(f"pipeline {wl.name} kv_len={wl.live_lengths} max_kv_len={wl.max_kv_len}")
     x = make_inputs(wl)
     g = upload(x)
     B, S, L = wl.B, wl.S, wl.L
-    decode = wl.name != "prefill_128k"
+    decode = wl.decode_form
+    mx = wl.max_kv_len
     if wl.has_indexer:
-        scores = run_indexer(dsa, g, L)
-        idx = run_topk(dsa, scores, g["kv_len"], wl.k)
+        scores = run_indexer(dsa, g, L, max_kv_len=mx)
+        idx = run_topk(dsa, scores, g["kv_len"], wl.k, max_kv_len=mx)
     else:
         scores, idx = None, g["indices"]
-    out = run_attention(dsa, g, idx, torch_dtype(wl.out_dtype), decode=decode)
+    out = run_attention(dsa, g, idx, torch_dtype(wl.out_dtype), decode=decode, max_kv_len=mx)
     torch.cuda.synchronize()
 
     rows = SAMPLE_ROWS[wl.name] or [(b, s) for b in range(B) for s in range(S)]
