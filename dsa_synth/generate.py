@@ -134,3 +134,25 @@ def make_new_tokens(B, S, H_kv, D, new_dtype, D_idx=64, idx_dtype="bf16", seed=0
     return {"k_new": _normal(rng, (B, S, H_kv, D), new_dtype),
             "v_new": _normal(rng, (B, S, H_kv, D), new_dtype),
             "key_state_new": _int_uniform(rng, -8, 8, (B, S, D_idx), idx_dtype)}
+
+
+def rope_tables(max_pos, D, base=1.0e6):
+    """Caller-side FP32 rotary tables [max_pos, D/2]: cos and sin of
+    p * base**(-2i/D), evaluated in FP64 and rounded to FP32."""
+    inv = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
+def make_rope_inputs(B, S, H, D, max_pos, x_dtype, kv_len, seed=0, base=1.0e6):
+    """Inputs of one RMSNorm + rotary call: head vectors x [B, S, H, D]
+    (N(0,1) times a per-head spread in [0.5, 8], rounded to x_dtype), the
+    FP32 norm weight [D] in [0.5, 1.5), the FP32 rotary tables and kv_len."""
+    rng = np.random.default_rng(seed)
+    spread = rng.uniform(0.5, 8.0, size=(1, 1, H, 1)).astype(np.float32)
+    x = rng.standard_normal(size=(B, S, H, D), dtype=np.float32) * spread
+    gamma = rng.uniform(0.5, 1.5, size=(D,)).astype(np.float32)
+    cos, sin = rope_tables(max_pos, D, base)
+    return {"x": torch.from_numpy(x).to(_TORCH[x_dtype]), "gamma": torch.from_numpy(gamma),
+            "cos": cos, "sin": sin, "kv_len": torch.tensor(list(kv_len), dtype=torch.int32)}
