@@ -104,6 +104,13 @@ def stage_bytes(w, kv_len):
     if w.has_indexer:
         app += B * S * w.D_idx * ELT[w.idx_dtype] * 2
     out["cache_append"] = app
+    # RMSNorm + rotary of the step's query, key and indexer-query heads
+    # (measured separately): head vectors read and written, tables' rows read.
+    out_elt = 2                                  # 16-bit output
+    rope = B * S * (w.H_q + w.H_kv) * w.D * (ELT[w.q_dtype] + out_elt) + B * S * w.D * 4 * 2
+    if w.has_indexer:
+        rope += B * S * w.H_idx * w.D_idx * (ELT[w.idx_dtype] + out_elt) + B * S * w.D_idx * 4 * 2
+    out["rmsnorm_rope"] = rope
     # Whole path without the score round trip (an artefact of the 4-call ABI).
     path = out["attention"]
     if w.has_indexer:
@@ -160,7 +167,7 @@ def main():
         sys.exit(2)
     import torch
     import sparse_gqa_attention_amd as dsa
-    from dsa_synth import BY_NAME, make_inputs, make_new_tokens
+    from dsa_synth import BY_NAME, make_inputs, make_new_tokens, make_rope_inputs
 
     w = BY_NAME[args.workload]
     decode = w.decode_form
@@ -225,7 +232,23 @@ def main():
             layer_pass(g)
 
     stage_fns = {st: (lambda st=st: [stage(st, g) for g in layers]) for st in stages}
-    extra_fns = {"cache_append": lambda: [append_stage(g) for g in layers]}
+    # RMSNorm + rotary of the step's heads: query (-> q dtype of the path),
+    # key (-> new K) and indexer query, FP16 output (BF16 for a BF16 path).
+    rope_out = torch.float16 if w.q_dtype != "bf16" or w.kv_dtype == "f16" else torch.bfloat16
+    rope_sets = []
+    for H_, D_, seed_ in [(w.H_q, w.D, 21), (w.H_kv, w.D, 22)] + (
+            [(w.H_idx, w.D_idx, 23)] if w.has_indexer else []):
+        ri = {kk: v.to(dev) for kk, v in make_rope_inputs(
+            B, S, H_, D_, L, "bf16" if w.q_dtype != "f32" else "f32", kv_len, seed=seed_).items()}
+        ri["out"] = torch.empty_like(ri["x"], dtype=rope_out)
+        rope_sets.append(ri)
+
+    def rope_stage():
+        for ri in rope_sets:
+            dsa.dsa_rmsnorm_rope(ri["x"], ri["gamma"], ri["cos"], ri["sin"], ri["kv_len"], ri["out"])
+
+    extra_fns = {"cache_append": lambda: [append_stage(g) for g in layers],
+                 "rmsnorm_rope": lambda: [rope_stage() for _ in layers]}
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -336,7 +359,10 @@ def main():
                      "bytes_per_call": sb[dominant]},
         "extra_stages": {st: {"us_per_call": round(v, 3), "bytes_per_call": sb[st],
                               "hbm_gbps": round(sb[st] / (v * 1e-6) / 1e9, 1),
-                              "note": "KV-cache append of the step's new tokens; not in value"}
+                              "note": {"cache_append": "KV-cache append of the step's new tokens",
+                                       "rmsnorm_rope": "RMSNorm + rotary of the step's query, key "
+                                                       "and indexer-query heads"}[st]
+                                      + "; measured on its own, not in value"}
                          for st, v in extra_us.items()},
     }
     if not args.no_cpu_baseline:

@@ -187,6 +187,39 @@ typedef struct {
 
 dsa_status dsa_cache_append(const dsa_cache_append_args* args, void* stream);
 
+/*
+ * RMSNorm + rotary position embedding in FP32 (ORT PR #33997, Description
+ * item 1: normalisation and rotation computed in FP32 with FP32 rotary
+ * tables and no intermediate 16-bit rounding, then rounded once to the
+ * FP16 or BF16 output).  For head vector x of token s of sequence b, at
+ * position p = kv_len[b] - S + s:
+ *   y_d   = gamma_d * x_d / sqrt(mean_d(x_d^2) + eps)
+ *   pair i = (i, i + D/2) ("rotate half"), or (2i, 2i+1) when interleaved:
+ *   out_a = y_a * cos[p,i] - y_b * sin[p,i]
+ *   out_b = y_b * cos[p,i] + y_a * sin[p,i]
+ * with correctly rounded FP32 square root and reciprocal.
+ *   x                  [B, S, H, D]   x_dtype (F32, F16 or BF16)
+ *   gamma              [D]            FP32
+ *   cos_cache, sin_cache [max_pos, D/2] FP32
+ *   kv_len             [B]            int32, device
+ *   out                [B, S, H, D]   out_dtype (F32, F16 or BF16), RNE;
+ *                      may alias x.  Rows whose position lies outside
+ *                      [0, max_pos) are left untouched.
+ * Supported: D in {64, 128}; eps finite and >= 0.  Used on query heads, key
+ * heads and indexer query heads alike (H is their head count).
+ */
+typedef struct {
+  const void* x;          int32_t x_dtype;
+  const float* gamma;
+  const float* cos_cache; const float* sin_cache;
+  const int32_t* kv_len;
+  int32_t B, S, H, D, max_pos;
+  float eps;              int32_t interleaved;
+  void* out;              int32_t out_dtype;
+} dsa_rmsnorm_rope_args;
+
+dsa_status dsa_rmsnorm_rope(const dsa_rmsnorm_rope_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

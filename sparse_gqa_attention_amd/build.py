@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "attention.hip", "cache_append.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "attention.hip", "cache_append.hip",
+           "rmsnorm_rope.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -81,4 +81,19 @@ struct CacheAppendLaunch {
 };
 void launch_cache_append(const CacheAppendLaunch& a, hipStream_t st);
 
+// ---------------------------------------------------------------- RMSNorm + rotary
+struct RopeLaunch {
+  const void* x;
+  const float* gamma;
+  const float* cos_cache;
+  const float* sin_cache;
+  const int32_t* kv_len;
+  void* out;
+  int x_dtype, out_dtype;
+  int B, S, H, D, max_pos;
+  float eps;
+  int interleaved;
+};
+void launch_rmsnorm_rope(const RopeLaunch& a, hipStream_t st);
+
 }  // namespace dsa

@@ -22,7 +22,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
 
 EXPORTS = ("dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "dsa_attention_workspace_bytes",
-           "dsa_attention_decode", "dsa_attention_prefill", "dsa_cache_append")
+           "dsa_attention_decode", "dsa_attention_prefill", "dsa_cache_append",
+           "dsa_rmsnorm_rope")
 
 
 class DsaError(RuntimeError):
@@ -57,6 +58,18 @@ class CacheAppendArgs(ctypes.Structure):
                 ("D", ctypes.c_int32), ("D_idx", ctypes.c_int32), ("L_cap", ctypes.c_int32)]
 
 
+class RopeArgs(ctypes.Structure):
+    """Mirror of dsa_rmsnorm_rope_args."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32),
+                ("gamma", ctypes.c_void_p),
+                ("cos_cache", ctypes.c_void_p), ("sin_cache", ctypes.c_void_p),
+                ("kv_len", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("max_pos", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("interleaved", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
@@ -79,6 +92,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = i32
         f.argtypes = [ctypes.POINTER(AttentionArgs), vp, sz, vp]
+    lib.dsa_rmsnorm_rope.restype = i32
+    lib.dsa_rmsnorm_rope.argtypes = [ctypes.POINTER(RopeArgs), vp]
     lib.dsa_cache_append.restype = i32
     lib.dsa_cache_append.argtypes = [ctypes.POINTER(CacheAppendArgs), vp]
     return lib
@@ -231,3 +246,27 @@ def dsa_cache_append(k_new, v_new, k_cache, v_cache, kv_len, k_scale=None, v_sca
     a = cache_append_args(k_new, v_new, k_cache, v_cache, kv_len, k_scale, v_scale,
                           key_state_new, key_state)
     _check(LIB.dsa_cache_append(ctypes.byref(a), _stream(stream)))
+
+
+# ------------------------------------------------------------------ RMSNorm + rotary
+def rope_args(x, gamma, cos_cache, sin_cache, kv_len, out, eps=1e-6, interleaved=False):
+    B, S, H, D = x.shape
+    a = RopeArgs()
+    a.x, a.x_dtype = x.data_ptr(), _DTYPE_CODE[x.dtype]
+    a.gamma, a.cos_cache, a.sin_cache = gamma.data_ptr(), cos_cache.data_ptr(), sin_cache.data_ptr()
+    a.kv_len = kv_len.data_ptr()
+    a.B, a.S, a.H, a.D, a.max_pos = B, S, H, D, cos_cache.shape[0]
+    a.eps, a.interleaved = float(eps), int(bool(interleaved))
+    a.out, a.out_dtype = out.data_ptr(), _DTYPE_CODE[out.dtype]
+    return a
+
+
+def dsa_rmsnorm_rope(x, gamma, cos_cache, sin_cache, kv_len, out, eps=1e-6, interleaved=False,
+                     stream=None):
+    """out = rotary(RMSNorm(x) * gamma) at position kv_len[b] - S + s, in FP32; see include/dsa.h."""
+    for t, n in ((x, "x"), (gamma, "gamma"), (cos_cache, "cos_cache"), (sin_cache, "sin_cache"),
+                 (kv_len, "kv_len"), (out, "out")):
+        _gpu(t, n)
+    a = rope_args(x, gamma, cos_cache, sin_cache, kv_len, out, eps, interleaved)
+    _check(LIB.dsa_rmsnorm_rope(ctypes.byref(a), _stream(stream)))
+    return out

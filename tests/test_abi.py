@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_and_library_agree(dsa):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(LIBPATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -167,6 +167,31 @@ def test_cache_append_validation(dsa):
     for kw, want in bad:
         assert call(_append(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
     assert call(_append(dsa, S=0, k_new=None, v_new=None)) == 0   # nothing to append
+
+
+def _rope(dsa, **kw):
+    a = dsa.dsa.RopeArgs()
+    base = dict(x=A16, x_dtype=2, gamma=A16, cos_cache=A16, sin_cache=A16, kv_len=A16,
+                B=1, S=8, H=24, D=128, max_pos=32768, eps=1e-6, interleaved=0, out=A16, out_dtype=1)
+    base.update(kw)
+    for f, v in base.items():
+        setattr(a, f, v)
+    return a
+
+
+def test_rmsnorm_rope_validation(dsa):
+    L = dsa.LIB
+    call = lambda a: L.dsa_rmsnorm_rope(ctypes.byref(a), None)
+    bad = [
+        (dict(D=96), "UNSUPPORTED"), (dict(max_pos=0), "INVALID"), (dict(eps=-1.0), "INVALID"),
+        (dict(eps=float("inf")), "INVALID"), (dict(x_dtype=3), "UNSUPPORTED"),
+        (dict(out_dtype=3), "UNSUPPORTED"), (dict(H=-1), "INVALID"),
+        (dict(gamma=None), "INVALID"), (dict(cos_cache=MIS), "MISALIGNED"),
+        (dict(out=None), "INVALID"), (dict(kv_len=MIS), "MISALIGNED"),
+    ]
+    for kw, want in bad:
+        assert call(_rope(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
+    assert call(_rope(dsa, H=0, x=None, out=None)) == 0
 
 
 def test_error_text_is_thread_local_and_cleared(dsa):
