@@ -111,6 +111,10 @@ def stage_bytes(w, kv_len):
     if w.has_indexer:
         rope += B * S * w.H_idx * w.D_idx * (ELT[w.idx_dtype] + out_elt) + B * S * w.D_idx * 4 * 2
     out["rmsnorm_rope"] = rope
+    # Attention whose S newest keys come as auxiliary K/V (BF16, or F32 next
+    # to an F32 cache) instead of from the cache.
+    aux_elt = 4 if w.kv_dtype == "f32" else 2
+    out["attention_aux"] = out["attention"] + B * S * w.H_kv * w.D * aux_elt * 2
     # Whole path without the score round trip (an artefact of the 4-call ABI).
     path = out["attention"]
     if w.has_indexer:
@@ -167,7 +171,7 @@ def main():
         sys.exit(2)
     import torch
     import sparse_gqa_attention_amd as dsa
-    from dsa_synth import BY_NAME, make_inputs, make_new_tokens, make_rope_inputs
+    from dsa_synth import BY_NAME, make_inputs, make_new_tokens, make_rope_inputs, make_aux_inputs
 
     w = BY_NAME[args.workload]
     decode = w.decode_form
@@ -247,8 +251,24 @@ def main():
         for ri in rope_sets:
             dsa.dsa_rmsnorm_rope(ri["x"], ri["gamma"], ri["cos"], ri["sin"], ri["kv_len"], ri["out"])
 
+    # Attention with the step's S newest tokens as auxiliary K/V.
+    aux = {kk: v.to(dev) for kk, v in make_aux_inputs(
+        B, S, w.H_kv, w.D, "f32" if w.kv_dtype == "f32" else "bf16", seed=24).items()}
+    a_aux = dsa.attention_args(g0["q"], g0["k_cache"], g0["v_cache"], idx, g0["kv_len"], out,
+                               g0["k_scale"], g0["v_scale"], max_kv_len=w.max_kv_len,
+                               aux_k=aux["aux_k"], aux_v=aux["aux_v"])
+    aux_ws = torch.empty(max(dsa.dsa_attention_workspace_bytes(a_aux, decode), 16),
+                         dtype=torch.uint8, device=dev)
+
+    def attention_aux_stage(g):
+        ind = idx if w.has_indexer else g["indices"]
+        attn(g["q"], g["k_cache"], g["v_cache"], ind, g["kv_len"], out,
+             k_scale=g["k_scale"], v_scale=g["v_scale"], workspace=aux_ws, max_kv_len=mx,
+             aux_k=aux["aux_k"], aux_v=aux["aux_v"])
+
     extra_fns = {"cache_append": lambda: [append_stage(g) for g in layers],
-                 "rmsnorm_rope": lambda: [rope_stage() for _ in layers]}
+                 "rmsnorm_rope": lambda: [rope_stage() for _ in layers],
+                 "attention_aux": lambda: [attention_aux_stage(g) for g in layers]}
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -361,7 +381,9 @@ def main():
                               "hbm_gbps": round(sb[st] / (v * 1e-6) / 1e9, 1),
                               "note": {"cache_append": "KV-cache append of the step's new tokens",
                                        "rmsnorm_rope": "RMSNorm + rotary of the step's query, key "
-                                                       "and indexer-query heads"}[st]
+                                                       "and indexer-query heads",
+                                       "attention_aux": "attention with the step's S newest tokens "
+                                                        "as auxiliary K/V"}[st]
                                       + "; measured on its own, not in value"}
                          for st, v in extra_us.items()},
     }

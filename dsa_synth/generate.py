@@ -156,3 +156,14 @@ def make_rope_inputs(B, S, H, D, max_pos, x_dtype, kv_len, seed=0, base=1.0e6):
     cos, sin = rope_tables(max_pos, D, base)
     return {"x": torch.from_numpy(x).to(_TORCH[x_dtype]), "gamma": torch.from_numpy(gamma),
             "cos": cos, "sin": sin, "kv_len": torch.tensor(list(kv_len), dtype=torch.int32)}
+
+
+def make_aux_inputs(B, S_aux, H_kv, D, aux_dtype, seed=0, value_scale=1.0):
+    """Auxiliary (not yet cached) K/V [B, S_aux, H_kv, D]: N(0,1) in aux_dtype,
+    V optionally multiplied by value_scale (large values exercise dtypes
+    whose range the cache dtype lacks)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal(size=(B, S_aux, H_kv, D), dtype=np.float32)
+    v = rng.standard_normal(size=(B, S_aux, H_kv, D), dtype=np.float32) * np.float32(value_scale)
+    return {"aux_k": torch.from_numpy(k).to(_TORCH[aux_dtype]),
+            "aux_v": torch.from_numpy(v).to(_TORCH[aux_dtype])}

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -129,6 +129,19 @@ dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S,
  * must lie within FP16 range.
  * softmax_scale <= 0 selects 1/sqrt(D).
  *
+ * Auxiliary K/V (ORT PR #33997 review and follow-up: fresh keys and values
+ * kept in their own floating type next to the main cache, taking part in the
+ * same softmax): aux_k, aux_v [B, aux_len, H_kv, D] in aux_dtype (F32, F16 or
+ * BF16; F32 when q is F32) hold the tokens at positions
+ * kv_len[b] - aux_len + t, which the cache does not hold yet.  Query (b,s)
+ * then attends to (i) its selected cache keys j < kv_len[b] - aux_len (cache
+ * entries in the aux range are ignored) and (ii) the aux tokens whose
+ * position is <= pos(b,s), in one softmax.  Aux values are never converted
+ * to the cache dtype: products run in their 16-bit type when the query has
+ * it (a BF16 query against F16 aux multiplies in FP16, as against an F16
+ * cache), otherwise in FP32.  Precondition: aux_len <= kv_len[b].  With aux
+ * keys both forms need workspace.
+ *
  * decode: the selected keys of each row are split over several workgroups
  * whose partial softmax states are merged exactly in a second kernel; it
  * needs dsa_attention_workspace_bytes(args, 1) bytes of workspace.
@@ -144,6 +157,9 @@ typedef struct {
   int32_t B, S, H_q, H_kv, D, L_cap, max_kv_len;
   float softmax_scale;
   void* out;            int32_t out_dtype;
+  /* Auxiliary K/V (aux_len = 0: none); see below. */
+  const void* aux_k;    const void* aux_v;    int32_t aux_dtype;
+  int32_t aux_len;
 } dsa_attention_args;
 
 size_t dsa_attention_workspace_bytes(const dsa_attention_args* args, int is_decode);
@@ -205,7 +221,7 @@ dsa_status dsa_cache_append(const dsa_cache_append_args* args, void* stream);
  *   out                [B, S, H, D]   out_dtype (F32, F16 or BF16), RNE;
  *                      may alias x.  Rows whose position lies outside
  *                      [0, max_pos) are left untouched.
- * Supported: D in {64, 128}; eps finite and >= 0.  Used on query heads, key
+ * Supported: D in {32, 64, 128}; eps finite and >= 0.  Used on query heads, key
  * heads and indexer query heads alike (H is their head count).
  */
 typedef struct {

@@ -53,6 +53,12 @@ struct AttnParams {
   float* part;
   int S, H_q, H_kv, L_cap, k, ratio, out_dtype, nsplit, kps;
   float scale;
+  int aux_tokens;     // cache keys at positions >= kv_len - aux_tokens are not attended
+  int kvl_const;      // >= 0: use this live length for every sequence (aux keys)
+  int dense;          // key slot j is key j (no index list)
+  int write_partial;  // write (m, l, O) partials instead of the output
+  int part_stride;    // splits per (row, head) in the partial buffer
+  int part_offset;    // first split index of this launch
 };
 
 __device__ __forceinline__ void store_out(void* out, size_t i, float v, int dt) {
@@ -109,7 +115,9 @@ __device__ __forceinline__ To cvt(From x) {
 
 template <int D, typename QT, typename KVT, typename MQK, typename MPV>
 struct AttnCfg {
-  static constexpr bool kF32Path = std::is_same<KVT, float>::value;
+  // FP32 operands (v_mfma_f32_16x16x4_f32): the FP32 cache, and query /
+  // auxiliary dtype pairs that no 16-bit type holds exactly.
+  static constexpr bool kF32Path = std::is_same<MQK, float>::value;
   static constexpr bool kInt8 = std::is_same<KVT, int8_t>::value;
   static constexpr int kQuarter = D / 4;             // elements of a row per lane
   static constexpr int kSteps = D / 32;              // QK K-steps (16-bit path)
@@ -136,11 +144,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
 
   const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
   const int b = row / p.S, s = row % p.S;
-  int kvl = p.kv_len[b];
+  int kvl = p.kvl_const >= 0 ? p.kvl_const : p.kv_len[b];
   kvl = kvl < 0 ? 0 : (kvl > p.L_cap ? p.L_cap : kvl);
   const int pos = kvl - p.S + s;
-  const int live = min(kvl, pos + 1);     // valid key indices are [0, live)
-  const int32_t* idx_row = p.indices + (size_t)row * p.k;
+  const int live = min(kvl - p.aux_tokens, pos + 1);   // valid key indices are [0, live)
+  const int32_t* idx_row = p.dense ? nullptr : p.indices + (size_t)row * p.k;
   const int k0 = split * p.kps;
   const int k1 = min(p.k, k0 + p.kps);
 
@@ -153,8 +161,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   int next_a = -1, next_b = -1;
   {
     const int ja = k0 + kTile * wave + c16, jb = ja + 16;
-    if (ja < k1) next_a = idx_row[ja];
-    if (jb < k1) next_b = idx_row[jb];
+    if (ja < k1) next_a = p.dense ? ja : idx_row[ja];
+    if (jb < k1) next_b = p.dense ? jb : idx_row[jb];
   }
   const int R = p.ratio;
   const bool head_ok = c16 < R;
@@ -192,8 +200,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     const int ia = next_a, ib = next_b;
     {
       const int ja = t0 + kTile * kAttnWaves + c16, jb = ja + 16;
-      next_a = ja < k1 ? idx_row[ja] : -1;
-      next_b = jb < k1 ? idx_row[jb] : -1;
+      next_a = ja < k1 ? (p.dense ? ja : idx_row[ja]) : -1;
+      next_b = jb < k1 ? (p.dense ? jb : idx_row[jb]) : -1;
     }
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
@@ -399,15 +407,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       O += fb[w * 16 + n] * *reinterpret_cast<const f32x4*>(&ob[((size_t)w * 16 + n) * OS + 4 * c]);
     const float L = hb[n];
     const size_t hrow = (size_t)row * p.H_q + g * R + n;
-    if (p.nsplit == 1) {
+    if (!p.write_partial) {
       store_out4(p.out, hrow * D + 4 * c, O, L, p.out_dtype);
     } else {
+      const size_t slot = hrow * p.part_stride + p.part_offset + split;
       float* pml = p.part;
-      float* po = p.part + (size_t)2 * gridDim.z * p.H_q * p.nsplit;
-      *reinterpret_cast<f32x4*>(&po[(hrow * p.nsplit + split) * D + 4 * c]) = O;
+      float* po = p.part + (size_t)2 * gridDim.z * p.H_q * p.part_stride;
+      *reinterpret_cast<f32x4*>(&po[slot * D + 4 * c]) = O;
       if (c == 0) {
-        pml[(hrow * p.nsplit + split) * 2 + 0] = hb[16 + n];
-        pml[(hrow * p.nsplit + split) * 2 + 1] = L;
+        pml[slot * 2 + 0] = hb[16 + n];
+        pml[slot * 2 + 1] = L;
       }
     }
   }
@@ -469,8 +478,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   }
 }
 
-template <int D, typename QT, typename KVT, typename MQK, typename MPV>
-void launch_cfg(const AttnLaunch& a, hipStream_t st) {
+AttnParams base_params(const AttnLaunch& a) {
   AttnParams p;
   p.q = a.q; p.k_cache = a.k_cache; p.v_cache = a.v_cache;
   p.k_scale = a.k_scale; p.v_scale = a.v_scale;
@@ -478,33 +486,79 @@ void launch_cfg(const AttnLaunch& a, hipStream_t st) {
   p.S = a.S; p.H_q = a.H_q; p.H_kv = a.H_kv; p.L_cap = a.L_cap; p.k = a.k;
   p.ratio = a.H_q / a.H_kv; p.out_dtype = a.out_dtype;
   p.nsplit = a.nsplit; p.kps = a.keys_per_split; p.scale = a.scale;
-  dim3 grid(a.nsplit, a.H_kv, a.B * a.S);
+  p.aux_tokens = a.aux_len; p.kvl_const = -1; p.dense = 0;
+  p.write_partial = a.nsplit > 1 || a.aux_len > 0;
+  p.part_stride = a.nsplit + (a.aux_len > 0 ? 1 : 0);
+  p.part_offset = 0;
+  return p;
+}
+
+template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+void launch_kernel(const AttnParams& p, int nsplit, int H_kv, int rows, hipStream_t st) {
+  dim3 grid(nsplit, H_kv, rows);
   hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV>), grid, dim3(kAttnThreads), 0, st, p);
-  if (a.nsplit > 1) {
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.B * a.S * a.H_q), dim3(kMergeThreads), 0, st,
-                       (const float*)a.part, a.B * a.S * a.H_q, a.nsplit, a.out, a.out_dtype);
+}
+
+// Main launch over the selected cache keys.
+template <int D>
+void launch_main(const AttnLaunch& a, const AttnParams& p, hipStream_t st) {
+  typedef _Float16 H;
+  typedef __bf16 BH;
+  const int rows = a.B * a.S;
+  if (a.kv_dtype == kF32) { launch_kernel<D, float, float, float, float>(p, a.nsplit, a.H_kv, rows, st); return; }
+  if (a.q_dtype == kBF16) {
+    if (a.kv_dtype == kF16) launch_kernel<D, BH, H, H, H>(p, a.nsplit, a.H_kv, rows, st);
+    else if (a.kv_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH>(p, a.nsplit, a.H_kv, rows, st);
+    else launch_kernel<D, BH, int8_t, BH, BH>(p, a.nsplit, a.H_kv, rows, st);
+  } else {
+    if (a.kv_dtype == kF16) launch_kernel<D, H, H, H, H>(p, a.nsplit, a.H_kv, rows, st);
+    else if (a.kv_dtype == kBF16) launch_kernel<D, H, BH, H, BH>(p, a.nsplit, a.H_kv, rows, st);
+    else launch_kernel<D, H, int8_t, H, BH>(p, a.nsplit, a.H_kv, rows, st);
+  }
+}
+
+// Auxiliary keys: every (row, KV head) attends its causal prefix of the S_aux
+// fresh keys, one workgroup each, writing the last partial split.  The aux
+// values keep their dtype: the products run in that 16-bit type when the
+// query has it too (a BF16 query is taken to FP16 against FP16 aux, as
+// against an FP16 cache), and in FP32 otherwise.
+template <int D>
+void launch_aux(const AttnLaunch& a, AttnParams p, hipStream_t st) {
+  typedef _Float16 H;
+  typedef __bf16 BH;
+  p.k_cache = a.aux_k; p.v_cache = a.aux_v; p.k_scale = p.v_scale = nullptr;
+  p.indices = nullptr; p.dense = 1; p.k = a.aux_len; p.kps = a.aux_len;
+  p.L_cap = a.aux_len; p.kvl_const = a.aux_len; p.aux_tokens = 0;
+  p.write_partial = 1; p.part_offset = a.nsplit;
+  const int rows = a.B * a.S;
+  if (a.q_dtype == kF32) { launch_kernel<D, float, float, float, float>(p, 1, a.H_kv, rows, st); return; }
+  if (a.q_dtype == kBF16) {
+    if (a.aux_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH>(p, 1, a.H_kv, rows, st);
+    else if (a.aux_dtype == kF16) launch_kernel<D, BH, H, H, H>(p, 1, a.H_kv, rows, st);
+    else launch_kernel<D, BH, float, float, float>(p, 1, a.H_kv, rows, st);
+  } else {
+    if (a.aux_dtype == kF16) launch_kernel<D, H, H, H, H>(p, 1, a.H_kv, rows, st);
+    else if (a.aux_dtype == kBF16) launch_kernel<D, H, BH, float, float>(p, 1, a.H_kv, rows, st);
+    else launch_kernel<D, H, float, float, float>(p, 1, a.H_kv, rows, st);
   }
 }
 
 template <int D>
 void launch_d(const AttnLaunch& a, hipStream_t st) {
-  typedef _Float16 H;
-  typedef __bf16 BH;
-  if (a.kv_dtype == kF32) { launch_cfg<D, float, float, float, float>(a, st); return; }
-  if (a.q_dtype == kBF16) {
-    if (a.kv_dtype == kF16) launch_cfg<D, BH, H, H, H>(a, st);
-    else if (a.kv_dtype == kBF16) launch_cfg<D, BH, BH, BH, BH>(a, st);
-    else launch_cfg<D, BH, int8_t, BH, BH>(a, st);
-  } else {
-    if (a.kv_dtype == kF16) launch_cfg<D, H, H, H, H>(a, st);
-    else if (a.kv_dtype == kBF16) launch_cfg<D, H, BH, H, BH>(a, st);
-    else launch_cfg<D, H, int8_t, H, BH>(a, st);
+  const AttnParams p = base_params(a);
+  launch_main<D>(a, p, st);
+  if (a.aux_len > 0) launch_aux<D>(a, p, st);
+  if (p.write_partial) {
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.B * a.S * a.H_q), dim3(kMergeThreads), 0, st,
+                       (const float*)a.part, a.B * a.S * a.H_q, p.part_stride, a.out, a.out_dtype);
   }
 }
 
 }  // namespace
 
 void plan_attention(AttnLaunch& a, bool decode) {
+  // The merge combines at most 64 splits; auxiliary keys take one of them.
+  const int max_split = a.aux_len > 0 ? 63 : 64;
   if (!decode || a.k <= 0) {
     a.nsplit = 1;
     a.keys_per_split = a.k > 0 ? a.k : 1;
@@ -519,9 +573,9 @@ void plan_attention(AttnLaunch& a, bool decode) {
   kps = ((kps + kTile - 1) / kTile) * kTile;
   if (kps < 128) kps = 128;
   long long ns = (a.k + kps - 1) / kps;
-  if (ns > 64) {
-    ns = 64;
-    kps = (a.k + 63) / 64;
+  if (ns > max_split) {
+    ns = max_split;
+    kps = (a.k + max_split - 1) / max_split;
     kps = ((kps + kTile - 1) / kTile) * kTile;
     ns = (a.k + kps - 1) / kps;
   }
@@ -530,8 +584,9 @@ void plan_attention(AttnLaunch& a, bool decode) {
 }
 
 size_t attention_partials_bytes(const AttnLaunch& a) {
-  if (a.nsplit <= 1) return 0;
-  return (size_t)a.B * a.S * a.H_q * a.nsplit * (a.D + 2) * sizeof(float);
+  const int splits = a.nsplit + (a.aux_len > 0 ? 1 : 0);
+  if (splits <= 1) return 0;
+  return (size_t)a.B * a.S * a.H_q * splits * (a.D + 2) * sizeof(float);
 }
 
 void launch_attention(const AttnLaunch& a, hipStream_t st) {

@@ -87,7 +87,20 @@ dsa_status validate_attention(const dsa_attention_args* a) {
     return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
   if ((long long)a->L_cap * a->H_kv * a->D >= (1LL << 40))
     return fail(DSA_ERR_UNSUPPORTED, "cache too large");
+  if (a->aux_len < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "aux_len=%d must be >= 0", a->aux_len);
+  if (a->aux_len > 0) {
+    const int ad = a->aux_dtype;
+    if (qd == DSA_F32 ? ad != DSA_F32 : (ad != DSA_F32 && ad != DSA_F16 && ad != DSA_BF16))
+      return fail(DSA_ERR_UNSUPPORTED, "auxiliary K/V dtype %s with q=%s is not supported",
+                  dtype_name(ad), dtype_name(qd));
+    if (a->aux_len > a->L_cap)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "aux_len=%d exceeds L_cap=%d", a->aux_len, a->L_cap);
+  }
   if ((long long)a->B * a->S == 0) return DSA_OK;
+  if (a->aux_len > 0) {
+    CHECK(check_ptr(a->aux_k, "aux_k"));
+    CHECK(check_ptr(a->aux_v, "aux_v"));
+  }
   CHECK(check_ptr(a->q, "q"));
   CHECK(check_ptr(a->k_cache, "k_cache"));
   CHECK(check_ptr(a->v_cache, "v_cache"));
@@ -112,6 +125,9 @@ dsa::AttnLaunch make_attn(const dsa_attention_args* a, bool decode) {
   l.B = a->B; l.S = a->S; l.H_q = a->H_q; l.H_kv = a->H_kv; l.D = a->D;
   l.L_cap = a->L_cap; l.k = a->k;
   l.scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / std::sqrt((float)a->D);
+  l.aux_k = a->aux_len > 0 ? a->aux_k : nullptr;
+  l.aux_v = a->aux_len > 0 ? a->aux_v : nullptr;
+  l.aux_dtype = a->aux_dtype; l.aux_len = a->aux_len;
   dsa::plan_attention(l, decode);
   return l;
 }
@@ -265,7 +281,8 @@ dsa_status dsa_rmsnorm_rope(const dsa_rmsnorm_rope_args* a, void* stream) {
   if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->B < 0 || a->S < 0 || a->H < 0)
     return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d H=%d must be >= 0", a->B, a->S, a->H);
-  if (a->D != 64 && a->D != 128) return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d not in {64, 128}", a->D);
+  if (a->D != 32 && a->D != 64 && a->D != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", a->D);
   if (a->max_pos < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "max_pos=%d must be >= 1", a->max_pos);
   if (!(a->eps >= 0.0f) || !std::isfinite(a->eps))
     return fail(DSA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");

@@ -59,8 +59,12 @@ struct AttnLaunch {
   float scale;
   int nsplit;         // key splits per (row, KV head)
   int keys_per_split;
+  const void* aux_k;  // auxiliary (not yet cached) K/V [B, aux_len, H_kv, D], or null
+  const void* aux_v;
+  int aux_dtype, aux_len;
 };
-// nsplit/keys_per_split for the decode form; prefill uses nsplit = 1.
+// nsplit/keys_per_split for the decode form; prefill uses nsplit = 1.  Set
+// aux_len first: auxiliary keys take one merge slot.
 void plan_attention(AttnLaunch& a, bool decode);
 size_t attention_partials_bytes(const AttnLaunch& a);
 void launch_attention(const AttnLaunch& a, hipStream_t st);

@@ -14,9 +14,9 @@
 // gfx950 design: the op is a streaming elementwise pass (bytes in = bytes
 // out), so it is built for coalescing, not MFMA.  One lane owns one rotated
 // pair, so the rotation needs no data exchange; the D/2 lanes of a head
-// vector (64 for D = 128, 32 for D = 64: two vectors per wave) reduce the
-// sum of squares with a segmented xor butterfly.  Rows whose position falls
-// outside the tables are not written.
+// vector (64 for D = 128; 32 or 16 for D = 64 or 32: 2 or 4 vectors per
+// wave) reduce the sum of squares with a segmented xor butterfly.  Rows
+// whose position falls outside the tables are not written.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -89,7 +89,8 @@ void launch_in(const RopeLaunch& a, hipStream_t st) {
 
 void launch_rmsnorm_rope(const RopeLaunch& a, hipStream_t st) {
   if ((long long)a.B * a.S * a.H == 0) return;
-  if (a.D == 64) launch_in<32>(a, st);
+  if (a.D == 32) launch_in<16>(a, st);
+  else if (a.D == 64) launch_in<32>(a, st);
   else launch_in<64>(a, st);
 }
 

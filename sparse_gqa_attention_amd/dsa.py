@@ -43,7 +43,9 @@ class AttentionArgs(ctypes.Structure):
                 ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H_q", ctypes.c_int32),
                 ("H_kv", ctypes.c_int32), ("D", ctypes.c_int32), ("L_cap", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32)]
+                ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+                ("aux_k", ctypes.c_void_p), ("aux_v", ctypes.c_void_p),
+                ("aux_dtype", ctypes.c_int32), ("aux_len", ctypes.c_int32)]
 
 
 class CacheAppendArgs(ctypes.Structure):
@@ -166,7 +168,7 @@ def dsa_topk(scores, kv_len, k, indices, workspace=None, max_kv_len=None, stream
 
 # ------------------------------------------------------------------ attention
 def attention_args(q, k_cache, v_cache, indices, kv_len, out, k_scale=None, v_scale=None,
-                   softmax_scale=0.0, max_kv_len=None):
+                   softmax_scale=0.0, max_kv_len=None, aux_k=None, aux_v=None):
     B, S, H_q, D = q.shape
     L, H_kv = k_cache.shape[1], k_cache.shape[2]
     a = AttentionArgs()
@@ -180,6 +182,9 @@ def attention_args(q, k_cache, v_cache, indices, kv_len, out, k_scale=None, v_sc
     a.max_kv_len = L if max_kv_len is None else max_kv_len
     a.softmax_scale = float(softmax_scale)
     a.out, a.out_dtype = out.data_ptr(), _DTYPE_CODE[out.dtype]
+    if aux_k is not None:
+        a.aux_k, a.aux_v = aux_k.data_ptr(), aux_v.data_ptr()
+        a.aux_dtype, a.aux_len = _DTYPE_CODE[aux_k.dtype], aux_k.shape[1]
     return a
 
 
@@ -188,12 +193,14 @@ def dsa_attention_workspace_bytes(args, is_decode):
 
 
 def _attention(fn, is_decode, q, k_cache, v_cache, indices, kv_len, out, k_scale, v_scale,
-               softmax_scale, workspace, max_kv_len, stream):
+               softmax_scale, workspace, max_kv_len, stream, aux_k=None, aux_v=None):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (indices, "indices"),
                  (kv_len, "kv_len"), (out, "out")):
         _gpu(t, n)
+    if aux_k is not None:
+        _gpu(aux_k, "aux_k"), _gpu(aux_v, "aux_v")
     a = attention_args(q, k_cache, v_cache, indices, kv_len, out, k_scale, v_scale,
-                       softmax_scale, max_kv_len)
+                       softmax_scale, max_kv_len, aux_k, aux_v)
     need = LIB.dsa_attention_workspace_bytes(ctypes.byref(a), int(is_decode))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -203,17 +210,20 @@ def _attention(fn, is_decode, q, k_cache, v_cache, indices, kv_len, out, k_scale
 
 
 def dsa_attention_decode(q, k_cache, v_cache, indices, kv_len, out, k_scale=None, v_scale=None,
-                         softmax_scale=0.0, workspace=None, max_kv_len=None, stream=None):
+                         softmax_scale=0.0, workspace=None, max_kv_len=None, stream=None,
+                         aux_k=None, aux_v=None):
     """Split-K sparse GQA attention (decode form); see include/dsa.h."""
     return _attention(LIB.dsa_attention_decode, True, q, k_cache, v_cache, indices, kv_len, out,
-                      k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream)
+                      k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream, aux_k, aux_v)
 
 
 def dsa_attention_prefill(q, k_cache, v_cache, indices, kv_len, out, k_scale=None, v_scale=None,
-                          softmax_scale=0.0, workspace=None, max_kv_len=None, stream=None):
+                          softmax_scale=0.0, workspace=None, max_kv_len=None, stream=None,
+                          aux_k=None, aux_v=None):
     """One workgroup per (row, KV head) sparse GQA attention (prefill form)."""
     return _attention(LIB.dsa_attention_prefill, False, q, k_cache, v_cache, indices, kv_len,
-                      out, k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream)
+                      out, k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream,
+                      aux_k, aux_v)
 
 
 def default_softmax_scale(D):

@@ -126,8 +126,20 @@ def test_attention_validation(dsa):
         (dict(q=MIS), "MISALIGNED"), (dict(out=None), "INVALID"),
         (dict(kv_dtype=3, k_scale=A16, v_scale=MIS), "MISALIGNED"),
     ]
+    aux = dict(aux_k=A16, aux_v=A16, aux_dtype=2, aux_len=8)
+    bad += [
+        (dict(aux_len=-1), "INVALID"),
+        (dict(aux, aux_dtype=3), "UNSUPPORTED"),             # INT8 auxiliary values
+        (dict(aux, q_dtype=0, kv_dtype=0, out_dtype=0), "UNSUPPORTED"),   # F32 q needs F32 aux
+        (dict(aux, aux_k=MIS), "MISALIGNED"), (dict(aux, aux_v=None), "INVALID"),
+        (dict(aux, aux_len=40000), "INVALID"),               # beyond L_cap
+    ]
     for kw, want in bad:
         assert call(_attn(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
+    ax = _attn(dsa, **aux)
+    assert L.dsa_attention_workspace_bytes(ctypes.byref(ax), 0) > 0   # prefill + aux: partials
+    assert (L.dsa_attention_workspace_bytes(ctypes.byref(ax), 1)
+            > L.dsa_attention_workspace_bytes(ctypes.byref(_attn(dsa)), 1))
     a = _attn(dsa)
     need = L.dsa_attention_workspace_bytes(ctypes.byref(a), 1)
     assert need > 0
@@ -183,7 +195,8 @@ def test_rmsnorm_rope_validation(dsa):
     L = dsa.LIB
     call = lambda a: L.dsa_rmsnorm_rope(ctypes.byref(a), None)
     bad = [
-        (dict(D=96), "UNSUPPORTED"), (dict(max_pos=0), "INVALID"), (dict(eps=-1.0), "INVALID"),
+        (dict(D=96), "UNSUPPORTED"), (dict(D=16), "UNSUPPORTED"),
+        (dict(max_pos=0), "INVALID"), (dict(eps=-1.0), "INVALID"),
         (dict(eps=float("inf")), "INVALID"), (dict(x_dtype=3), "UNSUPPORTED"),
         (dict(out_dtype=3), "UNSUPPORTED"), (dict(H=-1), "INVALID"),
         (dict(gamma=None), "INVALID"), (dict(cos_cache=MIS), "MISALIGNED"),

@@ -74,7 +74,7 @@ COMBOS = [("bf16", "f16"), ("f16", "f16"), ("f32", "f16"), ("bf16", "bf16"), ("f
 
 
 @pytest.mark.parametrize("x_dtype,out_dtype", COMBOS, ids=[f"{a}->{b}" for a, b in COMBOS])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("interleaved", [False, True])
 def test_rope_small(dsa, x_dtype, out_dtype, D, interleaved):
     # second sequence runs 2 positions past the tables: its last 2 rows stay untouched
