@@ -424,40 +424,45 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
 
 // Combine the key splits of one (row, head) in a fixed order (deterministic).
 // Thread t owns a float4 column chunk (t % (D/4)) and the splits
-// t / (D/4), + G, + 2G, ... (G = 256 / (D/4)); loads of all its splits are
-// independent and in flight together; the G partial sums meet in LDS.
+// t / (D/4), + G, + 2G, ... (G = 256 / (D/4)).  Every partial-O load is
+// issued before the split maxima are known (they do not depend on them), so
+// the kernel waits on one round of memory latency; the G partial sums meet
+// in LDS.
 constexpr int kMergeThreads = 256;
+constexpr int kMaxSplits = 64;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const float* __restrict__ part, int rows_h, int nsplit, void* out, int out_dtype) {
   constexpr int C4 = D / 4;                 // float4 chunks per row
   constexpr int G = kMergeThreads / C4;     // split groups
-  __shared__ float mm[64], ff[64], ll[64];
+  constexpr int Q = kMaxSplits / G;         // splits per thread at most
+  __shared__ float mm[kMaxSplits], ff[kMaxSplits], ll[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float4 acc[G][C4];
   const int hrow = blockIdx.x, t = threadIdx.x;
   const float* pml = part + (size_t)hrow * nsplit * 2;
   const float4* po = (const float4*)(part + (size_t)2 * rows_h * nsplit) + (size_t)hrow * nsplit * C4;
+  const int c = t % C4, g = t / C4;
+  float4 ov[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int sp = g + q * G;
+    ov[q] = sp < nsplit ? po[(size_t)sp * C4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (t < nsplit) { mm[t] = pml[2 * t]; ll[t] = pml[2 * t + 1]; }
   __syncthreads();
   float M = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mm[sp]);
   if (t < nsplit) ff[t] = (M == -INFINITY || mm[t] == -INFINITY) ? 0.0f : exp_keep_subnormal(mm[t] - M);
   __syncthreads();
-  const int c = t % C4, g = t / C4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  int sp = g;
-  for (; sp + G < nsplit; sp += 2 * G) {
-    const float4 a = po[(size_t)sp * C4 + c];
-    const float4 b = po[(size_t)(sp + G) * C4 + c];
-    const float fa = ff[sp], fb = ff[sp + G];
-    o.x += fa * a.x; o.y += fa * a.y; o.z += fa * a.z; o.w += fa * a.w;
-    o.x += fb * b.x; o.y += fb * b.y; o.z += fb * b.z; o.w += fb * b.w;
-  }
-  if (sp < nsplit) {
-    const float4 a = po[(size_t)sp * C4 + c];
-    const float fa = ff[sp];
-    o.x += fa * a.x; o.y += fa * a.y; o.z += fa * a.z; o.w += fa * a.w;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int sp = g + q * G;
+    if (sp < nsplit) {
+      const float f = ff[sp];
+      o.x += f * ov[q].x; o.y += f * ov[q].y; o.z += f * ov[q].z; o.w += f * ov[q].w;
+    }
   }
   acc[g][c] = o;
   __syncthreads();
@@ -470,11 +475,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
       const float4 v = acc[q][t];
       r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }
-    const size_t base = (size_t)hrow * D + 4 * t;
-    store_out(out, base + 0, L > 0.0f ? r.x / L : 0.0f, out_dtype);
-    store_out(out, base + 1, L > 0.0f ? r.y / L : 0.0f, out_dtype);
-    store_out(out, base + 2, L > 0.0f ? r.z / L : 0.0f, out_dtype);
-    store_out(out, base + 3, L > 0.0f ? r.w / L : 0.0f, out_dtype);
+    store_out4(out, (size_t)hrow * D + 4 * t, f32x4{r.x, r.y, r.z, r.w}, L, out_dtype);
   }
 }
 
