@@ -73,7 +73,8 @@ const char* dsa_last_error(void);
  *   scores     [B, S, L_cap]         FP32, written for j < kv_len[b];
  *              entries pos < j < kv_len[b] hold finite values that mean
  *              nothing, entries j >= kv_len[b] are left untouched.
- * Supported: 1 <= H_idx <= 16, D_idx in {32, 64, 128}.
+ * Supported: 1 <= H_idx <= 16, D_idx in {32, 64, 128}, L_cap <= 2^27
+ * (DSA_ERR_UNSUPPORTED otherwise).
  */
 dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx,
                              const void* key_state, dsa_dtype idx_dtype,

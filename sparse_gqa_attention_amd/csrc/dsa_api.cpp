@@ -162,6 +162,8 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* 
                              int D_idx, int L_cap, int max_kv_len, float* scores, void* stream) {
   if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
   if (L_cap < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "L_cap=%d must be >= 1", L_cap);
+  if (L_cap > dsa::kIndexerMaxLcap)
+    return fail(DSA_ERR_UNSUPPORTED, "L_cap=%d exceeds 2^27", L_cap);
   if (max_kv_len < 0 || max_kv_len > L_cap)
     return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
   if (idx_dtype != DSA_BF16 && idx_dtype != DSA_F16)

@@ -13,18 +13,26 @@
 // for 32 consecutive keys and lanes 32..63 token t1's: one coalesced
 // 128-byte store per half wave.
 //
-// A workgroup owns a run of up to KR keys and 2*PAIRS*WAVES query tokens (8
-// at decode, 32 at prefill).  The whole key run is copied into LDS once, by
-// direct global->LDS loads (16-byte chunks XOR-swizzled by row so that the
-// B-operand reads of different keys hit different banks), and every wave
-// multiplies its token pairs against all of it.  After that copy the
-// workgroup issues no vector-memory loads, only score stores: on gfx9 one
-// in-order counter tracks loads and stores alike, so a load issued behind
-// stores (a prefetch of the next key tile) would wait for those stores to be
-// acknowledged.  Query operands and head weights stay in registers.  Token
-// blocks are the fastest grid dimension and the XCD-aware renumbering below
-// keeps the workgroups sharing a key run on one XCD, so each key-state run is
-// fetched from HBM about once.
+// Prefill (indexer_stream_kernel): a workgroup holds 32 query tokens (8
+// waves x 2 token pairs; 16 tokens, one pair per wave, at D_idx 128) in
+// registers and streams a range of keys through two LDS buffers.  Each run of
+// keys is copied by direct global->LDS loads (16-byte chunks XOR-swizzled by
+// row so that the B-operand reads of different keys hit different banks);
+// the copy of the next run is issued before the current run is scored, so it
+// lands while the MFMAs run.  On gfx9 one in-order counter tracks loads and
+// stores alike, so the wait for that copy would also wait for every score
+// store issued after it, unless the count of those stores is known: scores
+// are written with buffer stores issued unconditionally (invalid lanes get an
+// out-of-range offset, which the hardware drops), so the wait names exactly
+// the stores of one run and never waits for their acknowledgement.
+//
+// Decode (indexer_score_kernel): a workgroup of 4 waves x 1 pair copies one
+// run of keys into LDS, then scores it; a decode step has too few keys per
+// workgroup to stream.
+//
+// Token blocks are the fastest grid dimension and the XCD-aware renumbering
+// keeps the workgroups sharing a key range on one XCD, so each key-state run
+// is fetched from HBM about once.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -49,33 +57,242 @@ struct IdxTraits {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename T, int DI, int PAIRS, int WAVES, int KR>
-__global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void indexer_score_kernel(
+// XCD-aware workgroup renumbering.  Workgroups are handed to the 8 XCDs
+// round-robin by linear id; renumber so that each XCD owns a contiguous range
+// of (token block, key block, batch) tiles in token-fastest order: the token
+// blocks that share a key range then run on one XCD and read it through that
+// XCD's L2.
+__device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
+  tx = blockIdx.x; ty = blockIdx.y; tz = blockIdx.z;
+  const int nx = gridDim.x, nxy = gridDim.x * gridDim.y;
+  const int total = nxy * gridDim.z;
+  if ((total & 7) == 0) {
+    const int lin = blockIdx.x + nx * blockIdx.y + nxy * blockIdx.z;
+    const int logical = (lin & 7) * (total >> 3) + (lin >> 3);
+    tz = logical / nxy;
+    ty = (logical - tz * nxy) / nx;
+    tx = logical - tz * nxy - ty * nx;
+  }
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// global_load_lds_dwordx4 written out, for copies whose completion the
+// caller tracks itself: the compiler does not see the LDS write, so it adds
+// no wait for it before later LDS reads (its alias analysis cannot tell the
+// two stream buffers apart and would wait for every outstanding load and
+// store).  Lane l's 16 bytes land at lds_dst + 16 * l.  M0 is saved and
+// restored, and one wait state separates its write from the load that
+// reads it.
+__device__ __forceinline__ void lds_dma16_untracked(const void* g, void* lds_dst) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_char*)lds_dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
+}
+
+// Direct global->LDS copy of key rows [j0, j1) of one sequence into dst.
+// Slot q holds chunk (q % kChunks) ^ swz(r) of row r = q / kChunks; a wave
+// fills 64 consecutive slots per load.  Rows are rounded up to whole 32-key
+// chunks; rows past j1 repeat row j1 - 1 (their scores are never stored).
+// UNTRACKED: issue the loads unseen by the compiler (see above).
+template <typename T, int DI, int NT, bool UNTRACKED>
+__device__ __forceinline__ void copy_key_rows(const T* __restrict__ ks_b, int j0, int j1,
+                                              uint4* __restrict__ dst, int wave, int l) {
+  using Tr = IdxTraits<T, DI>;
+  const int nvec = ((j1 - j0 + 31) & ~31) * Tr::kChunks;   // multiple of 64
+  for (int q0 = wave * kWave; q0 < nvec; q0 += NT) {
+    const int q = q0 + l;
+    const int r = q / Tr::kChunks, c = q % Tr::kChunks;
+    const int j = min(j0 + r, j1 - 1);
+    const T* src = ks_b + (size_t)j * DI + 8 * (c ^ Tr::swz(r));
+    if (UNTRACKED) lds_dma16_untracked(src, dst + q0);
+    else __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + q0), 16, 0, 0);
+  }
+}
+
+// A operands and head weights of one token pair (tokens s0, s0 + 1).
+// MFMA row m <-> token (m/4)%2 of the pair, head 4*(m/8) + m%4.  With the
+// 32x32 accumulator layout (element v of lane l is row 8*(v/4) + 4*(l/32)
+// + v%4) every lane then holds all 16 heads of one token, token l/32, as
+// elements v = head.  A operand: lane l supplies row l%32, k = 16*step +
+// 8*(l/32).  Loads are unconditional from clamped addresses (no per-load
+// branch); rows and heads out of range are zeroed afterwards.
+template <typename T, int DI>
+__device__ __forceinline__ void load_pair(const T* __restrict__ q_idx,
+                                          const float* __restrict__ w_idx, int b, int S, int H,
+                                          int s0, int col, int half,
+                                          typename vec8<T>::type (&a)[DI / 16], float (&wv)[16]) {
+  using V8 = typename vec8<T>::type;
+  {
+    const int s = s0 + ((col >> 2) & 1), h = 4 * (col >> 3) + (col & 3);
+    const bool ok = (s < S) && (h < H);
+    const T* src = q_idx + ((size_t)(b * S + min(s, S - 1)) * H + min(h, H - 1)) * DI;
+#pragma unroll
+    for (int st = 0; st < DI / 16; ++st) {
+      uint4 raw = ld_vec<uint4>(src + 16 * st + 8 * half);
+      if (!ok) raw = make_uint4(0, 0, 0, 0);
+      a[st] = __builtin_bit_cast(V8, raw);
+    }
+  }
+  const int s = s0 + half;
+  const float* wrow = w_idx + (size_t)(b * S + min(s, S - 1)) * H;
+  if (H == 16) {                       // 64-byte aligned row: four 16-byte loads
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const f32x4 w4 = ld_vec<f32x4>(wrow + 4 * v4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wv[4 * v4 + e] = w4[e];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) wv[v] = wrow[min(v, H - 1)];
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (s >= S || v >= H) wv[v] = 0.0f;
+}
+
+// Per-head dot products of one token pair with 32 keys: run row r of the
+// LDS copy is this lane's key (B column n = col).
+template <typename T, int DI, int PAIRS>
+__device__ __forceinline__ void score_chunk(const uint4* __restrict__ run, int r, int half,
+                                            const typename vec8<T>::type (&a)[PAIRS][DI / 16],
+                                            f32x16 (&acc)[PAIRS]) {
+  using Tr = IdxTraits<T, DI>;
+  using V8 = typename vec8<T>::type;
+#pragma unroll
+  for (int p = 0; p < PAIRS; ++p) acc[p] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < Tr::kSteps; ++st) {
+    const int ch = 2 * st + half;
+    const V8 bop = __builtin_bit_cast(V8, run[r * Tr::kChunks + (ch ^ Tr::swz(r))]);
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) acc[p] = mfma32x32x16(a[p][st], bop, acc[p]);
+  }
+}
+
+// Sum over the 16 heads (two chains of 8, then one add).
+__device__ __forceinline__ float head_sum(const float (&wv)[16], const f32x16& acc) {
+  float part0 = 0.0f, part1 = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) part0 += wv[v] * acc[v];
+#pragma unroll
+  for (int v = 8; v < 16; ++v) part1 += wv[v] * acc[v];
+  return part0 + part1;
+}
+
+// ------------------------------------------------------------------ prefill
+
+constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any record count used
+
+// Raw buffer resource (stride 0) over `bytes` bytes at p.  The fields pass
+// through readfirstlane so that the descriptor lives in scalar registers:
+// computed with vector instructions it would make every buffer store a
+// per-lane loop over distinct descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t nr = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)nr,
+                                           0x00020000);
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding, then a workgroup barrier with no memory fence (a fence would
+// wait for every outstanding store).  The empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+  // (15 = no wait), vmcnt[5:4] in bits [15:14].
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One stage of the key stream: issue the copy of the next run [jn, jn_end)
+// into `nxt` (none when jn >= jn_end), then score the run [jr, jr_end) held
+// in `cur`.  The copy is issued untracked: the wait for it is the caller's.
+// Every chunk issues exactly PAIRS buffer stores.
+template <typename T, int DI, int PAIRS, int NT>
+__device__ __forceinline__ void stream_stage(
+    const uint4* __restrict__ cur, uint4* __restrict__ nxt, const T* __restrict__ ks_b,
+    int jn, int jn_end, int jr, int jr_end, int wave, int l,
+    const typename vec8<T>::type (&a)[PAIRS][DI / 16], const float (&wv)[PAIRS][16],
+    __amdgpu_buffer_rsrc_t rs, const uint32_t (&row_off)[PAIRS]) {
+  if (jn < jn_end) copy_key_rows<T, DI, NT, true>(ks_b, jn, jn_end, nxt, wave, l);
+  const int half = l >> 5, col = l & 31;
+  for (int jc = jr; jc < jr_end; jc += 32) {
+    f32x16 acc[PAIRS];
+    score_chunk<T, DI, PAIRS>(cur, jc - jr + col, half, a, acc);
+    const bool key_ok = jc + col < jr_end;
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) {
+      const float total = head_sum(wv[p], acc[p]);
+      const uint32_t off = key_ok ? row_off[p] + 4u * (uint32_t)jc : kDropOffset;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), rs, off, 0, 0);
+    }
+  }
+}
+
+// The key stream [j_begin, j_end) in runs of R keys, the first already in b0.
+// Two stages per trip, the buffers swapping roles.  The wait before a stage
+// covers the copy issued at the start of the previous one: after it, that
+// stage (a full run of R keys) issued PAIRS * R / 32 stores.
+template <typename T, int DI, int PAIRS, int NT, int R>
+__device__ __forceinline__ void stream_keys(
+    uint4* __restrict__ b0, uint4* __restrict__ b1, const T* __restrict__ ks_b, int j_begin,
+    int j_end, int wave, int l, const typename vec8<T>::type (&a)[PAIRS][DI / 16],
+    const float (&wv)[PAIRS][16], __amdgpu_buffer_rsrc_t rs, const uint32_t (&row_off)[PAIRS]) {
+  constexpr int kStoresPerRun = PAIRS * R / 32;
+  int jr = j_begin;
+  while (true) {
+    int jr_end = min(jr + R, j_end);
+    stream_stage<T, DI, PAIRS, NT>(b0, b1, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+                                   wave, l, a, wv, rs, row_off);
+    if (jr_end >= j_end) break;
+    wait_vm_then_barrier<kStoresPerRun>();
+    jr = jr_end;
+    jr_end = min(jr + R, j_end);
+    stream_stage<T, DI, PAIRS, NT>(b1, b0, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+                                   wave, l, a, wv, rs, row_off);
+    if (jr_end >= j_end) break;
+    wait_vm_then_barrier<kStoresPerRun>();
+    jr = jr_end;
+  }
+}
+
+// R keys per LDS buffer (two buffers, 64 KB per workgroup: two workgroups
+// per CU).  Byte offsets within a wave's 4 score rows stay below 2^31 for
+// L_cap <= kIndexerMaxLcap.
+template <typename T, int DI, int PAIRS, int WAVES, int R>
+__global__ __launch_bounds__(WAVES * kWave, 4) void indexer_stream_kernel(
     const T* __restrict__ q_idx, const float* __restrict__ w_idx,
     const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
     int S, int H, int L_cap, int keys_per_wg, float* __restrict__ scores) {
   using Tr = IdxTraits<T, DI>;
   using V8 = typename vec8<T>::type;
   constexpr int NT = WAVES * kWave;
-  constexpr int kTokPerWg = 2 * PAIRS * WAVES;
-  __shared__ __attribute__((aligned(16))) uint4 run[KR * Tr::kChunks];
+  constexpr int kTokPerWave = 2 * PAIRS;
+  constexpr int kTokPerWg = kTokPerWave * WAVES;
+  static_assert(R % 32 == 0, "runs are whole 32-key chunks");
+  __shared__ __attribute__((aligned(16))) uint4 buf0[R * Tr::kChunks];
+  __shared__ __attribute__((aligned(16))) uint4 buf1[R * Tr::kChunks];
 
-  // Workgroups are handed to the 8 XCDs round-robin by linear id.  Renumber
-  // so that each XCD owns a contiguous range of (token block, key run, batch)
-  // tiles in token-fastest order: the token blocks that share a key run then
-  // run on one XCD and read it through that XCD's L2.
-  int tx = blockIdx.x, ty = blockIdx.y, tz = blockIdx.z;
-  {
-    const int nx = gridDim.x, nxy = gridDim.x * gridDim.y;
-    const int total = nxy * gridDim.z;
-    if ((total & 7) == 0) {
-      const int lin = blockIdx.x + nx * blockIdx.y + nxy * blockIdx.z;
-      const int logical = (lin & 7) * (total >> 3) + (lin >> 3);
-      tz = logical / nxy;
-      ty = (logical - tz * nxy) / nx;
-      tx = logical - tz * nxy - ty * nx;
-    }
-  }
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
   const int b = tz;
   int kvl = kv_len[b];
   kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
@@ -86,67 +303,74 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void indexer_sco
   const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
   if (j_begin >= j_end || j_begin > last_pos) return;
 
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const int half = l >> 5, col = l & 31;
+  const T* ks_b = key_state + (size_t)b * L_cap * DI;
+
+  copy_key_rows<T, DI, NT, true>(ks_b, j_begin, min(j_begin + R, j_end), buf0, wave, l);
+
+  V8 a[PAIRS][Tr::kSteps];
+  float wv[PAIRS][16];
+  const int s_w = s_first + wave * kTokPerWave;        // first token of this wave
+#pragma unroll
+  for (int p = 0; p < PAIRS; ++p)
+    load_pair<T, DI>(q_idx, w_idx, b, S, H, s_w + 2 * p, col, half, a[p], wv[p]);
+
+  // Score stores: one buffer resource per wave based at its first token's
+  // row; tokens past S fall outside its record count and are dropped.
+  const int n_tok = max(0, min(S - s_w, kTokPerWave));
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(
+      scores + ((size_t)b * S + min(s_w, S - 1)) * L_cap, (uint32_t)n_tok * (uint32_t)L_cap * 4u);
+  uint32_t row_off[PAIRS];
+#pragma unroll
+  for (int p = 0; p < PAIRS; ++p) {
+    const int t = 2 * p + half;
+    row_off[p] = t < n_tok ? (uint32_t)(t * L_cap + col) * 4u : kDropOffset;
+  }
+
+  wait_vmem();              // this wave's share of the first run has landed
+  __syncthreads();          // ... and every other wave's
+  stream_keys<T, DI, PAIRS, NT, R>(buf0, buf1, ks_b, j_begin, j_end, wave, l, a, wv, rs, row_off);
+}
+
+// ------------------------------------------------------------------ decode
+
+template <typename T, int DI, int PAIRS, int WAVES, int KR>
+__global__ __launch_bounds__(WAVES * kWave, 1) void indexer_score_kernel(
+    const T* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
+    int S, int H, int L_cap, int keys_per_wg, float* __restrict__ scores) {
+  using Tr = IdxTraits<T, DI>;
+  using V8 = typename vec8<T>::type;
+  constexpr int NT = WAVES * kWave;
+  constexpr int kTokPerWg = 2 * PAIRS * WAVES;
+  __shared__ __attribute__((aligned(16))) uint4 run[KR * Tr::kChunks];
+
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
+  const int b = tz;
+  int kvl = kv_len[b];
+  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
+  const int j_begin = ty * keys_per_wg;
+  const int j_end = min(j_begin + keys_per_wg, kvl);
+  const int s_first = tx * kTokPerWg;
+  const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
+  if (j_begin >= j_end || j_begin > last_pos) return;
+
   const int wave = threadIdx.x / kWave;
   const int l = lane_id();
   const int half = l >> 5;     // 0: lanes 0..31, 1: lanes 32..63
   const int col = l & 31;
+  const T* ks_b = key_state + (size_t)b * L_cap * DI;
+  copy_key_rows<T, DI, NT, false>(ks_b, j_begin, j_end, run, wave, l);
 
-  // ---- key run -> LDS.  Slot q holds chunk (q % kChunks) ^ swz(r) of
-  // run row r = q / kChunks; a wave fills 64 consecutive slots per load.
-  // Rows are rounded up to whole 32-key chunks; rows past the run repeat its
-  // last row (their scores are never stored).
-  {
-    const T* ks_b = key_state + (size_t)b * L_cap * DI;
-    const int nvec = ((j_end - j_begin + 31) & ~31) * Tr::kChunks;   // multiple of 64
-    for (int q0 = wave * kWave; q0 < nvec; q0 += NT) {
-      const int q = q0 + l;
-      const int r = q / Tr::kChunks, c = q % Tr::kChunks;
-      const int j = min(j_begin + r, j_end - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(ks_b + (size_t)j * DI + 8 * (c ^ Tr::swz(r))),
-                                       (lds_void*)(run + q0), 16, 0, 0);
-    }
-  }
-
-  // MFMA row m <-> token (m/4)%2 of the pair, head 4*(m/8) + m%4.  With the
-  // 32x32 accumulator layout (element v of lane l is row 8*(v/4) + 4*(l/32)
-  // + v%4) every lane then holds all 16 heads of one token, token l/32, as
-  // elements v = head.  A operand: lane l supplies row l%32, k = 16*step +
-  // 8*(l/32).
   V8 a[PAIRS][Tr::kSteps];
   float wv[PAIRS][16];
 #pragma unroll
-  for (int p = 0; p < PAIRS; ++p) {
-    const int s0 = s_first + wave * 2 * PAIRS + 2 * p;
-    // Loads are unconditional from clamped addresses (no per-load branch);
-    // rows and heads out of range are zeroed afterwards.
-    {
-      const int s = s0 + ((col >> 2) & 1), h = 4 * (col >> 3) + (col & 3);
-      const bool ok = (s < S) && (h < H);
-      const T* src = q_idx + ((size_t)(b * S + min(s, S - 1)) * H + min(h, H - 1)) * DI;
-#pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) {
-        uint4 raw = ld_vec<uint4>(src + 16 * st + 8 * half);
-        if (!ok) raw = make_uint4(0, 0, 0, 0);
-        a[p][st] = __builtin_bit_cast(V8, raw);
-      }
-    }
-    const int s = s0 + half;
-    const float* wrow = w_idx + (size_t)(b * S + min(s, S - 1)) * H;
-    if (H == 16) {                       // 64-byte aligned row: four 16-byte loads
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const f32x4 w4 = ld_vec<f32x4>(wrow + 4 * v4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[p][4 * v4 + e] = w4[e];
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) wv[p][v] = wrow[min(v, H - 1)];
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (s >= S || v >= H) wv[p][v] = 0.0f;
-  }
+  for (int p = 0; p < PAIRS; ++p)
+    load_pair<T, DI>(q_idx, w_idx, b, S, H, s_first + wave * 2 * PAIRS + 2 * p, col, half, a[p],
+                     wv[p]);
   // Score row of each pair's token for this lane (lanes 0..31: t0, 32..63: t1).
   float* srow[PAIRS];
   bool s_ok[PAIRS];
@@ -159,61 +383,52 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void indexer_sco
   wait_vmem();              // this wave's share of the run has landed in LDS
   __syncthreads();          // ... and every other wave's
 
-#pragma unroll 2
   for (int jc = j_begin; jc < j_end; jc += 32) {
-    const int r = jc - j_begin + col;      // this lane's run row (B column n = col)
     f32x16 acc[PAIRS];
-#pragma unroll
-    for (int p = 0; p < PAIRS; ++p) acc[p] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < Tr::kSteps; ++st) {
-      const int ch = 2 * st + half;
-      V8 bop = __builtin_bit_cast(V8, run[r * Tr::kChunks + (ch ^ Tr::swz(r))]);
-#pragma unroll
-      for (int p = 0; p < PAIRS; ++p) acc[p] = mfma32x32x16(a[p][st], bop, acc[p]);
-    }
+    score_chunk<T, DI, PAIRS>(run, jc - j_begin + col, half, a, acc);
     const bool key_ok = jc + col < j_end;
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p) {
-      // sum over the 16 heads (two chains of 8, then one add)
-      float part0 = 0.0f, part1 = 0.0f;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) part0 += wv[p][v] * acc[p][v];
-#pragma unroll
-      for (int v = 8; v < 16; ++v) part1 += wv[p][v] * acc[p][v];
-      const float total = part0 + part1;
+      const float total = head_sum(wv[p], acc[p]);
       if (s_ok[p] && key_ok) srow[p][jc] = total;
     }
   }
 }
 
+template <typename T, int DI, int PAIRS, int WAVES, int R>
+void launch_stream(const IndexerLaunch& a, hipStream_t st) {
+  dim3 grid(a.tok_blocks, a.key_blocks, a.B);
+  hipLaunchKernelGGL((indexer_stream_kernel<T, DI, PAIRS, WAVES, R>), grid, dim3(WAVES * kWave), 0,
+                     st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
+                     a.L_cap, a.keys_per_wg, a.scores);
+}
+
 template <typename T, int DI, int PAIRS, int WAVES, int KR>
-void launch_idx(const IndexerLaunch& a, hipStream_t st) {
+void launch_resident(const IndexerLaunch& a, hipStream_t st) {
   dim3 grid(a.tok_blocks, a.key_blocks, a.B);
   hipLaunchKernelGGL((indexer_score_kernel<T, DI, PAIRS, WAVES, KR>), grid, dim3(WAVES * kWave), 0,
                      st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
                      a.L_cap, a.keys_per_wg, a.scores);
 }
 
-// Largest key run a workgroup keeps in LDS: 64 KB at prefill (two
-// workgroups per CU), 32 KB at decode.
-template <int DI> constexpr int kPrefillRun = 65536 / (2 * DI);
-template <int DI> constexpr int kDecodeRun = 32768 / (2 * DI);
+// Keys per LDS buffer: prefill streams through two 32 KB buffers, decode
+// keeps one 32 KB run.
+template <int DI> constexpr int kRun = 32768 / (2 * DI);
 
-template <typename T, bool PREFILL>
+template <typename T>
 void launch_idx_d(const IndexerLaunch& a, hipStream_t st) {
   switch (a.D_idx) {
     case 32:
-      if (PREFILL) launch_idx<T, 32, 2, 8, kPrefillRun<32>>(a, st);
-      else launch_idx<T, 32, 1, 4, kDecodeRun<32>>(a, st);
+      if (a.prefill) launch_stream<T, 32, 2, 8, kRun<32>>(a, st);
+      else launch_resident<T, 32, 1, 4, kRun<32>>(a, st);
       break;
     case 64:
-      if (PREFILL) launch_idx<T, 64, 2, 8, kPrefillRun<64>>(a, st);
-      else launch_idx<T, 64, 1, 4, kDecodeRun<64>>(a, st);
+      if (a.prefill) launch_stream<T, 64, 2, 8, kRun<64>>(a, st);
+      else launch_resident<T, 64, 1, 4, kRun<64>>(a, st);
       break;
     default:   // one token pair per wave keeps the 128-dim operands in registers
-      if (PREFILL) launch_idx<T, 128, 1, 8, kPrefillRun<128>>(a, st);
-      else launch_idx<T, 128, 1, 4, kDecodeRun<128>>(a, st);
+      if (a.prefill) launch_stream<T, 128, 1, 8, kRun<128>>(a, st);
+      else launch_resident<T, 128, 1, 4, kRun<128>>(a, st);
       break;
   }
 }
@@ -225,21 +440,29 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
   a.B = B;
   a.S = S;
   a.D_idx = D_idx;
-  // Decode (S <= 8): 4 waves x 1 token pair.  Prefill: 8 waves x 2 pairs
-  // (1 pair for D_idx = 128), 32 tokens sharing every key run.
+  // Decode (S <= 8): 4 waves x 1 token pair, one key run per workgroup.
+  // Prefill: 8 waves x 2 pairs (1 pair for D_idx = 128) streaming key runs.
   const bool prefill = S > 8;
   a.prefill = prefill;
   a.pairs = prefill && D_idx < 128 ? 2 : 1;
   a.waves = prefill ? 8 : 4;
-  a.tile = (prefill ? 65536 : 32768) / (2 * D_idx);   // key-run capacity (LDS)
+  a.tile = 32768 / (2 * D_idx);      // keys per LDS buffer
   const int tok_per_wg = 2 * a.pairs * a.waves;
   a.tok_blocks = (S + tok_per_wg - 1) / tok_per_wg;
-  // Aim for ~1024 workgroups (4 per CU); runs are whole 32-key chunks and
-  // fit the LDS capacity.
-  const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
-  long long kpw = ((want + 31) / 32) * 32;
-  if (kpw < 32) kpw = 32;
-  if (kpw > a.tile) kpw = a.tile;
+  long long kpw;
+  if (prefill) {
+    // ~1024 workgroups (two rounds of two per CU), each streaming whole runs.
+    const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
+    kpw = ((want + a.tile - 1) / a.tile) * a.tile;
+    if (kpw < a.tile) kpw = a.tile;
+  } else {
+    // ~1024 workgroups (4 per CU); runs are whole 32-key chunks and fit the
+    // LDS capacity.
+    const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
+    kpw = ((want + 31) / 32) * 32;
+    if (kpw < 32) kpw = 32;
+    if (kpw > a.tile) kpw = a.tile;
+  }
   a.keys_per_wg = (int)kpw;
   a.key_blocks = (int)((max_kv_len + kpw - 1) / kpw);
   return a;
@@ -247,12 +470,8 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
 
 void launch_indexer(const IndexerLaunch& a, hipStream_t st) {
   if (a.key_blocks == 0 || a.tok_blocks == 0 || a.B == 0) return;
-  const bool prefill = a.prefill;
-  if (a.bf16) {
-    if (prefill) launch_idx_d<__bf16, true>(a, st); else launch_idx_d<__bf16, false>(a, st);
-  } else {
-    if (prefill) launch_idx_d<_Float16, true>(a, st); else launch_idx_d<_Float16, false>(a, st);
-  }
+  if (a.bf16) launch_idx_d<__bf16>(a, st);
+  else launch_idx_d<_Float16>(a, st);
 }
 
 }  // namespace dsa

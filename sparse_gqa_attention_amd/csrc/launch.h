@@ -18,14 +18,16 @@ struct IndexerLaunch {
   float* scores;
   int B, S, H, D_idx, L_cap;
   bool bf16;
-  bool prefill;     // S > 8: 8-wave workgroups, 64 KB key runs
+  bool prefill;     // S > 8: 8-wave workgroups streaming key runs
   int pairs;        // token pairs per wave (1 or 2)
   int waves;        // waves per workgroup
-  int tile;         // key-run capacity of a workgroup (keys held in LDS)
+  int tile;         // keys per LDS buffer
   int tok_blocks;   // grid.x
   int keys_per_wg;  // keys per workgroup
   int key_blocks;   // grid.y
 };
+// Largest L_cap the indexer supports (32-bit byte offsets of score stores).
+constexpr int kIndexerMaxLcap = 1 << 27;
 IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len);
 void launch_indexer(const IndexerLaunch& a, hipStream_t st);
 

@@ -72,3 +72,35 @@ def test_indexer_prefill_128k_sampled_rows(dsa):
         ref = oracle.indexer_scores_row(x["q_idx"][0, s], x["w_idx"][0, s], x["key_state"][0], pos)
         a, r = got[i, :pos + 1], ref[:pos + 1]
         assert np.array_equal(a, r), f"row {s}: {first_mismatch(a, r)}"
+
+
+# Prefill shapes long enough that each workgroup streams several key runs
+# through its two LDS buffers (odd and even run counts, a ragged last run,
+# partial token blocks, one short sequence), checked on sampled rows.
+# (B, S, H_idx, D_idx, L, kv_len, idx dtype, sampled token rows)
+STREAMED = [
+    (2, 70, 16, 64, 300000, [300000, 123457], "bf16", [0, 1, 2, 3, 31, 32, 63, 64, 65, 68, 69]),
+    (1, 40, 16, 32, 600000, None, "f16", [0, 7, 8, 33, 39]),
+    (1, 33, 8, 128, 400000, [399999], "bf16", [0, 15, 16, 31, 32]),
+]
+
+
+@pytest.mark.parametrize("case", STREAMED, ids=lambda c: f"B{c[0]}S{c[1]}D{c[3]}L{c[4]}")
+def test_indexer_prefill_streamed_sampled_rows(dsa, case):
+    B, S, H, Di, L, kv, dt, rows = case
+    say(f"indexer streamed prefill {case[:7]}")
+    w = scaled(SPEC_DECODE_32K, B=B, S=S, H_idx=H, D_idx=Di, L=L, H_q=2, H_kv=1, D=64,
+               idx_dtype=dt, seed=2000 + Di)
+    x = make_inputs(w, kv_len=kv)
+    scores = run_indexer(dsa, upload(x), L)
+    torch.cuda.synchronize()
+    kv_len = x["kv_len"].tolist()
+    for b in range(B):
+        got = scores[b, rows].cpu().double().numpy()
+        for i, s in enumerate(rows):
+            pos = kv_len[b] - S + s
+            ref = oracle.indexer_scores_row(x["q_idx"][b, s], x["w_idx"][b, s], x["key_state"][b],
+                                            pos)
+            a, r = got[i, :pos + 1], ref[:pos + 1]
+            assert np.array_equal(a, r), f"b={b} row {s}: {first_mismatch(a, r)}"
+            assert np.all(np.isnan(got[i, kv_len[b]:])), f"b={b} row {s}: wrote past kv_len"
