@@ -24,15 +24,20 @@
 // store issued after it, unless the count of those stores is known: scores
 // are written with buffer stores issued unconditionally (invalid lanes get an
 // out-of-range offset, which the hardware drops), so the wait names exactly
-// the stores of one run and never waits for their acknowledgement.
+// the stores of one run and never waits for their acknowledgement.  Full
+// runs are scored by fully unrolled code whose LDS reads, score stores and
+// copy addresses are lane constants plus immediate or scalar offsets, so the
+// vector ALU work per chunk is the head-weighted sums alone.
 //
 // Decode (indexer_score_kernel): a workgroup of 4 waves x 1 pair copies one
 // run of keys into LDS, then scores it; a decode step has too few keys per
 // workgroup to stream.
 //
-// Token blocks are the fastest grid dimension and the XCD-aware renumbering
-// keeps the workgroups sharing a key range on one XCD, so each key-state run
-// is fetched from HBM about once.
+// The XCD-aware renumbering dispatches the token blocks that share a key
+// range consecutively on one XCD and deals key ranges to the XCDs in turn,
+// so key-state runs are read through L2 (about 33 MB of HBM-side fetch for
+// a 2048-token prefill at 128K, against 1 GiB of LDS copies) and every XCD
+// gets an equal share of every sequence.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -58,20 +63,24 @@ struct IdxTraits {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // XCD-aware workgroup renumbering.  Workgroups are handed to the 8 XCDs
-// round-robin by linear id; renumber so that each XCD owns a contiguous range
-// of (token block, key block, batch) tiles in token-fastest order: the token
-// blocks that share a key range then run on one XCD and read it through that
-// XCD's L2.
+// round-robin by linear id.  A key group (key block ty of sequence tz) is
+// read by all tok_blocks token blocks; renumber so that each key group's
+// token blocks are dispatched consecutively on one XCD (they then share the
+// run through that XCD's L2) and key groups are dealt to the XCDs in turn,
+// so every XCD gets an equal share of every sequence's keys whatever the
+// sequence lengths.  Needs a multiple of 8 key groups (the planner rounds
+// the key blocks up); otherwise the dispatch order is kept.
 __device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
   tx = blockIdx.x; ty = blockIdx.y; tz = blockIdx.z;
-  const int nx = gridDim.x, nxy = gridDim.x * gridDim.y;
-  const int total = nxy * gridDim.z;
-  if ((total & 7) == 0) {
-    const int lin = blockIdx.x + nx * blockIdx.y + nxy * blockIdx.z;
-    const int logical = (lin & 7) * (total >> 3) + (lin >> 3);
-    tz = logical / nxy;
-    ty = (logical - tz * nxy) / nx;
-    tx = logical - tz * nxy - ty * nx;
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int groups = ny * gridDim.z;
+  if ((groups & 7) == 0) {
+    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int k = lin >> 3;                  // dispatch slot within the XCD
+    const int g = (k / nx) * 8 + (lin & 7);  // key group
+    tx = k - (k / nx) * nx;
+    tz = g / ny;
+    ty = g - tz * ny;
   }
 }
 
@@ -222,17 +231,127 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// global_load_lds_dwordx4 with a scalar base and a per-lane 32-bit byte
+// offset, untracked as above: lane l's 16 bytes from sbase + voff land at
+// lds_dst + 16 * l.
+__device__ __forceinline__ void lds_dma16_saddr_untracked(const void* sbase, uint32_t voff,
+                                                          void* lds_dst) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_char*)lds_dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m)
+      : "memory");
+}
+
+// Per-lane constants of a full run.  The swizzle depends on the low four
+// bits of the row only, and both the copy (NT / kChunks rows per load) and
+// the chunks (32 rows) advance the row by multiples of 16, so every address
+// of a full run is a lane constant plus a compile-time or scalar offset.
+template <typename T, int DI, int NT>
+struct FullRunLane {
+  using Tr = IdxTraits<T, DI>;
+  static_assert((NT / Tr::kChunks) % 16 == 0, "copy rows per load must keep the swizzle");
+  uint32_t dma_off;              // byte offset of this lane's 16-byte source chunk
+  uint32_t b_off[Tr::kSteps];    // uint4 index of this lane's B operand per K-step
+  __device__ __forceinline__ FullRunLane(int wave, int l) {
+    const int q = wave * kWave + l;
+    const int r = q / Tr::kChunks, c = q % Tr::kChunks;
+    dma_off = (uint32_t)(r * DI * (int)sizeof(T) + 16 * (c ^ Tr::swz(r)));
+    const int half = l >> 5, col = l & 31;
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st)
+      b_off[st] = (uint32_t)(col * Tr::kChunks + ((2 * st + half) ^ Tr::swz(col)));
+  }
+};
+
+// Copy of the R rows starting at src (a full run) into dst: the addresses
+// are scalar bases plus the lane constant, no per-load vector arithmetic.
+template <typename T, int DI, int NT, int R>
+__device__ __forceinline__ void copy_full_run(const T* __restrict__ src, uint4* __restrict__ dst,
+                                              int wave, const FullRunLane<T, DI, NT>& ln) {
+  using Tr = IdxTraits<T, DI>;
+  static_assert((R * Tr::kChunks) % NT == 0, "a full run is a whole number of loads per wave");
+  constexpr int kRowsPerLoad = NT / Tr::kChunks;
+#pragma unroll
+  for (int k = 0; k < R * Tr::kChunks / NT; ++k)
+    lds_dma16_saddr_untracked(src + (size_t)k * kRowsPerLoad * DI, ln.dma_off,
+                              dst + wave * kWave + k * NT);
+}
+
+// Scores of a full run [jr, jr + R) held in `cur`, fully unrolled: LDS reads
+// and score stores use immediate offsets from lane constants, so the VALU
+// work per chunk is the head-weighted sums alone.  Every chunk issues
+// exactly PAIRS buffer stores (all lanes in range: a full run has no key
+// past its end).
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
+__device__ __forceinline__ void score_full_run(
+    const uint4* __restrict__ cur, int jr, const FullRunLane<T, DI, NT>& ln,
+    const typename vec8<T>::type (&a)[PAIRS][DI / 16], const float (&wv)[PAIRS][16],
+    __amdgpu_buffer_rsrc_t rs, const uint32_t (&row_off)[PAIRS]) {
+  using Tr = IdxTraits<T, DI>;
+  using V8 = typename vec8<T>::type;
+  uint32_t off[PAIRS];
+#pragma unroll
+  for (int p = 0; p < PAIRS; ++p) off[p] = row_off[p] + 4u * (uint32_t)jr;
+  // PREFETCH: B operands of chunk c + 1 are read before chunk c's epilogue,
+  // so the LDS latency hides behind the head sums (16 more registers).
+  V8 bop[2][Tr::kSteps];
+#pragma unroll
+  for (int st = 0; st < Tr::kSteps; ++st)
+    bop[0][st] = __builtin_bit_cast(V8, cur[ln.b_off[st]]);
+#pragma unroll
+  for (int c = 0; c < R / 32; ++c) {
+    f32x16 acc[PAIRS];
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) acc[p] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st) {
+#pragma unroll
+      for (int p = 0; p < PAIRS; ++p) acc[p] = mfma32x32x16(a[p][st], bop[c & 1][st], acc[p]);
+    }
+    if (PREFETCH && c + 1 < R / 32) {
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st)
+        bop[(c + 1) & 1][st] =
+            __builtin_bit_cast(V8, cur[ln.b_off[st] + (c + 1) * 32 * Tr::kChunks]);
+    }
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs,
+                                            off[p] + 128u * c, 0, 0);
+    if (!PREFETCH && c + 1 < R / 32) {
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st)
+        bop[(c + 1) & 1][st] =
+            __builtin_bit_cast(V8, cur[ln.b_off[st] + (c + 1) * 32 * Tr::kChunks]);
+    }
+  }
+}
+
 // One stage of the key stream: issue the copy of the next run [jn, jn_end)
 // into `nxt` (none when jn >= jn_end), then score the run [jr, jr_end) held
 // in `cur`.  The copy is issued untracked: the wait for it is the caller's.
-// Every chunk issues exactly PAIRS buffer stores.
-template <typename T, int DI, int PAIRS, int NT>
+// Every chunk issues exactly PAIRS buffer stores.  Full runs take the
+// unrolled paths; the last, partial run of a range the general ones.
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
 __device__ __forceinline__ void stream_stage(
     const uint4* __restrict__ cur, uint4* __restrict__ nxt, const T* __restrict__ ks_b,
-    int jn, int jn_end, int jr, int jr_end, int wave, int l,
+    int jn, int jn_end, int jr, int jr_end, int wave, int l, const FullRunLane<T, DI, NT>& ln,
     const typename vec8<T>::type (&a)[PAIRS][DI / 16], const float (&wv)[PAIRS][16],
     __amdgpu_buffer_rsrc_t rs, const uint32_t (&row_off)[PAIRS]) {
-  if (jn < jn_end) copy_key_rows<T, DI, NT, true>(ks_b, jn, jn_end, nxt, wave, l);
+  if (jn_end - jn == R) copy_full_run<T, DI, NT, R>(ks_b + (size_t)jn * DI, nxt, wave, ln);
+  else if (jn < jn_end) copy_key_rows<T, DI, NT, true>(ks_b, jn, jn_end, nxt, wave, l);
+  if (jr_end - jr == R) {
+    score_full_run<T, DI, PAIRS, NT, R, PREFETCH>(cur, jr, ln, a, wv, rs, row_off);
+    return;
+  }
   const int half = l >> 5, col = l & 31;
   for (int jc = jr; jc < jr_end; jc += 32) {
     f32x16 acc[PAIRS];
@@ -240,9 +359,9 @@ __device__ __forceinline__ void stream_stage(
     const bool key_ok = jc + col < jr_end;
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p) {
-      const float total = head_sum(wv[p], acc[p]);
       const uint32_t off = key_ok ? row_off[p] + 4u * (uint32_t)jc : kDropOffset;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs, off, 0,
+                                            0);
     }
   }
 }
@@ -251,23 +370,24 @@ __device__ __forceinline__ void stream_stage(
 // Two stages per trip, the buffers swapping roles.  The wait before a stage
 // covers the copy issued at the start of the previous one: after it, that
 // stage (a full run of R keys) issued PAIRS * R / 32 stores.
-template <typename T, int DI, int PAIRS, int NT, int R>
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
 __device__ __forceinline__ void stream_keys(
     uint4* __restrict__ b0, uint4* __restrict__ b1, const T* __restrict__ ks_b, int j_begin,
-    int j_end, int wave, int l, const typename vec8<T>::type (&a)[PAIRS][DI / 16],
+    int j_end, int wave, int l, const FullRunLane<T, DI, NT>& ln,
+    const typename vec8<T>::type (&a)[PAIRS][DI / 16],
     const float (&wv)[PAIRS][16], __amdgpu_buffer_rsrc_t rs, const uint32_t (&row_off)[PAIRS]) {
   constexpr int kStoresPerRun = PAIRS * R / 32;
   int jr = j_begin;
   while (true) {
     int jr_end = min(jr + R, j_end);
-    stream_stage<T, DI, PAIRS, NT>(b0, b1, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
-                                   wave, l, a, wv, rs, row_off);
+    stream_stage<T, DI, PAIRS, NT, R, PREFETCH>(b0, b1, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+                                      wave, l, ln, a, wv, rs, row_off);
     if (jr_end >= j_end) break;
     wait_vm_then_barrier<kStoresPerRun>();
     jr = jr_end;
     jr_end = min(jr + R, j_end);
-    stream_stage<T, DI, PAIRS, NT>(b1, b0, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
-                                   wave, l, a, wv, rs, row_off);
+    stream_stage<T, DI, PAIRS, NT, R, PREFETCH>(b1, b0, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+                                      wave, l, ln, a, wv, rs, row_off);
     if (jr_end >= j_end) break;
     wait_vm_then_barrier<kStoresPerRun>();
     jr = jr_end;
@@ -277,8 +397,8 @@ __device__ __forceinline__ void stream_keys(
 // R keys per LDS buffer (two buffers, 64 KB per workgroup: two workgroups
 // per CU).  Byte offsets within a wave's 4 score rows stay below 2^31 for
 // L_cap <= kIndexerMaxLcap.
-template <typename T, int DI, int PAIRS, int WAVES, int R>
-__global__ __launch_bounds__(WAVES * kWave, 4) void indexer_stream_kernel(
+template <typename T, int DI, int PAIRS, int WAVES, int R, int WPE, bool PREFETCH>
+__global__ __launch_bounds__(WAVES * kWave, WPE) void indexer_stream_kernel(
     const T* __restrict__ q_idx, const float* __restrict__ w_idx,
     const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
     int S, int H, int L_cap, int keys_per_wg, float* __restrict__ scores) {
@@ -308,7 +428,9 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void indexer_stream_kernel(
   const int half = l >> 5, col = l & 31;
   const T* ks_b = key_state + (size_t)b * L_cap * DI;
 
-  copy_key_rows<T, DI, NT, true>(ks_b, j_begin, min(j_begin + R, j_end), buf0, wave, l);
+  const FullRunLane<T, DI, NT> ln(wave, l);
+  if (j_end - j_begin >= R) copy_full_run<T, DI, NT, R>(ks_b + (size_t)j_begin * DI, buf0, wave, ln);
+  else copy_key_rows<T, DI, NT, true>(ks_b, j_begin, j_end, buf0, wave, l);
 
   V8 a[PAIRS][Tr::kSteps];
   float wv[PAIRS][16];
@@ -331,7 +453,8 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void indexer_stream_kernel(
 
   wait_vmem();              // this wave's share of the first run has landed
   __syncthreads();          // ... and every other wave's
-  stream_keys<T, DI, PAIRS, NT, R>(buf0, buf1, ks_b, j_begin, j_end, wave, l, a, wv, rs, row_off);
+  stream_keys<T, DI, PAIRS, NT, R, PREFETCH>(buf0, buf1, ks_b, j_begin, j_end, wave, l, ln, a, wv, rs,
+                                   row_off);
 }
 
 // ------------------------------------------------------------------ decode
@@ -395,12 +518,32 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void indexer_score_kernel(
   }
 }
 
-template <typename T, int DI, int PAIRS, int WAVES, int R>
+// Prefill workgroup shapes per D_idx: waves, token pairs per wave, keys per
+// LDS buffer (two buffers), the launch bound in waves per SIMD, workgroups
+// resident per CU (LDS- and register-limited), and whether a full run
+// reads the next chunk's B operands ahead.
+template <int DI> struct StreamCfg;
+template <> struct StreamCfg<32> {
+  static constexpr int kWaves = 8, kPairs = 2, kRun = 512, kWpe = 4, kWgPerCu = 2;
+  static constexpr bool kPrefetch = false;
+};
+template <> struct StreamCfg<64> {
+  static constexpr int kWaves = 8, kPairs = 2, kRun = 256, kWpe = 4, kWgPerCu = 2;
+  static constexpr bool kPrefetch = false;
+};
+template <> struct StreamCfg<128> {    // one pair keeps the 128-dim operands in registers
+  static constexpr int kWaves = 8, kPairs = 1, kRun = 128, kWpe = 4, kWgPerCu = 2;
+  static constexpr bool kPrefetch = false;
+};
+
+template <typename T, int DI>
 void launch_stream(const IndexerLaunch& a, hipStream_t st) {
+  using C = StreamCfg<DI>;
   dim3 grid(a.tok_blocks, a.key_blocks, a.B);
-  hipLaunchKernelGGL((indexer_stream_kernel<T, DI, PAIRS, WAVES, R>), grid, dim3(WAVES * kWave), 0,
-                     st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
-                     a.L_cap, a.keys_per_wg, a.scores);
+  hipLaunchKernelGGL(
+      (indexer_stream_kernel<T, DI, C::kPairs, C::kWaves, C::kRun, C::kWpe, C::kPrefetch>), grid,
+      dim3(C::kWaves * kWave), 0, st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state,
+      a.kv_len, a.S, a.H, a.L_cap, a.keys_per_wg, a.scores);
 }
 
 template <typename T, int DI, int PAIRS, int WAVES, int KR>
@@ -411,27 +554,37 @@ void launch_resident(const IndexerLaunch& a, hipStream_t st) {
                      a.L_cap, a.keys_per_wg, a.scores);
 }
 
-// Keys per LDS buffer: prefill streams through two 32 KB buffers, decode
-// keeps one 32 KB run.
-template <int DI> constexpr int kRun = 32768 / (2 * DI);
+// Decode keeps one 32 KB run per workgroup (4 waves x 1 token pair).
+template <int DI> constexpr int kDecodeRun = 32768 / (2 * DI);
 
 template <typename T>
 void launch_idx_d(const IndexerLaunch& a, hipStream_t st) {
   switch (a.D_idx) {
     case 32:
-      if (a.prefill) launch_stream<T, 32, 2, 8, kRun<32>>(a, st);
-      else launch_resident<T, 32, 1, 4, kRun<32>>(a, st);
+      if (a.prefill) launch_stream<T, 32>(a, st);
+      else launch_resident<T, 32, 1, 4, kDecodeRun<32>>(a, st);
       break;
     case 64:
-      if (a.prefill) launch_stream<T, 64, 2, 8, kRun<64>>(a, st);
-      else launch_resident<T, 64, 1, 4, kRun<64>>(a, st);
+      if (a.prefill) launch_stream<T, 64>(a, st);
+      else launch_resident<T, 64, 1, 4, kDecodeRun<64>>(a, st);
       break;
-    default:   // one token pair per wave keeps the 128-dim operands in registers
-      if (a.prefill) launch_stream<T, 128, 1, 8, kRun<128>>(a, st);
-      else launch_resident<T, 128, 1, 4, kRun<128>>(a, st);
+    default:
+      if (a.prefill) launch_stream<T, 128>(a, st);
+      else launch_resident<T, 128, 1, 4, kDecodeRun<128>>(a, st);
       break;
   }
 }
+
+template <int DI>
+void stream_shape(IndexerLaunch& a, int& wg_per_cu) {
+  using C = StreamCfg<DI>;
+  a.waves = C::kWaves;
+  a.pairs = C::kPairs;
+  a.tile = C::kRun;
+  wg_per_cu = C::kWgPerCu;
+}
+
+constexpr int kNumCUs = 256;
 
 }  // namespace
 
@@ -440,31 +593,53 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
   a.B = B;
   a.S = S;
   a.D_idx = D_idx;
-  // Decode (S <= 8): 4 waves x 1 token pair, one key run per workgroup.
-  // Prefill: 8 waves x 2 pairs (1 pair for D_idx = 128) streaming key runs.
-  const bool prefill = S > 8;
+  // Decode (S <= 8) keeps one run per workgroup; a context so long that its
+  // key blocks would exceed the grid's y limit streams as prefill does.
+  const bool prefill = S > 8 || (long long)max_kv_len > 60000LL * (32768 / (2 * D_idx));
   a.prefill = prefill;
-  a.pairs = prefill && D_idx < 128 ? 2 : 1;
-  a.waves = prefill ? 8 : 4;
-  a.tile = 32768 / (2 * D_idx);      // keys per LDS buffer
-  const int tok_per_wg = 2 * a.pairs * a.waves;
-  a.tok_blocks = (S + tok_per_wg - 1) / tok_per_wg;
-  long long kpw;
   if (prefill) {
-    // ~1024 workgroups (two rounds of two per CU), each streaming whole runs.
-    const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
-    kpw = ((want + a.tile - 1) / a.tile) * a.tile;
-    if (kpw < a.tile) kpw = a.tile;
+    // Streaming workgroups.  Each takes a whole number of runs; pick the
+    // runs per workgroup that minimise the modelled time: dispatch rounds
+    // of the resident workgroup slots, each as long as one workgroup's runs
+    // plus about half a run of prologue (query operands, first copy).
+    int wg_per_cu = 1;
+    if (D_idx == 32) stream_shape<32>(a, wg_per_cu);
+    else if (D_idx == 64) stream_shape<64>(a, wg_per_cu);
+    else stream_shape<128>(a, wg_per_cu);
+    const int tok_per_wg = 2 * a.pairs * a.waves;
+    a.tok_blocks = (S + tok_per_wg - 1) / tok_per_wg;
+    const long long runs = ((long long)max_kv_len + a.tile - 1) / a.tile;
+    const long long slots = (long long)kNumCUs * wg_per_cu;
+    const long long tiles_per_run = (long long)a.tok_blocks * B;
+    long long best_rpw = 1;
+    double best_time = -1.0;
+    const long long max_rpw = runs < 4096 ? runs : 4096;
+    for (long long rpw = 1; rpw <= max_rpw; ++rpw) {
+      const long long kb = (((runs + rpw - 1) / rpw) + 7) & ~7LL;
+      const long long rounds = (tiles_per_run * kb + slots - 1) / slots;
+      const double t = (double)rounds * ((double)rpw + 0.5);
+      if (best_time < 0.0 || t < best_time - 1e-9) {
+        best_time = t;
+        best_rpw = rpw;
+      }
+    }
+    a.keys_per_wg = (int)(best_rpw * a.tile);
   } else {
-    // ~1024 workgroups (4 per CU); runs are whole 32-key chunks and fit the
-    // LDS capacity.
+    // Decode (S <= 8): 4 waves x 1 token pair, one key run per workgroup;
+    // ~1024 workgroups (4 per CU), runs of whole 32-key chunks.
+    a.pairs = 1;
+    a.waves = 4;
+    a.tile = 32768 / (2 * D_idx);
+    a.tok_blocks = (S + 7) / 8;
     const long long want = ((long long)max_kv_len * B * a.tok_blocks + 1023) / 1024;
-    kpw = ((want + 31) / 32) * 32;
+    long long kpw = ((want + 31) / 32) * 32;
     if (kpw < 32) kpw = 32;
     if (kpw > a.tile) kpw = a.tile;
+    a.keys_per_wg = (int)kpw;
   }
-  a.keys_per_wg = (int)kpw;
-  a.key_blocks = (int)((max_kv_len + kpw - 1) / kpw);
+  // Key blocks rounded up to a multiple of 8 for the XCD renumbering; the
+  // extra blocks start past max_kv_len and exit at once.
+  a.key_blocks = (int)((((long long)max_kv_len + a.keys_per_wg - 1) / a.keys_per_wg + 7) & ~7LL);
   return a;
 }
 
