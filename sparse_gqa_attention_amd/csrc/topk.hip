@@ -573,19 +573,34 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // ====================================================================== multi plan
 enum { kModeAll = 0, kModeList = 1, kModeExact = 2 };
 
+// Candidates of chunk c of a row are kept in index order: in the chunk's
+// own slots when there are at most kSlotCap of them, else in a block of the
+// row's pool reserved with one atomic.  Meta[c] = (count, pool offset or
+// kNoPool).  A pool that would overflow flags the row for the exact path.
+constexpr int kSlotCap = 64;
+constexpr uint32_t kNoPool = 0xFFFFFFFFu;
+// Chunks of 256..2048 keys: at most 2^24 / 2048 per row (a chunk below 2048
+// keys only when the row has at most 1024 of them).
+constexpr int kMaxChunks = 8192;
+
 struct MultiWs {
-  uint32_t* state;   // [rows][4]: T_lo, mode, list count, spare
-  uint2* list;       // [rows][kMultiCap]: (key, index)
+  uint32_t* state;   // [rows][4]: T_lo, mode, pool count, pool overflow flag
+  uint2* meta;       // [rows][chunks]: (candidates, pool offset | kNoPool)
+  uint2* slots;      // [rows][chunks][kSlotCap]: (key, index)
+  uint2* pool;       // [rows][kMultiCap]: (key, index)
 };
 
-__host__ __device__ inline MultiWs carve(void* ws, int rows) {
+__host__ __device__ inline MultiWs carve(void* ws, int rows, int chunks) {
   MultiWs m;
   m.state = (uint32_t*)ws;
-  m.list = (uint2*)((uint32_t*)ws + (size_t)rows * 4);
+  m.meta = (uint2*)(m.state + (size_t)rows * 4);
+  m.slots = m.meta + (size_t)rows * chunks;
+  m.pool = m.slots + (size_t)rows * chunks * kSlotCap;
   return m;
 }
-__host__ inline size_t multi_ws_bytes(int rows) {
-  return (size_t)rows * 4 * 4 + (size_t)rows * kMultiCap * sizeof(uint2);
+__host__ inline size_t multi_ws_bytes(int rows, int chunks) {
+  return (size_t)rows * 4 * 4 +
+         (size_t)rows * ((size_t)chunks * (1 + kSlotCap) + kMultiCap) * sizeof(uint2);
 }
 
 constexpr int kStateThreads = 1024;
@@ -634,55 +649,80 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
   if (t == 0) { st[0] = T_lo; st[1] = mode; st[2] = 0; st[3] = 0; }
 }
 
-// KB: candidates of one chunk appended to the row's list (one reservation).
+// KB: candidates of one chunk, in index order.  Lane t owns the U
+// consecutive keys j0 + U t + [0, U), so a block scan of the per-lane counts
+// gives every candidate its rank in the chunk.
+template <int U, bool VEC>
 __global__ __launch_bounds__(kChunkThreads) void topk_collect_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int chunk, MultiWs m) {
+    int chunk, int chunks, MultiWs m) {
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t base_slot;
+  __shared__ uint32_t pool_base;
   const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
-  const uint32_t* st = m.state + row * 4;
+  uint32_t* st = m.state + row * 4;
   if (st[1] != kModeList) return;
   const uint32_t T_lo = st[0];
   const int n = row_count(kv_len, row, S, L_cap);
   const int j0 = c * chunk, j1 = min(j0 + chunk, n);
   if (j0 >= j1) return;
-  const float* src = scores + (size_t)row * L_cap;
-  constexpr int U = kChunkKeysPerThread;    // chunk <= U * kChunkThreads
+  const float* src = scores + (size_t)row * L_cap + j0 + U * t;
+  const int lim = j1 - j0 - U * t;          // keys of this lane inside the row: min(U, lim)
+  float v[U];
+  if (VEC && lim >= U) {                    // 16-byte aligned: L_cap % 4 == 0, U % 4 == 0
+#pragma unroll
+    for (int u4 = 0; u4 < U / 4; ++u4) {
+      const float4 q = reinterpret_cast<const float4*>(src)[u4];
+      v[4 * u4] = q.x; v[4 * u4 + 1] = q.y; v[4 * u4 + 2] = q.z; v[4 * u4 + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = u < lim ? src[u] : 0.0f;
+  }
   uint32_t key[U];
-  uint32_t cnt = 0;
+  uint32_t hits = 0, cnt = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int j = j0 + u * kChunkThreads + t;
-    key[u] = j < j1 ? score_key(src[j]) : 0u;
-    cnt += (j < j1 && key[u] >= T_lo) ? 1u : 0u;
+    key[u] = score_key(v[u]);
+    const bool hit = u < lim && key[u] >= T_lo;
+    hits |= (uint32_t)hit << u;
+    cnt += hit ? 1u : 0u;
   }
   uint32_t total;
   uint32_t pos = block_exclusive_scan<kChunkThreads>(cnt, scratch, &total);
-  if (total == 0) return;
-  if (t == 0) base_slot = atomicAdd(&m.state[row * 4 + 2], total);
-  __syncthreads();
-  pos += base_slot;
-  uint2* list = m.list + (size_t)row * kMultiCap;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = j0 + u * kChunkThreads + t;
-    if (j < j1 && key[u] >= T_lo) {
-      if (pos < (uint32_t)kMultiCap) list[pos] = make_uint2(key[u], (uint32_t)j);
-      ++pos;
+  uint2* dst = m.slots + ((size_t)row * chunks + c) * kSlotCap;
+  uint32_t poff = kNoPool;
+  if (total > (uint32_t)kSlotCap) {
+    if (t == 0) pool_base = atomicAdd(&st[2], total);
+    __syncthreads();
+    poff = pool_base;
+    if (poff + total > (uint32_t)kMultiCap) {      // the row's list is too long
+      if (t == 0) st[3] = 1u;
+      return;
     }
+    dst = m.pool + (size_t)row * kMultiCap + poff;
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (hits >> u & 1u) dst[pos++] = make_uint2(key[u], (uint32_t)(j0 + U * t + u));
+  if (t == 0) m.meta[(size_t)row * chunks + c] = make_uint2(total, poff);
 }
 
 // KC: exact selection and ordered emission, one workgroup per row.
-// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | bitmap segment; the
-// fallback's sel/tie segments reuse the list area.
-constexpr size_t kFinishLds = (size_t)(2 * kMultiCap + kSegWords) * 4;
+// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | chunk prefix offsets
+// [chunks + 1] | chunk pool offsets [chunks]; the fallback's sel/tie
+// segments reuse the list area.
+__host__ inline size_t finish_lds_bytes(int chunks) {
+  return (size_t)(2 * kMultiCap + 2 * chunks + 1) * 4;
+}
 static_assert(kMultiCap >= kSegWords, "fallback segments must fit the list area");
+
+template <int NT>
+__device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
+                             uint32_t take, int32_t* out, uint32_t* scratch);
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, MultiWs m, int32_t* __restrict__ indices) {
+    int k, int chunk, int chunks, MultiWs m, int32_t* __restrict__ indices) {
   constexpr int NT = kFinishThreads;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scratch[32];
@@ -691,37 +731,90 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   Lds s{hist, scratch, misc};
   uint32_t* lkey = dyn;
   uint32_t* lidx = dyn + kMultiCap;
-  uint32_t* bm = dyn + 2 * kMultiCap;
+  uint32_t* pre = dyn + 2 * kMultiCap;          // [chunks + 1]
+  uint32_t* poff = pre + chunks + 1;            // [chunks]
   const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
   int32_t* out = indices + (size_t)row * k;
   const uint32_t* st = m.state + row * 4;
   const uint32_t mode = st[1];
   if (mode == kModeAll) { write_all<NT>(out, n, k); return; }
-  const int cnt = (int)st[2];
   const float* src = scores + (size_t)row * L_cap;
-  if (mode == kModeList && cnt >= k && cnt <= kMultiCap) {
-    const uint4* list4 = reinterpret_cast<const uint4*>(m.list + (size_t)row * kMultiCap);
-    constexpr int U = kMultiCap / 2 / NT;   // two entries per 16-byte load
-    uint4 e[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i2 = u * NT + t;
-      e[u] = 2 * i2 < cnt ? list4[i2] : make_uint4(0, 0, 0, 0);
+  if (mode == kModeList && st[3] == 0u) {
+    // chunk counts -> prefix offsets (lane t sums chunks [cpt t, cpt (t+1)))
+    const int nch = (n + chunk - 1) / chunk;
+    const int cpt = (nch + NT - 1) / NT;
+    const int c0 = min(t * cpt, nch), c1 = min(c0 + cpt, nch);
+    const uint2* meta = m.meta + (size_t)row * chunks;
+    uint32_t local = 0;
+    for (int c = c0; c < c1; ++c) local += meta[c].x;
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<NT>(local, scratch, &total);
+    for (int c = c0; c < c1; ++c) {
+      const uint2 mc = meta[c];
+      pre[c] = run;
+      poff[c] = mc.y;
+      run += mc.x;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i2 = u * NT + t;
-      if (2 * i2 < cnt) { lkey[2 * i2] = e[u].x; lidx[2 * i2] = e[u].y; }
-      if (2 * i2 + 1 < cnt) { lkey[2 * i2 + 1] = e[u].z; lidx[2 * i2 + 1] = e[u].w; }
-    }
+    if (t == 0) pre[nch] = total;
     __syncthreads();
-    select_from_list<NT>([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, cnt, n,
-                         k, bm, out, s);
-    return;
+    if (total >= (uint32_t)k && total <= (uint32_t)kMultiCap) {
+      // gather in index order: entry i belongs to the chunk c with
+      // pre[c] <= i < pre[c + 1]
+      const uint2* slots = m.slots + (size_t)row * chunks * kSlotCap;
+      const uint2* pool = m.pool + (size_t)row * kMultiCap;
+      for (int i = t; i < (int)total; i += NT) {
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+        }
+        const uint32_t r = (uint32_t)i - pre[lo];
+        const uint2 e = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
+        lkey[i] = e.x;
+        lidx[i] = e.y;
+      }
+      __syncthreads();
+      uint32_t T, take, eq;
+      radix_select<NT>([&](int i, uint32_t& key) { key = lkey[i]; return true; }, (int)total,
+                       (uint32_t)k, s, T, take, eq);
+      emit_ordered<NT>(lkey, lidx, (int)total, T, take, out, scratch);
+      return;
+    }
   }
   select_exact_row<NT>([&](int j) { return score_key(src[j]); }, n, k, dyn, dyn + kSegWords,
                        out, s);
+}
+
+// Ordered emission from a list sorted by index: entry i is kept iff its key
+// is above T, or equals T and fewer than `take` keys equal to T come before
+// it; its output slot is the number of kept entries before it.  One block
+// scan of the two counts packed in 16-bit halves (m <= kMultiCap < 2^16).
+template <int NT>
+__device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
+                             uint32_t take, int32_t* out, uint32_t* scratch) {
+  static_assert(kMultiCap < 65536, "packed counts");
+  const int per = (m + NT - 1) / NT;
+  const int i0 = min(threadIdx.x * per, m), i1 = min(i0 + per, m);
+  uint32_t gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = lkey[i];
+    gt += key > T ? 1u : 0u;
+    eq += key == T ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<NT>(gt | (eq << 16), scratch, &total);
+  uint32_t g = before & 0xFFFFu, e = before >> 16;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = lkey[i];
+    if (key > T) {
+      out[g + (e < take ? e : take)] = (int32_t)lidx[i];
+      ++g;
+    } else if (key == T) {
+      if (e < take) out[g + e] = (int32_t)lidx[i];
+      ++e;
+    }
+  }
 }
 
 template <typename K>
@@ -753,7 +846,8 @@ TopkPlan plan_topk(int B, int S, int L_cap, int k) {
     while (ch < want && ch < kChunkKeysPerThread * kChunkThreads) ch *= 2;
     p.chunk = ch;
     p.chunks = (L_cap + ch - 1) / ch;
-    p.ws_bytes = multi_ws_bytes(p.rows);
+    if (p.chunks > kMaxChunks) p.chunks = kMaxChunks;     // unreachable for L_cap <= 2^24
+    p.ws_bytes = multi_ws_bytes(p.rows, p.chunks);
   }
   return p;
 }
@@ -765,7 +859,7 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   if (!lds_opt_in) {
     opt_in_lds(topk_resident_kernel<kResThreads>, kResLds);
     opt_in_lds(topk_stream_kernel<512, kRowCap>, Stream512::kLds);
-    opt_in_lds(topk_finish_kernel, kFinishLds);
+    opt_in_lds(topk_finish_kernel, finish_lds_bytes(kMaxChunks));
     lds_opt_in = true;
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
@@ -779,13 +873,35 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
                          scores, kv_len, S, L_cap, k, vec4, indices);
       return;
     default: {
-      MultiWs m = carve(ws, p.rows);
+      MultiWs m = carve(ws, p.rows, p.chunks);
       hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.rows), dim3(kStateThreads), 0, st, scores,
                          kv_len, S, L_cap, k, m);
-      hipLaunchKernelGGL(topk_collect_kernel, dim3(p.chunks, p.rows), dim3(kChunkThreads), 0, st,
-                         scores, kv_len, S, L_cap, p.chunk, m);
-      hipLaunchKernelGGL(topk_finish_kernel, dim3(p.rows), dim3(kFinishThreads), kFinishLds, st,
-                         scores, kv_len, S, L_cap, k, m, indices);
+      const dim3 cg(p.chunks, p.rows);
+      switch (p.chunk / kChunkThreads) {
+        case 1:
+          hipLaunchKernelGGL((topk_collect_kernel<1, false>), cg, dim3(kChunkThreads), 0, st,
+                             scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          break;
+        case 2:
+          hipLaunchKernelGGL((topk_collect_kernel<2, false>), cg, dim3(kChunkThreads), 0, st,
+                             scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          break;
+        case 4:
+          if (vec4) hipLaunchKernelGGL((topk_collect_kernel<4, true>), cg, dim3(kChunkThreads), 0,
+                                       st, scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          else hipLaunchKernelGGL((topk_collect_kernel<4, false>), cg, dim3(kChunkThreads), 0, st,
+                                  scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          break;
+        default:
+          if (vec4) hipLaunchKernelGGL((topk_collect_kernel<8, true>), cg, dim3(kChunkThreads), 0,
+                                       st, scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          else hipLaunchKernelGGL((topk_collect_kernel<8, false>), cg, dim3(kChunkThreads), 0, st,
+                                  scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+          break;
+      }
+      hipLaunchKernelGGL(topk_finish_kernel, dim3(p.rows), dim3(kFinishThreads),
+                         finish_lds_bytes(p.chunks), st, scores, kv_len, S, L_cap, k, p.chunk,
+                         p.chunks, m, indices);
     }
   }
 }

@@ -127,3 +127,34 @@ def test_topk_sample_heavy_rows_use_exact_fallback(dsa, B, S, L, k, sample):
         pos = _sample_positions(n, sample)
         sc[0, s, pos] = 1000.0 + r.integers(0, 50, size=pos.shape[0])
     _check(dsa, torch.from_numpy(sc), [L], k, what=f"sample-heavy/{sample}")
+
+
+@pytest.mark.parametrize("B,S,L,k,span", [(1, 8, 262144, 2048, 3000),    # last chunks overflow their slots
+                                          (2, 4, 100000, 1500, 40000)])  # spread over many chunks
+def test_topk_recency_clustered_candidates(dsa, B, S, L, k, span):
+    # Scores with the top-k concentrated in the most recent `span` positions
+    # of each row: in the multi plan the chunks there hold far more
+    # candidates than their own slots, so their lists go to the row's pool
+    # while the older chunks keep theirs; the merged list must stay ordered.
+    r = rng(16)
+    sc = r.standard_normal((B, S, L)).astype(np.float32)
+    kv = [L] * B
+    for b in range(B):
+        for s in range(S):
+            n = kv[b] - S + s + 1
+            sc[b, s, max(0, n - span):n] += 4.0
+    _check(dsa, torch.from_numpy(sc), kv, k, what=f"recency/{span}")
+
+
+def test_topk_ties_across_chunks_keep_lowest_indices(dsa):
+    # 4000 keys share the top value 2.0 at random positions over the whole
+    # row, the rest lie in [0, 1): the k-th largest value is 2.0 and only the
+    # 3000 lowest-indexed of its keys (spread over every chunk) may be taken.
+    r = rng(17)
+    B, S, L, k = 1, 8, 90000, 3000
+    sc = r.random((B, S, L)).astype(np.float32)
+    for s in range(S):
+        sc[0, s, r.choice(L - S, size=4000, replace=False)] = 2.0
+    got = _check(dsa, torch.from_numpy(sc), [L], k, what="ties across chunks")
+    tied = np.flatnonzero(sc[0, 0, :L - S + 1] == 2.0)
+    assert np.array_equal(got[0, 0], tied[:k])
