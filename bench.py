@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "85f31d24df1d7c22",
-    "spec_decode_32k": {"indexer": 5431027, "topk": 1416774, "attention": 16382615 + 1700646},
-    "decode_256k": {"indexer": 42127818, "topk": 227301 + 8795785 + 524361, "attention": 18599302 + 1700666},
-    "prefill_128k": {"indexer": 2187158527, "topk": 1156417558, "attention": 2386535726},
-    "int8_batched_decode_64k": {"attention": 1149192037 + 9736040},
+    "sources": "700252953cbead24",
+    "spec_decode_32k": {"attention": 18088150, "indexer": 5430491, "topk": 1415101},
+    "decode_256k": {"attention": 20310951, "indexer": 42130824, "topk": 9556294},
+    "prefill_128k": {"attention": 2390782706, "indexer": 1141511291, "topk": 1156724273},
+    "int8_batched_decode_64k": {"attention": 1157511915},
 }
 
 

@@ -55,7 +55,6 @@ struct AttnParams {
   float scale;
   int aux_tokens;     // cache keys at positions >= kv_len - aux_tokens are not attended
   int kvl_const;      // >= 0: use this live length for every sequence (aux keys)
-  int dense;          // key slot j is key j (no index list)
   int write_partial;  // write (m, l, O) partials instead of the output
   int part_stride;    // splits per (row, head) in the partial buffer
   int part_offset;    // first split index of this launch
@@ -136,7 +135,8 @@ struct AttnCfg {
       kVBytes + kSclBytes > kMergeBytes ? kVBytes + kSclBytes : kMergeBytes;
 };
 
-template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+// DENSE: key slot j is key j (the auxiliary keys), no index list.
+template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   using Cfg = AttnCfg<D, QT, KVT, MQK, MPV>;
   constexpr int Q4 = Cfg::kQuarter;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   kvl = kvl < 0 ? 0 : (kvl > p.L_cap ? p.L_cap : kvl);
   const int pos = kvl - p.S + s;
   const int live = min(kvl - p.aux_tokens, pos + 1);   // valid key indices are [0, live)
-  const int32_t* idx_row = p.dense ? nullptr : p.indices + (size_t)row * p.k;
+  const int32_t* idx_row = DENSE ? nullptr : p.indices + (size_t)row * p.k;
   const int k0 = split * p.kps;
   const int k1 = min(p.k, k0 + p.kps);
 
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   int next_a = -1, next_b = -1;
   {
     const int ja = k0 + kTile * wave + c16, jb = ja + 16;
-    if (ja < k1) next_a = p.dense ? ja : idx_row[ja];
-    if (jb < k1) next_b = p.dense ? jb : idx_row[jb];
+    if (ja < k1) next_a = DENSE ? ja : idx_row[ja];
+    if (jb < k1) next_b = DENSE ? jb : idx_row[jb];
   }
   const int R = p.ratio;
   const bool head_ok = c16 < R;
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     const int ia = next_a, ib = next_b;
     {
       const int ja = t0 + kTile * kAttnWaves + c16, jb = ja + 16;
-      next_a = ja < k1 ? (p.dense ? ja : idx_row[ja]) : -1;
-      next_b = jb < k1 ? (p.dense ? jb : idx_row[jb]) : -1;
+      next_a = ja < k1 ? (DENSE ? ja : idx_row[ja]) : -1;
+      next_b = jb < k1 ? (DENSE ? jb : idx_row[jb]) : -1;
     }
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
@@ -487,17 +487,18 @@ AttnParams base_params(const AttnLaunch& a) {
   p.S = a.S; p.H_q = a.H_q; p.H_kv = a.H_kv; p.L_cap = a.L_cap; p.k = a.k;
   p.ratio = a.H_q / a.H_kv; p.out_dtype = a.out_dtype;
   p.nsplit = a.nsplit; p.kps = a.keys_per_split; p.scale = a.scale;
-  p.aux_tokens = a.aux_len; p.kvl_const = -1; p.dense = 0;
+  p.aux_tokens = a.aux_len; p.kvl_const = -1;
   p.write_partial = a.nsplit > 1 || a.aux_len > 0;
   p.part_stride = a.nsplit + (a.aux_len > 0 ? 1 : 0);
   p.part_offset = 0;
   return p;
 }
 
-template <int D, typename QT, typename KVT, typename MQK, typename MPV>
+template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE = false>
 void launch_kernel(const AttnParams& p, int nsplit, int H_kv, int rows, hipStream_t st) {
   dim3 grid(nsplit, H_kv, rows);
-  hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV>), grid, dim3(kAttnThreads), 0, st, p);
+  hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV, DENSE>), grid, dim3(kAttnThreads), 0, st,
+                     p);
 }
 
 // Main launch over the selected cache keys.
@@ -528,19 +529,19 @@ void launch_aux(const AttnLaunch& a, AttnParams p, hipStream_t st) {
   typedef _Float16 H;
   typedef __bf16 BH;
   p.k_cache = a.aux_k; p.v_cache = a.aux_v; p.k_scale = p.v_scale = nullptr;
-  p.indices = nullptr; p.dense = 1; p.k = a.aux_len; p.kps = a.aux_len;
+  p.indices = nullptr; p.k = a.aux_len; p.kps = a.aux_len;
   p.L_cap = a.aux_len; p.kvl_const = a.aux_len; p.aux_tokens = 0;
   p.write_partial = 1; p.part_offset = a.nsplit;
   const int rows = a.B * a.S;
-  if (a.q_dtype == kF32) { launch_kernel<D, float, float, float, float>(p, 1, a.H_kv, rows, st); return; }
+  if (a.q_dtype == kF32) { launch_kernel<D, float, float, float, float, true>(p, 1, a.H_kv, rows, st); return; }
   if (a.q_dtype == kBF16) {
-    if (a.aux_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH>(p, 1, a.H_kv, rows, st);
-    else if (a.aux_dtype == kF16) launch_kernel<D, BH, H, H, H>(p, 1, a.H_kv, rows, st);
-    else launch_kernel<D, BH, float, float, float>(p, 1, a.H_kv, rows, st);
+    if (a.aux_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH, true>(p, 1, a.H_kv, rows, st);
+    else if (a.aux_dtype == kF16) launch_kernel<D, BH, H, H, H, true>(p, 1, a.H_kv, rows, st);
+    else launch_kernel<D, BH, float, float, float, true>(p, 1, a.H_kv, rows, st);
   } else {
-    if (a.aux_dtype == kF16) launch_kernel<D, H, H, H, H>(p, 1, a.H_kv, rows, st);
-    else if (a.aux_dtype == kBF16) launch_kernel<D, H, BH, float, float>(p, 1, a.H_kv, rows, st);
-    else launch_kernel<D, H, float, float, float>(p, 1, a.H_kv, rows, st);
+    if (a.aux_dtype == kF16) launch_kernel<D, H, H, H, H, true>(p, 1, a.H_kv, rows, st);
+    else if (a.aux_dtype == kBF16) launch_kernel<D, H, BH, float, float, true>(p, 1, a.H_kv, rows, st);
+    else launch_kernel<D, H, float, float, float, true>(p, 1, a.H_kv, rows, st);
   }
 }
 
