@@ -50,10 +50,12 @@ constexpr int kSampleBlock = 256;      // consecutive keys per sample block
 constexpr int kSegWords = 2048;        // bitmap segment: 65536 indices
 constexpr int kSegBits = kSegWords * 32;
 constexpr int kResKeys = 32768;        // longest row the resident plan holds
-constexpr int kResCap = 4096;
+constexpr int kResCap = 4096;          // candidate list; the select's histogram follows it
 constexpr int kResSample = 2048;       // sample of a resident row (already in LDS)
 constexpr int kRowCap = 4096;
 constexpr int kMultiCap = 8192;
+static_assert(kMultiCap < 65536 && kResCap < 65536, "ordered emission packs counts in 16 bits");
+static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits the row area");
 constexpr int kMultiSample = 4096;     // sample of the threshold kernel
 constexpr int kChunkThreads = 256;
 constexpr int kChunkKeysPerThread = 8;
@@ -150,6 +152,104 @@ __device__ void radix_select(Get get, int count, uint32_t need, const Lds& s, ui
   }
   T = prefix;
   take = need;
+}
+
+// Exact selection over keys that all lie in [base, base + range]: radix
+// digits of (key - base), 12 bits wide (kRelBins bins), the first level
+// taking the top bits of `range`.  Candidate lists span a narrow key range
+// above the sample threshold, so absolute top-bit digits would pile them into
+// a few bins (LDS atomics on one address serialise) and need three levels;
+// relative digits spread them and need two levels for ranges below 2^24.
+// Returns T = the need-th largest key, take = how many keys equal to T
+// belong to the top `need`.  hist: kRelBins words of LDS.  Block-wide;
+// 1 <= need <= count.
+constexpr int kRelBits = 12;
+constexpr int kRelBins = 1 << kRelBits;
+
+template <int NT>
+__device__ void select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t* scratch,
+                               uint32_t* misc) {
+  constexpr int BPT = kRelBins / NT;
+  static_assert(BPT * NT == kRelBins, "block size must divide the bin count");
+  const int t = threadIdx.x;
+  if (t == 0) { misc[0] = 0; misc[1] = 0; }
+  uint32_t h[BPT];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = hist[kRelBins - 1 - (t * BPT + i)];
+    local += h[i];
+  }
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<NT>(local, scratch, &total);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    if (before < need && need <= before + h[i]) {
+      misc[0] = (uint32_t)(kRelBins - 1 - (t * BPT + i));
+      misc[1] = before;
+    }
+    before += h[i];
+  }
+  __syncthreads();
+}
+
+template <int NT, typename KeyOf>
+__device__ void radix_select_rel(KeyOf key_of, int count, uint32_t need, uint32_t base,
+                                 uint32_t range, uint32_t* hist, uint32_t* scratch,
+                                 uint32_t* misc, uint32_t& T, uint32_t& take) {
+  const int top = range ? 32 - __clz(range) : 0;          // bit length of the range
+  int hi = top > kRelBits ? top : kRelBits;               // bits [lo, hi) are this level's
+  uint32_t prefix = 0;                                    // digits fixed so far (bits >= hi)
+  while (true) {
+    const int lo = hi > kRelBits ? hi - kRelBits : 0;
+    for (int i = threadIdx.x; i < kRelBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < count; i += NT) {
+      const uint32_t d = key_of(i) - base;
+      if (hi >= 32 || (d >> hi) == (prefix >> hi))
+        atomicAdd(&hist[(d >> lo) & (kRelBins - 1)], 1u);
+    }
+    __syncthreads();
+    select_bin_rel<NT>(hist, need, scratch, misc);
+    need -= misc[1];
+    prefix |= misc[0] << lo;
+    __syncthreads();
+    if (lo == 0) break;
+    hi = lo;
+  }
+  T = base + prefix;
+  take = need;
+}
+
+// Ordered emission from a list sorted by index: entry i is kept iff its key
+// is above T, or equals T and fewer than `take` keys equal to T come before
+// it; its output slot is the number of kept entries before it.  One block
+// scan of the two counts packed in 16-bit halves (m < 2^16).
+template <int NT>
+__device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
+                             uint32_t take, int32_t* out, uint32_t* scratch) {
+  // m <= kMultiCap < 2^16 (multi plan), m <= kResCap (resident plan)
+  const int per = (m + NT - 1) / NT;
+  const int i0 = min(threadIdx.x * per, m), i1 = min(i0 + per, m);
+  uint32_t gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = lkey[i];
+    gt += key > T ? 1u : 0u;
+    eq += key == T ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<NT>(gt | (eq << 16), scratch, &total);
+  uint32_t g = before & 0xFFFFu, e = before >> 16;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = lkey[i];
+    if (key > T) {
+      out[g + (e < take ? e : take)] = (int32_t)lidx[i];
+      ++g;
+    } else if (key == T) {
+      if (e < take) out[g + e] = (int32_t)lidx[i];
+      ++e;
+    }
+  }
 }
 
 // Keep the `m` lowest set bits of x.
@@ -382,37 +482,42 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
       radix_select<NT>(
           [&](int i, uint32_t& key) { key = rowk[sample_pos<kResSample>(i, n)]; return true; },
           kResSample, (uint32_t)sample_rank(k, n, kResSample), s, T_lo, take, eq, 2);
-    // ---- candidates.  Each lane reads its keys 4 at a time (16-byte LDS
-    // reads), keeps a hit mask (one bit per key), reserves its slots with one atomic
-    // per wave and writes its indices; list order is irrelevant.
-    constexpr int R4 = kResKeys / 4 / NT;       // 16-byte groups per lane
-    static_assert(R4 * 4 <= 64, "hit mask holds one bit per key of a lane");
-    if (t == 0) s.misc[8] = 0;
-    __syncthreads();
+    // ---- candidates, in index order.  Lane t owns keys [32 t, 32 t + 32):
+    // eight 16-byte LDS reads, rotated by t so that any 8 consecutive lanes
+    // read distinct bank groups; one block scan of the hit counts ranks
+    // every candidate.  The largest key - T_lo sizes the select's digits.
+    constexpr int KPL = kResKeys / NT;          // keys per lane
+    static_assert(KPL == 32, "hit mask holds one bit per key of a lane");
+    if (t == 0) s.misc[11] = 0;                 // ordered by the scan's barrier
     const uint4* row4 = reinterpret_cast<const uint4*>(rowk);
-    uint64_t mask = 0;
+    uint32_t mask = 0, span = 0;
 #pragma unroll
-    for (int i = 0; i < R4; ++i) {
-      const int g = i * NT + t;                 // keys 4g .. 4g+3
-      if (4 * g < n) {
-        const uint4 q = row4[g];
-        mask |= (uint64_t)(q.x >= T_lo && 4 * g + 0 < n) << (4 * i + 0);
-        mask |= (uint64_t)(q.y >= T_lo && 4 * g + 1 < n) << (4 * i + 1);
-        mask |= (uint64_t)(q.z >= T_lo && 4 * g + 2 < n) << (4 * i + 2);
-        mask |= (uint64_t)(q.w >= T_lo && 4 * g + 3 < n) << (4 * i + 3);
+    for (int i = 0; i < KPL / 4; ++i) {
+      const int g = (i + t) & (KPL / 4 - 1);
+      const int j = KPL * t + 4 * g;
+      const uint4 q = row4[(KPL / 4) * t + g];
+      const uint32_t kq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool hit = j + e < n && kq[e] >= T_lo;
+        mask |= (uint32_t)hit << (4 * g + e);
+        if (hit) span = max(span, kq[e] - T_lo);
       }
     }
-    uint32_t slot = wave_reserve((uint32_t)__popcll(mask), &s.misc[8]);
-    for (uint64_t mm = mask; mm; mm &= mm - 1) {
-      const int b = __ffsll((unsigned long long)mm) - 1;
-      if (slot < (uint32_t)kResCap) lidx[slot] = (uint32_t)(4 * ((b >> 2) * NT + t) + (b & 3));
+    uint32_t m_total;
+    uint32_t slot = block_exclusive_scan<NT>((uint32_t)__popc(mask), s.scratch, &m_total);
+    span = wave_max_u32(span);
+    if (lane_id() == 0) atomicMax(&s.misc[11], span);
+    for (uint32_t mm = mask; mm; mm &= mm - 1) {
+      if (slot < (uint32_t)kResCap) lidx[slot] = (uint32_t)(KPL * t + __ffs(mm) - 1);
       ++slot;
     }
     __syncthreads();
-    const int m = (int)s.misc[8];
+    const int m = (int)m_total;
     if (m >= k && m <= kResCap) {
       // The row is no longer needed beyond the candidates' keys: gather them
-      // into a compact key array at the front of the row area.
+      // into a compact key array at the front of the row area; the
+      // select's histogram goes right after it.
       constexpr int MU = kResCap / NT;
       uint32_t kk[MU];
 #pragma unroll
@@ -427,8 +532,10 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
         if (i < m) rowk[i] = kk[u];
       }
       __syncthreads();
-      select_from_list<NT>([&](int i) { return rowk[i]; }, [&](int i) { return lidx[i]; }, m, n,
-                           k, s.hist, out, s);
+      uint32_t T, take;
+      radix_select_rel<NT>([&](int i) { return rowk[i]; }, m, (uint32_t)k, T_lo, s.misc[11],
+                           rowk + kResCap, s.scratch, s.misc, T, take);
+      emit_ordered<NT>(rowk, lidx, m, T, take, out, s.scratch);
       return;
     }
   }
@@ -716,15 +823,11 @@ __host__ inline size_t finish_lds_bytes(int chunks) {
 }
 static_assert(kMultiCap >= kSegWords, "fallback segments must fit the list area");
 
-template <int NT>
-__device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
-                             uint32_t take, int32_t* out, uint32_t* scratch);
-
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
     int k, int chunk, int chunks, MultiWs m, int32_t* __restrict__ indices) {
   constexpr int NT = kFinishThreads;
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kRelBins];        // kBins for the fallback, kRelBins for the list
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t misc[kMiscWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
@@ -741,6 +844,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   if (mode == kModeAll) { write_all<NT>(out, n, k); return; }
   const float* src = scores + (size_t)row * L_cap;
   if (mode == kModeList && st[3] == 0u) {
+    if (t == 0) misc[11] = 0;                 // candidate key span, ordered by the scan's barrier
     // chunk counts -> prefix offsets (lane t sums chunks [cpt t, cpt (t+1)))
     const int nch = (n + chunk - 1) / chunk;
     const int cpt = (nch + NT - 1) / NT;
@@ -763,58 +867,44 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       // pre[c] <= i < pre[c + 1]
       const uint2* slots = m.slots + (size_t)row * chunks * kSlotCap;
       const uint2* pool = m.pool + (size_t)row * kMultiCap;
-      for (int i = t; i < (int)total; i += NT) {
-        int lo = 0, hi = nch - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+      const uint32_t T_lo = st[0];
+      constexpr int G = kMultiCap / NT;      // entries per lane; all loads in flight first
+      uint2 e[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = g * NT + t;
+        if (i < (int)total) {
+          int lo = 0, hi = nch - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+          }
+          const uint32_t r = (uint32_t)i - pre[lo];
+          e[g] = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
         }
-        const uint32_t r = (uint32_t)i - pre[lo];
-        const uint2 e = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
-        lkey[i] = e.x;
-        lidx[i] = e.y;
       }
+      uint32_t span = 0;                     // largest key - T_lo of this lane
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = g * NT + t;
+        if (i < (int)total) {
+          lkey[i] = e[g].x;
+          lidx[i] = e[g].y;
+          span = max(span, e[g].x - T_lo);
+        }
+      }
+      span = wave_max_u32(span);
+      if (lane_id() == 0) atomicMax(&misc[11], span);
       __syncthreads();
-      uint32_t T, take, eq;
-      radix_select<NT>([&](int i, uint32_t& key) { key = lkey[i]; return true; }, (int)total,
-                       (uint32_t)k, s, T, take, eq);
+      uint32_t T, take;
+      radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
+                           misc[11], hist, scratch, misc, T, take);
       emit_ordered<NT>(lkey, lidx, (int)total, T, take, out, scratch);
       return;
     }
   }
   select_exact_row<NT>([&](int j) { return score_key(src[j]); }, n, k, dyn, dyn + kSegWords,
                        out, s);
-}
-
-// Ordered emission from a list sorted by index: entry i is kept iff its key
-// is above T, or equals T and fewer than `take` keys equal to T come before
-// it; its output slot is the number of kept entries before it.  One block
-// scan of the two counts packed in 16-bit halves (m <= kMultiCap < 2^16).
-template <int NT>
-__device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
-                             uint32_t take, int32_t* out, uint32_t* scratch) {
-  static_assert(kMultiCap < 65536, "packed counts");
-  const int per = (m + NT - 1) / NT;
-  const int i0 = min(threadIdx.x * per, m), i1 = min(i0 + per, m);
-  uint32_t gt = 0, eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = lkey[i];
-    gt += key > T ? 1u : 0u;
-    eq += key == T ? 1u : 0u;
-  }
-  uint32_t total;
-  const uint32_t before = block_exclusive_scan<NT>(gt | (eq << 16), scratch, &total);
-  uint32_t g = before & 0xFFFFu, e = before >> 16;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = lkey[i];
-    if (key > T) {
-      out[g + (e < take ? e : take)] = (int32_t)lidx[i];
-      ++g;
-    } else if (key == T) {
-      if (e < take) out[g + e] = (int32_t)lidx[i];
-      ++e;
-    }
-  }
 }
 
 template <typename K>
