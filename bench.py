@@ -46,7 +46,8 @@ def sources_digest():
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_gqa_attention_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "sparse_gqa_attention_amd", "csrc")
+    for f in sorted(sum((glob.glob(os.path.join(csrc, p)) for p in ("*.hip", "*.h", "*.cpp")), [])):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -13,14 +13,18 @@
 //    sample / n is the expected sample rank of the k-th largest key.  The
 //    bin's lower edge T_lo is at or below that key; every key >= T_lo is a
 //    candidate (about 1.2k + 4 sqrt(e) n/sample keys).
-// 2. Collection.  One pass over the row appends the candidates to a list.
+// 2. Collection.  One pass over the row lists the candidates; the resident
+//    and multi plans keep the list in index order.
 // 3. Exact selection on the list, in LDS: radix select of the k-th largest
-//    key T; when only some of the keys equal to T fit, the lowest indices
-//    win: one wave ranks up to 64 tied indices directly, more go through a
-//    radix select on the complemented index.  An entry is kept iff key > T
-//    or (key == T and index <= cut).  Exactly k entries.
-// 4. Ordered emission: the kept indices are set in an LDS bitmap one index
-//    segment at a time and written in ascending order by a block scan.
+//    key T (index-ordered lists: 12-bit digits of key - T_lo, two levels
+//    for key spans below 2^24).  When only some of the keys equal to T fit,
+//    the lowest indices win.  Exactly k entries.
+// 4. Ordered emission.  An index-ordered list is compacted by one block scan
+//    (a key equal to T is kept while fewer than `take` equal keys precede
+//    it).  The streaming plan's unordered list sets the kept indices in an
+//    LDS bitmap one index segment at a time, written in ascending order by a
+//    block scan, ties cut by a wave ranking (<= 64 tied indices) or a radix
+//    select on the complemented index.
 // When the list holds fewer than k keys, overflows, or k itself exceeds its
 // capacity, an exact fallback selects from the whole row (three radix
 // passes) and emits from selection/tie bitmaps, carrying the tie count
@@ -33,10 +37,11 @@
 //  * streaming -- many rows (prefill: 2048 rows of 131072 keys): one
 //    512-thread workgroup per row reading the row ~1.06 times.
 //  * multi     -- few rows longer than 32768 keys (decode at 256K): KA (one
-//    workgroup per row) computes T_lo and resets the row's list counter, KB
-//    (many workgroups per row) collects with one list reservation per
-//    workgroup, KC (one workgroup per row) selects and emits.  Kernel
-//    boundaries order the three.
+//    workgroup per row) computes T_lo and resets the row's pool counter, KB
+//    (many workgroups per row) lists each chunk's candidates in index order
+//    in the chunk's own slots (or a block of the row's pool), KC (one
+//    workgroup per row) gathers the chunks in order, selects and emits.
+//    Kernel boundaries order the three.
 #include "dsa_device.h"
 #include "launch.h"
 
