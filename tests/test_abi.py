@@ -63,6 +63,8 @@ def test_indexer_validation(dsa):
     assert "BF16" in dsa.dsa_last_error()
     assert call(dt=3) == _status("UNSUPPORTED")
     assert call(mx=4097) == _status("INVALID")
+    assert call(Lc=(1 << 27) + 1, mx=4096) == _status("UNSUPPORTED")   # 32-bit score offsets
+    assert "2^27" in dsa.dsa_last_error()
     assert call(B=-1) == _status("INVALID")
     assert call(q=None) == _status("INVALID")
     assert "q_idx" in dsa.dsa_last_error()

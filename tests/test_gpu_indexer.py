@@ -6,7 +6,7 @@ import torch
 import oracle
 from dsa_synth import (SPEC_DECODE_32K, TINY_DECODE, DECODE_256K, PREFILL_128K,
                        make_inputs, scaled)
-from gpu_util import dsa, first_mismatch, run_indexer, say, upload  # noqa: F401
+from gpu_util import DEV, dsa, first_mismatch, run_indexer, say, upload  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,32 @@ def test_indexer_prefill_streamed_sampled_rows(dsa, case):
             a, r = got[i, :pos + 1], ref[:pos + 1]
             assert np.array_equal(a, r), f"b={b} row {s}: {first_mismatch(a, r)}"
             assert np.all(np.isnan(got[i, kv_len[b]:])), f"b={b} row {s}: wrote past kv_len"
+
+
+def test_indexer_decode_beyond_grid_limit_streams(dsa):
+    # A decode step (S <= 8) over more keys than one-run workgroups can cover
+    # within the grid's y limit (60000 runs of 128 keys at D_idx 128) takes
+    # the streaming kernel.  Small integer inputs keep every score exact;
+    # sampled keys (first and last runs, random ones) are checked against the
+    # oracle applied to those key rows alone.
+    B, S, H, Di, L = 1, 2, 2, 128, 8_000_000
+    say(f"indexer decode beyond grid limit L={L}")
+    g = torch.Generator(device=DEV).manual_seed(21)
+    ks = torch.randint(-4, 5, (B, L, Di), generator=g, device=DEV).to(torch.bfloat16)
+    q = torch.randint(-4, 5, (B, S, H, Di), generator=g, device=DEV).to(torch.bfloat16)
+    w = torch.randint(1, 5, (B, S, H), generator=g, device=DEV).to(torch.float32)
+    kv = torch.tensor([L], dtype=torch.int32, device=DEV)
+    scores = torch.full((B, S, L), float("nan"), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_score(q, w, ks, kv, scores)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(22)
+    keys = np.unique(np.concatenate([np.arange(0, 300), np.arange(L - 300, L),
+                                     r.integers(0, L, size=4000)]))
+    sub = ks[0, torch.from_numpy(keys).to(DEV)].float().cpu().numpy()
+    for s in range(S):
+        pos = L - S + s
+        ok = keys[keys <= pos]
+        ref = oracle.indexer_scores_row(q[0, s].float().cpu().numpy(), w[0, s].cpu().numpy(),
+                                        sub[:len(ok)], len(ok) - 1)
+        got = scores[0, s, torch.from_numpy(ok).to(DEV)].double().cpu().numpy()
+        assert np.array_equal(got, ref), f"s={s}: {first_mismatch(got, ref)}"
