@@ -84,14 +84,33 @@ __device__ __forceinline__ void store_out4(void* out, size_t i, f32x4 O, float L
   }
 }
 
-// N elements of T from global memory (N * sizeof(T) a multiple of 16).
-template <typename T, int N>
-__device__ __forceinline__ void load_elems(const T* src, T (&dst)[N]) {
-  constexpr int NV = N * (int)sizeof(T) / 16;
-  uint4 tmp[NV];
+// Lane-interleaved row load.  A lane of group g4 (0..3) takes N elements of
+// a row in chunks of E: lane element j = c*E + e is row element
+// (4c + g4)*E + e.  With E elements of the KV type per 16 bytes, the four
+// groups read adjacent 16-byte pieces, so one load instruction covers 64
+// contiguous bytes of each of its 16 rows.  (A lane-contiguous quarter
+// spread every instruction over four separate pieces per row, and the
+// texture addresser was the bottleneck of the gathers.)  The dot product
+// is unchanged by the permutation as long as query and key use the same
+// one; values are written to LDS at their true positions.
+template <typename T, int E, int N>
+__device__ __forceinline__ void load_perm(const T* row, int g4, T (&dst)[N]) {
+  constexpr int CB = E * (int)sizeof(T);          // bytes per chunk: 8, 16 or 32
+  static_assert(N % E == 0 && CB % 8 == 0, "whole chunks of 8-byte multiples");
 #pragma unroll
-  for (int i = 0; i < NV; ++i) tmp[i] = ld_vec<uint4>((const char*)src + 16 * i);
-  __builtin_memcpy(dst, tmp, sizeof(dst));
+  for (int c = 0; c < N / E; ++c) {
+    const char* src = (const char*)(row + (4 * c + g4) * E);
+    if constexpr (CB == 8) {
+      const uint2 v = ld_vec<uint2>(src);
+      __builtin_memcpy(&dst[c * E], &v, 8);
+    } else {
+#pragma unroll
+      for (int b = 0; b < CB / 16; ++b) {
+        const uint4 v = ld_vec<uint4>(src + 16 * b);
+        __builtin_memcpy(&dst[c * E + b * (16 / (int)sizeof(T))], &v, 16);
+      }
+    }
+  }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -119,6 +138,11 @@ struct AttnCfg {
   static constexpr bool kF32Path = std::is_same<MQK, float>::value;
   static constexpr bool kInt8 = std::is_same<KVT, int8_t>::value;
   static constexpr int kQuarter = D / 4;             // elements of a row per lane
+  // Elements per lane chunk of a KV row (load_perm): 16 bytes of a 16/32-bit
+  // cache, so an instruction covers 64 contiguous bytes of a row (prefill
+  // attention 632 -> 492 us at 128K); the whole 32-byte quarter of an INT8
+  // row (measured faster than 16-byte chunks there).
+  static constexpr int kChunkElems = kInt8 ? kQuarter : 16 / (int)sizeof(KVT);
   static constexpr int kSteps = D / 32;              // QK K-steps (16-bit path)
   static constexpr int kDTiles = D / 16;             // O^T tiles of 16 dims
   // LDS row padding (elements).  16-bit rows are padded by 32 bytes so that
@@ -177,8 +201,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   // ---- Q^T operand: lane holds head c16, dims [Q4*g4, Q4*g4 + Q4)
   QT qraw[Q4];
   {
-    const QT* qrow = (const QT*)p.q + ((size_t)row * p.H_q + h) * D + Q4 * g4;
-    load_elems<QT, Q4>(qrow, qraw);
+    const QT* qrow = (const QT*)p.q + ((size_t)row * p.H_q + h) * D;
+    load_perm<QT, Cfg::kChunkElems, Q4>(qrow, g4, qraw);
     if (!head_ok) {
 #pragma unroll
       for (int i = 0; i < Q4; ++i) qraw[i] = cvt<QT>(0.0f);
@@ -205,15 +229,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     }
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
-    const KVT* krow_a = kbase + (size_t)(va ? ia : 0) * kv_row_stride + Q4 * g4;
-    const KVT* krow_b = kbase + (size_t)(vb ? ib : 0) * kv_row_stride + Q4 * g4;
-    const KVT* vrow_a = vbase + (size_t)(va ? ia : 0) * kv_row_stride + Q4 * g4;
-    const KVT* vrow_b = vbase + (size_t)(vb ? ib : 0) * kv_row_stride + Q4 * g4;
+    const KVT* krow_a = kbase + (size_t)(va ? ia : 0) * kv_row_stride;
+    const KVT* krow_b = kbase + (size_t)(vb ? ib : 0) * kv_row_stride;
+    const KVT* vrow_a = vbase + (size_t)(va ? ia : 0) * kv_row_stride;
+    const KVT* vrow_b = vbase + (size_t)(vb ? ib : 0) * kv_row_stride;
+    constexpr int E = Cfg::kChunkElems;
     KVT kra[Q4], krb[Q4], vra[Q4], vrb[Q4];
-    load_elems<KVT, Q4>(krow_a, kra);
-    load_elems<KVT, Q4>(krow_b, krb);
-    load_elems<KVT, Q4>(vrow_a, vra);
-    load_elems<KVT, Q4>(vrow_b, vrb);
+    load_perm<KVT, E, Q4>(krow_a, g4, kra);
+    load_perm<KVT, E, Q4>(krow_b, g4, krb);
+    load_perm<KVT, E, Q4>(vrow_a, g4, vra);
+    load_perm<KVT, E, Q4>(vrow_b, g4, vrb);
     // INT8: lane l fetches one scale of key (l % 32): k_scale for l < 32,
     // v_scale above (lane l holds that key's index as ia or ib).
     float my_scale = 0.0f;
@@ -257,14 +282,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       MPV va_c[Q4], vb_c[Q4];
 #pragma unroll
       for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
-      constexpr int NV = Q4 * (int)sizeof(MPV) / 16;
-      uint4 ta[NV], tb[NV];
-      __builtin_memcpy(ta, va_c, sizeof(ta));
-      __builtin_memcpy(tb, vb_c, sizeof(tb));
-      uint4* da = (uint4*)(vt + (size_t)c16 * Cfg::kVStride + Q4 * g4);
-      uint4* db = (uint4*)(vt + (size_t)(16 + c16) * Cfg::kVStride + Q4 * g4);
+      // chunk c of this lane goes to dims (4c + g4)*E .. +E of its key rows
+      constexpr int NV = E * (int)sizeof(MPV) / 16;   // 16-byte stores per chunk
+      static_assert(NV * 16 == E * (int)sizeof(MPV), "chunks of whole 16-byte stores");
+      MPV* ra = vt + (size_t)c16 * Cfg::kVStride + g4 * E;
+      MPV* rb = vt + (size_t)(16 + c16) * Cfg::kVStride + g4 * E;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) { da[i] = ta[i]; db[i] = tb[i]; }
+      for (int c = 0; c < Q4 / E; ++c) {
+        uint4 ta[NV], tb[NV];
+        __builtin_memcpy(ta, &va_c[c * E], sizeof(ta));
+        __builtin_memcpy(tb, &vb_c[c * E], sizeof(tb));
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          reinterpret_cast<uint4*>(ra + 4 * c * E)[i] = ta[i];
+          reinterpret_cast<uint4*>(rb + 4 * c * E)[i] = tb[i];
+        }
+      }
     }
     if constexpr (Cfg::kInt8) scl[l] = (l < 32) ? my_scale * p.scale : my_scale;
     // This wave's LDS writes must land before its reads below.
