@@ -84,22 +84,20 @@ __device__ __forceinline__ void store_out4(void* out, size_t i, f32x4 O, float L
   }
 }
 
-// Lane-interleaved row load.  A lane of group g4 (0..3) takes N elements of
-// a row in chunks of E: lane element j = c*E + e is row element
-// (4c + g4)*E + e.  With E elements of the KV type per 16 bytes, the four
-// groups read adjacent 16-byte pieces, so one load instruction covers 64
-// contiguous bytes of each of its 16 rows.  (A lane-contiguous quarter
-// spread every instruction over four separate pieces per row, and the
-// texture addresser was the bottleneck of the gathers.)  The dot product
-// is unchanged by the permutation as long as query and key use the same
-// one; values are written to LDS at their true positions.
+// Interleaved row load.  Quarter q (0..3) of a row is taken in chunks of E
+// elements: element j = c*E + e of the result is row element (4c + q)*E + e.
+// With E elements of the KV type per 16 bytes and the four quarters of a
+// row in four consecutive lanes, one load instruction covers 64 contiguous
+// bytes of each row it touches.  The QK dot product is unchanged by the
+// permutation as long as query and key use the same one; values are
+// written to LDS at their true positions.
 template <typename T, int E, int N>
-__device__ __forceinline__ void load_perm(const T* row, int g4, T (&dst)[N]) {
+__device__ __forceinline__ void load_perm(const T* row, int q, T (&dst)[N]) {
   constexpr int CB = E * (int)sizeof(T);          // bytes per chunk: 8, 16 or 32
   static_assert(N % E == 0 && CB % 8 == 0, "whole chunks of 8-byte multiples");
 #pragma unroll
   for (int c = 0; c < N / E; ++c) {
-    const char* src = (const char*)(row + (4 * c + g4) * E);
+    const char* src = (const char*)(row + (4 * c + q) * E);
     if constexpr (CB == 8) {
       const uint2 v = ld_vec<uint2>(src);
       __builtin_memcpy(&dst[c * E], &v, 8);
@@ -111,6 +109,18 @@ __device__ __forceinline__ void load_perm(const T* row, int g4, T (&dst)[N]) {
       }
     }
   }
+}
+
+// dst = src of lane `from` (per 32-bit word, through ds_bpermute).
+template <typename T, int N>
+__device__ __forceinline__ void lane_gather(const T (&src)[N], int from, T (&dst)[N]) {
+  constexpr int NW = N * (int)sizeof(T) / 4;
+  static_assert(NW * 4 == N * (int)sizeof(T), "whole 32-bit words");
+  uint32_t w[NW];
+  __builtin_memcpy(w, src, sizeof(w));
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(from * 4, (int)w[i]);
+  __builtin_memcpy(dst, w, sizeof(w));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -138,10 +148,10 @@ struct AttnCfg {
   static constexpr bool kF32Path = std::is_same<MQK, float>::value;
   static constexpr bool kInt8 = std::is_same<KVT, int8_t>::value;
   static constexpr int kQuarter = D / 4;             // elements of a row per lane
-  // Elements per lane chunk of a KV row (load_perm): 16 bytes of a 16/32-bit
-  // cache, so an instruction covers 64 contiguous bytes of a row (prefill
-  // attention 632 -> 492 us at 128K); the whole 32-byte quarter of an INT8
-  // row (measured faster than 16-byte chunks there).
+  // Loads of K/V rows: coalesced (four consecutive lanes per row) with
+  // 16-byte chunks, or, for INT8, a 32-byte quarter per lane in the MFMA
+  // layout.  Elements per chunk of a lane (load_perm).
+  static constexpr bool kCoalesced = !kInt8;
   static constexpr int kChunkElems = kInt8 ? kQuarter : 16 / (int)sizeof(KVT);
   static constexpr int kSteps = D / 32;              // QK K-steps (16-bit path)
   static constexpr int kDTiles = D / 16;             // O^T tiles of 16 dims
@@ -229,16 +239,41 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     }
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
-    const KVT* krow_a = kbase + (size_t)(va ? ia : 0) * kv_row_stride;
-    const KVT* krow_b = kbase + (size_t)(vb ? ib : 0) * kv_row_stride;
-    const KVT* vrow_a = vbase + (size_t)(va ? ia : 0) * kv_row_stride;
-    const KVT* vrow_b = vbase + (size_t)(vb ? ib : 0) * kv_row_stride;
+    // K and V rows are loaded coalesced: lane l reads row l/4 of each half
+    // tile, chunks 4c + l%4, so four consecutive lanes cover 64 contiguous
+    // bytes of one row and the texture addresser merges them (rows
+    // themselves are scattered).  K then moves into the MFMA layout -- lane
+    // c16 + 16 g4 holds chunks 4c + g4 of row c16, which load lane
+    // 4 c16 + g4 read -- by lane permutes; V goes to LDS as loaded.
+    // INT8 rows (128 bytes) keep the MFMA layout for the loads: lane
+    // c16 + 16 g4 reads the 32-byte quarter g4 of row c16 (measured faster
+    // than the coalesced form there).
+    constexpr bool kCoal = Cfg::kCoalesced;
+    const int lrow = kCoal ? l >> 2 : c16, lq = kCoal ? l & 3 : g4;
+    const int ia_l = kCoal ? __shfl(ia, lrow, kWave) : ia;
+    const int ib_l = kCoal ? __shfl(ib, lrow, kWave) : ib;
+    const bool va_l = ia_l >= 0 && ia_l < live;
+    const bool vb_l = ib_l >= 0 && ib_l < live;
+    const KVT* krow_a = kbase + (size_t)(va_l ? ia_l : 0) * kv_row_stride;
+    const KVT* krow_b = kbase + (size_t)(vb_l ? ib_l : 0) * kv_row_stride;
+    const KVT* vrow_a = vbase + (size_t)(va_l ? ia_l : 0) * kv_row_stride;
+    const KVT* vrow_b = vbase + (size_t)(vb_l ? ib_l : 0) * kv_row_stride;
     constexpr int E = Cfg::kChunkElems;
     KVT kra[Q4], krb[Q4], vra[Q4], vrb[Q4];
-    load_perm<KVT, E, Q4>(krow_a, g4, kra);
-    load_perm<KVT, E, Q4>(krow_b, g4, krb);
-    load_perm<KVT, E, Q4>(vrow_a, g4, vra);
-    load_perm<KVT, E, Q4>(vrow_b, g4, vrb);
+    if constexpr (kCoal) {
+      KVT kla[Q4], klb[Q4];
+      load_perm<KVT, E, Q4>(krow_a, lq, kla);
+      load_perm<KVT, E, Q4>(krow_b, lq, klb);
+      load_perm<KVT, E, Q4>(vrow_a, lq, vra);
+      load_perm<KVT, E, Q4>(vrow_b, lq, vrb);
+      lane_gather(kla, 4 * c16 + g4, kra);
+      lane_gather(klb, 4 * c16 + g4, krb);
+    } else {
+      load_perm<KVT, E, Q4>(krow_a, lq, kra);
+      load_perm<KVT, E, Q4>(krow_b, lq, krb);
+      load_perm<KVT, E, Q4>(vrow_a, lq, vra);
+      load_perm<KVT, E, Q4>(vrow_b, lq, vrb);
+    }
     // INT8: lane l fetches one scale of key (l % 32): k_scale for l < 32,
     // v_scale above (lane l holds that key's index as ia or ib).
     float my_scale = 0.0f;
@@ -282,11 +317,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       MPV va_c[Q4], vb_c[Q4];
 #pragma unroll
       for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
-      // chunk c of this lane goes to dims (4c + g4)*E .. +E of its key rows
+      // chunk c of this lane goes to dims (4c + lq)*E .. +E of its key rows
       constexpr int NV = E * (int)sizeof(MPV) / 16;   // 16-byte stores per chunk
       static_assert(NV * 16 == E * (int)sizeof(MPV), "chunks of whole 16-byte stores");
-      MPV* ra = vt + (size_t)c16 * Cfg::kVStride + g4 * E;
-      MPV* rb = vt + (size_t)(16 + c16) * Cfg::kVStride + g4 * E;
+      MPV* ra = vt + (size_t)lrow * Cfg::kVStride + lq * E;
+      MPV* rb = vt + (size_t)(16 + lrow) * Cfg::kVStride + lq * E;
 #pragma unroll
       for (int c = 0; c < Q4 / E; ++c) {
         uint4 ta[NV], tb[NV];
