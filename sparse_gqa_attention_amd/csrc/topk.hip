@@ -632,29 +632,40 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
     };
     int done = 0;
     if (vec4) {
+      // Hits are tested on floats: x >= f_lo <=> score_key(x) >= T_lo
+      // (score_key is order-preserving and gives -0.0 the key of +0.0;
+      // denormals are preserved in comparisons).  Only hits become keys.
+      const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
       const float4* src4 = reinterpret_cast<const float4*>(src);
       const int n4 = n / 4;
       for (int b4 = 0; b4 < n4; b4 += 4 * NT) {
-        float4 q[4];
+        float x[16];
+        uint32_t hm = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i4 = b4 + u * NT + t;
-          q[u] = i4 < n4 ? src4[i4] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          const float4 q = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          x[4 * u + 0] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
         }
-        uint32_t kk[16];
-        int jj[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int i4 = b4 + u * NT + t;
-          const bool ok = i4 < n4;
-          kk[4 * u + 0] = ok ? score_key(q[u].x) : 0u;
-          kk[4 * u + 1] = ok ? score_key(q[u].y) : 0u;
-          kk[4 * u + 2] = ok ? score_key(q[u].z) : 0u;
-          kk[4 * u + 3] = ok ? score_key(q[u].w) : 0u;
+          const bool ok = b4 + u * NT + t < n4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) jj[4 * u + e] = ok ? 4 * i4 + e : -1;
+          for (int e = 0; e < 4; ++e) hm |= (uint32_t)(ok && x[4 * u + e] >= f_lo) << (4 * u + e);
         }
-        place(kk, jj, 16);
+        if (__ballot(hm != 0u) == 0) continue;            // wave-uniform
+        uint32_t slot = wave_reserve((uint32_t)__popc(hm), &s.misc[8]);
+        if (hm) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if ((hm >> e) & 1u) {
+              if (slot < (uint32_t)CAP) {
+                lkey[slot] = score_key(x[e]);
+                lidx[slot] = (uint32_t)(4 * (b4 + (e >> 2) * NT + t) + (e & 3));
+              }
+              ++slot;
+            }
+        }
       }
       done = 4 * n4;
     }
