@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "e36ef2560a43e6f0",
-    "spec_decode_32k": {"attention": 18089692, "indexer": 5431032, "topk": 1353810},
-    "decode_256k": {"attention": 20306782, "indexer": 42128682, "topk": 9577342},
-    "prefill_128k": {"attention": 2389469759, "indexer": 1141498288, "topk": 1156652110},
-    "int8_batched_decode_64k": {"attention": 1156943103},
+    "sources": "bebafcf70811fe7e",
+    "spec_decode_32k": {"attention": 18085988, "indexer": 5431029, "topk": 1353811},
+    "decode_256k": {"attention": 20306699, "indexer": 42130791, "topk": 9577709},
+    "prefill_128k": {"attention": 3453504084, "indexer": 1141484169, "topk": 1156219702},
+    "int8_batched_decode_64k": {"attention": 1159270403},
 }
 
 
