@@ -420,7 +420,11 @@ __device__ void select_exact_row(KeyAt key_at, int n, int k, uint32_t* sel, uint
 }
 
 // ====================================================================== resident plan
-// Dynamic LDS: row keys [kResKeys] | hist | scratch | misc | list indices [kResCap].
+// Dynamic LDS: row scores [kResKeys] (later the candidates' keys and the
+// select's histogram) | hist | scratch | misc | list indices [kResCap].
+// The row stays in LDS as FP32: hits are tested on floats and only the
+// sample and the candidates become keys, which keeps the per-key work of
+// the one-workgroup row small.
 constexpr int kResThreads = 1024;
 constexpr size_t kResLds = (size_t)(kResKeys + kBins + 32 + kMiscWords + kResCap) * 4;
 
@@ -429,6 +433,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
     int k, int vec4, int32_t* __restrict__ indices) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  float* rowf = reinterpret_cast<float*>(lds);
   uint32_t* rowk = lds;
   Lds s{lds + kResKeys, lds + kResKeys + kBins, lds + kResKeys + kBins + 32};
   uint32_t* lidx = s.misc + kMiscWords;
@@ -443,6 +448,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     constexpr int U = kResKeys / 4 / NT;
     const int n4 = (n + 3) / 4;                 // 4*n4 <= L_cap since L_cap % 4 == 0
     const float4* src4 = reinterpret_cast<const float4*>(src);
+    float4* row4 = reinterpret_cast<float4*>(rowf);
     float4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -452,12 +458,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i4 = u * NT + t;
-      if (i4 < n4) {
-        rowk[4 * i4 + 0] = score_key(v[u].x);
-        rowk[4 * i4 + 1] = score_key(v[u].y);
-        rowk[4 * i4 + 2] = score_key(v[u].z);
-        rowk[4 * i4 + 3] = score_key(v[u].w);
-      }
+      if (i4 < n4) row4[i4] = v[u];
     }
   } else {
     constexpr int U = 8;
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = b0 + u * NT + t;
-        if (j < n) rowk[j] = score_key(v[u]);
+        if (j < n) rowf[j] = v[u];
       }
     }
   }
@@ -481,38 +482,46 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     // ---- threshold from the sample (the row itself when short)
     uint32_t T_lo, take, eq;
     if (n <= kResSample)
-      radix_select<NT>([&](int i, uint32_t& key) { key = rowk[i]; return true; }, n,
+      radix_select<NT>([&](int i, uint32_t& key) { key = score_key(rowf[i]); return true; }, n,
                        (uint32_t)k, s, T_lo, take, eq, 2);
     else
       radix_select<NT>(
-          [&](int i, uint32_t& key) { key = rowk[sample_pos<kResSample>(i, n)]; return true; },
+          [&](int i, uint32_t& key) {
+            key = score_key(rowf[sample_pos<kResSample>(i, n)]);
+            return true;
+          },
           kResSample, (uint32_t)sample_rank(k, n, kResSample), s, T_lo, take, eq, 2);
-    // ---- candidates, in index order.  Lane t owns keys [32 t, 32 t + 32):
-    // eight 16-byte LDS reads, rotated by t so that any 8 consecutive lanes
-    // read distinct bank groups; one block scan of the hit counts ranks
-    // every candidate.  The largest key - T_lo sizes the select's digits.
+    // ---- candidates, in index order.  Lane t owns keys [32 t, 32 t + 32)
+    // and tests them on floats: x >= f_lo <=> score_key(x) >= T_lo
+    // (score_key is order-preserving and gives -0.0 the key of +0.0;
+    // denormals are preserved in comparisons).  A threshold inside the -inf
+    // bin has a NaN pattern and no hits; the exact fallback then runs.
+    // Eight 16-byte LDS reads, rotated by t so that any 8 consecutive lanes
+    // read distinct bank groups: read i covers the lane's chunk
+    // g = (i + t) % 8.  Hit bits are shifted in from the last read to the
+    // first (bit 4 i + e: element e of read i), and one rotation by
+    // 4 (t % 8) moves them to bit 4 g + e, the key's offset in the lane's
+    // range.  One block scan of the hit counts ranks every candidate.
+    const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
     constexpr int KPL = kResKeys / NT;          // keys per lane
     static_assert(KPL == 32, "hit mask holds one bit per key of a lane");
     if (t == 0) s.misc[11] = 0;                 // ordered by the scan's barrier
-    const uint4* row4 = reinterpret_cast<const uint4*>(rowk);
-    uint32_t mask = 0, span = 0;
+    const float4* row4 = reinterpret_cast<const float4*>(rowf);
+    uint32_t mask = 0;
 #pragma unroll
-    for (int i = 0; i < KPL / 4; ++i) {
-      const int g = (i + t) & (KPL / 4 - 1);
-      const int j = KPL * t + 4 * g;
-      const uint4 q = row4[(KPL / 4) * t + g];
-      const uint32_t kq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool hit = j + e < n && kq[e] >= T_lo;
-        mask |= (uint32_t)hit << (4 * g + e);
-        if (hit) span = max(span, kq[e] - T_lo);
-      }
+    for (int i = KPL / 4 - 1; i >= 0; --i) {
+      const float4 q = row4[(KPL / 4) * t + ((i + t) & (KPL / 4 - 1))];
+      mask = (mask << 1) | (q.w >= f_lo ? 1u : 0u);
+      mask = (mask << 1) | (q.z >= f_lo ? 1u : 0u);
+      mask = (mask << 1) | (q.y >= f_lo ? 1u : 0u);
+      mask = (mask << 1) | (q.x >= f_lo ? 1u : 0u);
     }
+    const uint32_t rot = 4u * (uint32_t)(t & (KPL / 4 - 1));
+    mask = (mask << rot) | (mask >> ((32u - rot) & 31u));
+    const int nv = n - KPL * t;                 // keys of this lane inside the row
+    mask &= nv >= KPL ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
     uint32_t m_total;
     uint32_t slot = block_exclusive_scan<NT>((uint32_t)__popc(mask), s.scratch, &m_total);
-    span = wave_max_u32(span);
-    if (lane_id() == 0) atomicMax(&s.misc[11], span);
     for (uint32_t mm = mask; mm; mm &= mm - 1) {
       if (slot < (uint32_t)kResCap) lidx[slot] = (uint32_t)(KPL * t + __ffs(mm) - 1);
       ++slot;
@@ -520,16 +529,21 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     __syncthreads();
     const int m = (int)m_total;
     if (m >= k && m <= kResCap) {
-      // The row is no longer needed beyond the candidates' keys: gather them
-      // into a compact key array at the front of the row area; the
-      // select's histogram goes right after it.
+      // The row is no longer needed beyond the candidates: their keys go to
+      // a compact array at the front of the row area, the select's
+      // histogram right after it.  The largest key - T_lo sizes the
+      // select's digits.
       constexpr int MU = kResCap / NT;
       uint32_t kk[MU];
+      uint32_t span = 0;
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
         const int i = u * NT + t;
-        kk[u] = i < m ? rowk[lidx[i]] : 0u;
+        kk[u] = i < m ? score_key(rowf[lidx[i]]) : 0u;
+        if (i < m) span = max(span, kk[u] - T_lo);
       }
+      span = wave_max_u32(span);
+      if (lane_id() == 0) atomicMax(&s.misc[11], span);
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
@@ -547,15 +561,15 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   // ---- exact fallback over the LDS row; sel/tie bitmaps in the hist area
   // (n <= 32768 keys: 1024 words each).
   uint32_t T, take, eq;
-  radix_select<NT>([&](int i, uint32_t& key) { key = rowk[i]; return true; }, n, (uint32_t)k, s,
-                   T, take, eq);
+  radix_select<NT>([&](int i, uint32_t& key) { key = score_key(rowf[i]); return true; }, n,
+                   (uint32_t)k, s, T, take, eq);
   uint32_t* sel = s.hist;
   uint32_t* tie = s.hist + kBins / 2;
   const int lane = lane_id();
   const int span = ((n + 63) / 64) * 64;
   for (int r = t; r < span; r += NT) {
     const bool valid = r < n;
-    const uint32_t key = valid ? rowk[r] : 0u;
+    const uint32_t key = valid ? score_key(rowf[r]) : 0u;
     const uint64_t mg = __ballot(valid && key > T);
     const uint64_t me = __ballot(valid && key == T);
     const int w0 = (r - lane) >> 5;

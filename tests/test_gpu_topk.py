@@ -93,6 +93,20 @@ def test_topk_signed_zero_and_minus_inf(dsa):
         _check(dsa, sc, [L] * B, k, what="zeros/-inf")
 
 
+def test_topk_denormal_and_signed_zero_thresholds(dsa):
+    # Thresholds among denormals of either sign and signed zeros: the plans
+    # that test hits on floats must agree with the key order there (no
+    # flushing to zero, -0.0 equal to +0.0).
+    r = rng(17)
+    tiny = np.float32(2.0 ** -149)
+    for (B, S, L, k) in [(1, 8, 32768, 2048), (1, 130, 3000, 256), (1, 8, 40000, 2048)]:
+        for lo, hi in ((-40, 41), (-40, 1)):
+            codes = r.integers(lo, hi, size=(B, S, L))
+            sc = codes.astype(np.float32) * tiny
+            sc[(codes == 0) & (r.random(size=codes.shape) < 0.5)] = np.float32(-0.0)
+            _check(dsa, torch.from_numpy(sc), [L] * B, k, what=f"denormals[{lo},{hi})")
+
+
 def test_topk_prefill_128k_shape(dsa):
     sc = indexer_like_scores(rng(13), (1, 2048, 131072))
     _check(dsa, sc, [131072], 2048, rows=[(0, s) for s in (0, 1, 500, 1023, 1024, 2047)],
