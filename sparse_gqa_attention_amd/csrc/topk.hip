@@ -419,6 +419,59 @@ __device__ void select_exact_row(KeyAt key_at, int n, int k, uint32_t* sel, uint
   }
 }
 
+// Variants of radix_select (two levels) and radix_select_rel for callers
+// that zeroed one histogram per level beforehand and give each level its
+// own result words: three barriers per level instead of five.
+//
+// Lower bound of the need-th largest key: the 22-bit bin edge (low 10 bits
+// zero) after levels on bits [31:21] and [20:10].  h0, h1: kBins zeroed
+// words each; misc[0..3] receive the levels' results.
+template <int NT, typename Get>
+__device__ void radix_lower_bound_pre(Get get, int count, uint32_t need, uint32_t* h0,
+                                      uint32_t* h1, uint32_t* scratch, uint32_t* misc,
+                                      uint32_t& T_lo) {
+  for (int i = threadIdx.x; i < count; i += NT) atomicAdd(&h0[get(i) >> 21], 1u);
+  __syncthreads();
+  select_bin<NT>(h0, need, scratch, misc);
+  const uint32_t b0 = misc[0];
+  need -= misc[1];
+  for (int i = threadIdx.x; i < count; i += NT) {
+    const uint32_t key = get(i);
+    if ((key >> 21) == b0) atomicAdd(&h1[(key >> 10) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  select_bin<NT>(h1, need, scratch, misc + 2);
+  T_lo = (b0 << 21) | (misc[2] << 10);
+}
+
+// radix_select_rel over up to three zeroed histograms (hists + lvl *
+// kRelBins); misc[2 lvl], misc[2 lvl + 1] receive level lvl's results.
+template <int NT, typename KeyOf>
+__device__ void radix_select_rel_pre(KeyOf key_of, int count, uint32_t need, uint32_t base,
+                                     uint32_t range, uint32_t* hists, uint32_t* scratch,
+                                     uint32_t* misc, uint32_t& T, uint32_t& take) {
+  const int top = range ? 32 - __clz(range) : 0;
+  int hi = top > kRelBits ? top : kRelBits;
+  uint32_t prefix = 0;
+  for (int lvl = 0;; ++lvl) {                             // at most 3 levels (hi <= 32)
+    const int lo = hi > kRelBits ? hi - kRelBits : 0;
+    uint32_t* hist = hists + lvl * kRelBins;
+    for (int i = threadIdx.x; i < count; i += NT) {
+      const uint32_t d = key_of(i) - base;
+      if (hi >= 32 || (d >> hi) == (prefix >> hi))
+        atomicAdd(&hist[(d >> lo) & (kRelBins - 1)], 1u);
+    }
+    __syncthreads();
+    select_bin_rel<NT>(hist, need, scratch, misc + 2 * lvl);
+    need -= misc[2 * lvl + 1];
+    prefix |= misc[2 * lvl] << lo;
+    if (lo == 0) break;
+    hi = lo;
+  }
+  T = base + prefix;
+  take = need;
+}
+
 // ====================================================================== resident plan
 // Dynamic LDS: row scores [kResKeys] (later the candidates' keys and the
 // select's histogram) | hist | scratch | misc | list indices [kResCap].
@@ -476,21 +529,22 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
       }
     }
   }
+  // The sample threshold's two histograms: hist, and the list area, which
+  // is free until the candidates are listed.
+  uint32_t* h1 = lidx;
+  for (int i = t; i < kBins; i += NT) { s.hist[i] = 0; h1[i] = 0; }
   __syncthreads();
 
   if (k <= kResCap) {
     // ---- threshold from the sample (the row itself when short)
-    uint32_t T_lo, take, eq;
+    uint32_t T_lo;
     if (n <= kResSample)
-      radix_select<NT>([&](int i, uint32_t& key) { key = score_key(rowf[i]); return true; }, n,
-                       (uint32_t)k, s, T_lo, take, eq, 2);
+      radix_lower_bound_pre<NT>([&](int i) { return score_key(rowf[i]); }, n, (uint32_t)k,
+                                s.hist, h1, s.scratch, s.misc, T_lo);
     else
-      radix_select<NT>(
-          [&](int i, uint32_t& key) {
-            key = score_key(rowf[sample_pos<kResSample>(i, n)]);
-            return true;
-          },
-          kResSample, (uint32_t)sample_rank(k, n, kResSample), s, T_lo, take, eq, 2);
+      radix_lower_bound_pre<NT>(
+          [&](int i) { return score_key(rowf[sample_pos<kResSample>(i, n)]); }, kResSample,
+          (uint32_t)sample_rank(k, n, kResSample), s.hist, h1, s.scratch, s.misc, T_lo);
     // ---- candidates, in index order.  Lane t owns keys [32 t, 32 t + 32)
     // and tests them on floats: x >= f_lo <=> score_key(x) >= T_lo
     // (score_key is order-preserving and gives -0.0 the key of +0.0;
@@ -522,12 +576,11 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     mask &= nv >= KPL ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
     uint32_t m_total;
     uint32_t slot = block_exclusive_scan<NT>((uint32_t)__popc(mask), s.scratch, &m_total);
-    for (uint32_t mm = mask; mm; mm &= mm - 1) {
-      if (slot < (uint32_t)kResCap) lidx[slot] = (uint32_t)(KPL * t + __ffs(mm) - 1);
-      ++slot;
+    const int m = (int)m_total;
+    if (m >= k && m <= kResCap) {               // block-uniform; else the list is not used
+      for (uint32_t mm = mask; mm; mm &= mm - 1) lidx[slot++] = (uint32_t)(KPL * t + __ffs(mm) - 1);
     }
     __syncthreads();
-    const int m = (int)m_total;
     if (m >= k && m <= kResCap) {
       // The row is no longer needed beyond the candidates: their keys go to
       // a compact array at the front of the row area, the select's
@@ -542,18 +595,24 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
         kk[u] = i < m ? score_key(rowf[lidx[i]]) : 0u;
         if (i < m) span = max(span, kk[u] - T_lo);
       }
-      span = wave_max_u32(span);
-      if (lane_id() == 0) atomicMax(&s.misc[11], span);
+      span = wave_inclusive_max_u32(span);
+      if (lane_id() == kWave - 1) atomicMax(&s.misc[11], span);
       __syncthreads();
+      // keys to the front of the row area, the select's three level
+      // histograms zeroed right after them
+      uint32_t* hists = rowk + kResCap;
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
         const int i = u * NT + t;
         if (i < m) rowk[i] = kk[u];
       }
+      static_assert(kResCap + 3 * kRelBins <= kResKeys, "select histograms fit the row area");
+      uint4* h4 = reinterpret_cast<uint4*>(hists);
+      for (int i = t; i < 3 * kRelBins / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
       uint32_t T, take;
-      radix_select_rel<NT>([&](int i) { return rowk[i]; }, m, (uint32_t)k, T_lo, s.misc[11],
-                           rowk + kResCap, s.scratch, s.misc, T, take);
+      radix_select_rel_pre<NT>([&](int i) { return rowk[i]; }, m, (uint32_t)k, T_lo, s.misc[11],
+                               hists, s.scratch, s.misc + 4, T, take);
       emit_ordered<NT>(rowk, lidx, m, T, take, out, s.scratch);
       return;
     }
@@ -923,8 +982,8 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
           span = max(span, e[g].x - T_lo);
         }
       }
-      span = wave_max_u32(span);
-      if (lane_id() == 0) atomicMax(&misc[11], span);
+      span = wave_inclusive_max_u32(span);
+      if (lane_id() == kWave - 1) atomicMax(&misc[11], span);
       __syncthreads();
       uint32_t T, take;
       radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
