@@ -807,11 +807,10 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
     int k, MultiWs m) {
   constexpr int NT = kStateThreads;
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t h0[kBins], h1[kBins];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t misc[kMiscWords];
+  __shared__ uint32_t misc[4];
   __shared__ uint32_t sample[kMultiSample];
-  Lds s{hist, scratch, misc};
   const int row = blockIdx.x, t = threadIdx.x;
   const int n = row_count(kv_len, row, S, L_cap);
   uint32_t* st = m.state + row * 4;
@@ -827,16 +826,16 @@ __global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
         const int i = u * NT + t;
         v[u] = i < cnt ? src[n <= kMultiSample ? i : sample_pos<kMultiSample>(i, n)] : 0.0f;
       }
+      for (int i = t; i < kBins; i += NT) { h0[i] = 0u; h1[i] = 0u; }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = u * NT + t;
         if (i < cnt) sample[i] = score_key(v[u]);
       }
       __syncthreads();
-      uint32_t take, eq;
-      radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
-                       (uint32_t)(n <= kMultiSample ? k : sample_rank(k, n, kMultiSample)), s,
-                       T_lo, take, eq, 2);
+      radix_lower_bound_pre<NT>([&](int i) { return sample[i]; }, cnt,
+                                (uint32_t)(n <= kMultiSample ? k : sample_rank(k, n, kMultiSample)),
+                                h0, h1, scratch, misc, T_lo);
       mode = kModeList;
     } else {
       mode = kModeExact;
