@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "bebafcf70811fe7e",
-    "spec_decode_32k": {"attention": 18085988, "indexer": 5431029, "topk": 1353811},
-    "decode_256k": {"attention": 20306699, "indexer": 42130791, "topk": 9577709},
-    "prefill_128k": {"attention": 3453504084, "indexer": 1141484169, "topk": 1156219702},
-    "int8_batched_decode_64k": {"attention": 1159270403},
+    "sources": "393ec125b40ae98e",
+    "spec_decode_32k": {"attention": 18086035, "indexer": 5431034, "topk": 1300445},
+    "decode_256k": {"attention": 20306295, "indexer": 42129906, "topk": 9551915},
+    "prefill_128k": {"attention": 3454297109, "indexer": 1141516368, "topk": 1156552012},
+    "int8_batched_decode_64k": {"attention": 1158820773},
 }
 
 

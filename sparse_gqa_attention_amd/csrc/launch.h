@@ -33,7 +33,7 @@ void launch_indexer(const IndexerLaunch& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
 struct TopkPlan {
-  int kind;            // resident / streaming (512 or 1024 threads) / multi
+  int kind;            // streaming / resident / multi
   int rows;            // B*S
   int chunk;           // keys per chunk workgroup (multi)
   int chunks;          // chunk workgroups per row (multi)

@@ -35,7 +35,9 @@
 //    1024-thread workgroup per row loads the row once into LDS (128 KB of
 //    keys) and does everything there.
 //  * streaming -- many rows (prefill: 2048 rows of 131072 keys): one
-//    512-thread workgroup per row reading the row ~1.06 times.
+//    1024-thread workgroup per row reading the row ~1.06 times (two
+//    workgroups per CU: at most 64 VGPRs, four 16-byte loads per lane in
+//    flight).
 //  * multi     -- few rows longer than 32768 keys (decode at 256K): KA (one
 //    workgroup per row) computes T_lo and resets the row's pool counter, KB
 //    (many workgroups per row) lists each chunk's candidates in index order
@@ -64,8 +66,10 @@ static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits t
 constexpr int kMultiSample = 4096;     // sample of the threshold kernel
 constexpr int kChunkThreads = 256;
 constexpr int kChunkKeysPerThread = 8;
+constexpr int kStreamLoads = 4;        // 16-byte loads per lane in flight (streaming plan)
+static_assert(4 * kStreamLoads <= 32, "one hit bit per key of a lane's step");
 
-enum PlanKind { kPlanStream512 = 0, kPlanResident = 1, kPlanMulti = 2 };
+enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanMulti = 2 };
 
 // Radix levels: key bits [31:21], [20:10], [9:0].
 __device__ __forceinline__ int lvl_shift(int lvl) { return lvl == 0 ? 21 : (lvl == 1 ? 10 : 0); }
@@ -681,12 +685,13 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
       const int i = u * NT + t;
       if (i < cnt) sample[i] = score_key(v[u]);
     }
+    for (int i = t; i < kBins; i += NT) { s.hist[i] = 0u; bm[i] = 0u; }   // bm: free until emission
     __syncthreads();
-    uint32_t T_lo, take, eq;
-    radix_select<NT>([&](int i, uint32_t& key) { key = sample[i]; return true; }, cnt,
-                     (uint32_t)(n <= kSample ? k : sample_rank(k, n, kSample)), s, T_lo, take,
-                     eq, 2);
-    // ---- one pass over the row: 16-byte loads, 4 per lane in flight
+    uint32_t T_lo;
+    radix_lower_bound_pre<NT>([&](int i) { return sample[i]; }, cnt,
+                              (uint32_t)(n <= kSample ? k : sample_rank(k, n, kSample)), s.hist,
+                              bm, s.scratch, s.misc, T_lo);
+    // ---- one pass over the row: 16-byte loads, kStreamLoads per lane in flight
     uint32_t* lkey = regionA;
     uint32_t* lidx = regionA + CAP;
     if (t == 0) s.misc[8] = 0;
@@ -711,17 +716,18 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
       const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
       const float4* src4 = reinterpret_cast<const float4*>(src);
       const int n4 = n / 4;
-      for (int b4 = 0; b4 < n4; b4 += 4 * NT) {
-        float x[16];
+      constexpr int V = kStreamLoads;
+      for (int b4 = 0; b4 < n4; b4 += V * NT) {
+        float x[4 * V];
         uint32_t hm = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < V; ++u) {
           const int i4 = b4 + u * NT + t;
           const float4 q = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
           x[4 * u + 0] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < V; ++u) {
           const bool ok = b4 + u * NT + t < n4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hm |= (uint32_t)(ok && x[4 * u + e] >= f_lo) << (4 * u + e);
@@ -730,7 +736,7 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
         uint32_t slot = wave_reserve((uint32_t)__popc(hm), &s.misc[8]);
         if (hm) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
+          for (int e = 0; e < 4 * V; ++e)
             if ((hm >> e) & 1u) {
               if (slot < (uint32_t)CAP) {
                 lkey[slot] = score_key(x[e]);
@@ -1001,7 +1007,8 @@ void opt_in_lds(K kernel, size_t bytes) {
                             (int)bytes);
 }
 
-using Stream512 = StreamCfg<512, kRowCap>;
+constexpr int kStreamThreads = 1024;
+using StreamPlan = StreamCfg<kStreamThreads, kRowCap>;
 
 }  // namespace
 
@@ -1011,7 +1018,7 @@ TopkPlan plan_topk(int B, int S, int L_cap, int k) {
   p.rows = B * S;
   const long long rows = p.rows;
   if (rows >= 128) {
-    p.kind = kPlanStream512;
+    p.kind = kPlanStream;
   } else if (L_cap <= kResKeys) {
     p.kind = kPlanResident;
   } else {
@@ -1036,15 +1043,16 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
     opt_in_lds(topk_resident_kernel<kResThreads>, kResLds);
-    opt_in_lds(topk_stream_kernel<512, kRowCap>, Stream512::kLds);
+    opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap>, StreamPlan::kLds);
     opt_in_lds(topk_finish_kernel, finish_lds_bytes(kMaxChunks));
     lds_opt_in = true;
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
   switch (p.kind) {
-    case kPlanStream512:
-      hipLaunchKernelGGL((topk_stream_kernel<512, kRowCap>), dim3(p.rows), dim3(512),
-                         Stream512::kLds, st, scores, kv_len, S, L_cap, k, vec4, indices);
+    case kPlanStream:
+      hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap>), dim3(p.rows),
+                         dim3(kStreamThreads), StreamPlan::kLds, st, scores, kv_len, S, L_cap, k,
+                         vec4, indices);
       return;
     case kPlanResident:
       hipLaunchKernelGGL((topk_resident_kernel<kResThreads>), dim3(p.rows), dim3(kResThreads), kResLds, st,
