@@ -784,6 +784,7 @@ constexpr uint32_t kNoPool = 0xFFFFFFFFu;
 // Chunks of 256..2048 keys: at most 2^24 / 2048 per row (a chunk below 2048
 // keys only when the row has at most 1024 of them).
 constexpr int kMaxChunks = 8192;
+constexpr int kSpecSlots = 16384;      // slots per row the finish kernel loads up front
 
 struct MultiWs {
   uint32_t* state;   // [rows][4]: T_lo, mode, pool count, pool overflow flag
@@ -931,6 +932,20 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   uint32_t* pre = dyn + 2 * kMultiCap;          // [chunks + 1]
   uint32_t* poff = pre + chunks + 1;            // [chunks]
   const int row = blockIdx.x, t = threadIdx.x;
+  // With at most kSpecSlots slots per row, every slot is loaded first, before
+  // the state and the counts are known: slot positions are fixed, so these
+  // loads overlap the count scan (slots past a chunk's count are ignored).
+  constexpr int SG = kSpecSlots / NT;
+  const bool spec = chunks * kSlotCap <= kSpecSlots;      // grid-uniform
+  const uint2* slots = m.slots + (size_t)row * chunks * kSlotCap;
+  uint2 se[SG];
+  if (spec) {
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      const int i = g * NT + t;
+      if (i < chunks * kSlotCap) se[g] = slots[i];
+    }
+  }
   const int n = row_count(kv_len, row, S, L_cap);
   int32_t* out = indices + (size_t)row * k;
   const uint32_t* st = m.state + row * 4;
@@ -938,7 +953,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
   if (mode == kModeAll) { write_all<NT>(out, n, k); return; }
   const float* src = scores + (size_t)row * L_cap;
   if (mode == kModeList && st[3] == 0u) {
-    if (t == 0) misc[11] = 0;                 // candidate key span, ordered by the scan's barrier
+    // candidate key span; whether any chunk listed into the pool (both
+    // ordered by the scan's barrier)
+    if (t == 0) { misc[11] = 0; misc[12] = 0; }
     // chunk counts -> prefix offsets (lane t sums chunks [cpt t, cpt (t+1)))
     const int nch = (n + chunk - 1) / chunk;
     const int cpt = (nch + NT - 1) / NT;
@@ -953,38 +970,58 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       pre[c] = run;
       poff[c] = mc.y;
       run += mc.x;
+      if (mc.y != kNoPool) misc[12] = 1u;
     }
     if (t == 0) pre[nch] = total;
     __syncthreads();
     if (total >= (uint32_t)k && total <= (uint32_t)kMultiCap) {
-      // gather in index order: entry i belongs to the chunk c with
-      // pre[c] <= i < pre[c + 1]
-      const uint2* slots = m.slots + (size_t)row * chunks * kSlotCap;
       const uint2* pool = m.pool + (size_t)row * kMultiCap;
       const uint32_t T_lo = st[0];
-      constexpr int G = kMultiCap / NT;      // entries per lane; all loads in flight first
-      uint2 e[G];
+      uint32_t span = 0;                     // largest key - T_lo of this lane
+      if (spec) {
+        // slot r of chunk c goes to list entry pre[c] + r
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int i = g * NT + t;
-        if (i < (int)total) {
-          int lo = 0, hi = nch - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+        for (int g = 0; g < SG; ++g) {
+          const int i = g * NT + t;
+          const int c = i / kSlotCap, r = i % kSlotCap;
+          if (c < nch && poff[c] == kNoPool && (uint32_t)r < pre[c + 1] - pre[c]) {
+            lkey[pre[c] + r] = se[g].x;
+            lidx[pre[c] + r] = se[g].y;
+            span = max(span, se[g].x - T_lo);
           }
-          const uint32_t r = (uint32_t)i - pre[lo];
-          e[g] = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
         }
       }
-      uint32_t span = 0;                     // largest key - T_lo of this lane
+      if (!spec || misc[12] != 0u) {
+        // gather in index order: entry i belongs to the chunk c with
+        // pre[c] <= i < pre[c + 1] (only pooled chunks' entries when the
+        // slots are already placed)
+        constexpr int G = kMultiCap / NT;    // entries per lane; all loads in flight first
+        uint2 e[G];
+        uint32_t want = 0;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int i = g * NT + t;
-        if (i < (int)total) {
-          lkey[i] = e[g].x;
-          lidx[i] = e[g].y;
-          span = max(span, e[g].x - T_lo);
+        for (int g = 0; g < G; ++g) {
+          const int i = g * NT + t;
+          if (i < (int)total) {
+            int lo = 0, hi = nch - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+            }
+            const uint32_t r = (uint32_t)i - pre[lo];
+            if (!spec || poff[lo] != kNoPool) {
+              e[g] = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
+              want |= 1u << g;
+            }
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int i = g * NT + t;
+          if (want >> g & 1u) {
+            lkey[i] = e[g].x;
+            lidx[i] = e[g].y;
+            span = max(span, e[g].x - T_lo);
+          }
         }
       }
       span = wave_inclusive_max_u32(span);
