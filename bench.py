@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "393ec125b40ae98e",
-    "spec_decode_32k": {"attention": 18086035, "indexer": 5431034, "topk": 1300445},
-    "decode_256k": {"attention": 20306295, "indexer": 42129906, "topk": 9551915},
-    "prefill_128k": {"attention": 3454297109, "indexer": 1141516368, "topk": 1156552012},
-    "int8_batched_decode_64k": {"attention": 1158820773},
+    "sources": "a24b4ff2535579dc",
+    "spec_decode_32k": {"attention": 18085992, "indexer": 5431067, "topk": 1304666},
+    "decode_256k": {"attention": 20302967, "indexer": 42128761, "topk": 9760508},
+    "prefill_128k": {"attention": 3453792559, "indexer": 1141506516, "topk": 1156553868},
+    "int8_batched_decode_64k": {"attention": 1158779457},
 }
 
 
