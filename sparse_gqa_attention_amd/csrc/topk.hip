@@ -495,29 +495,34 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   Lds s{lds + kResKeys, lds + kResKeys + kBins, lds + kResKeys + kBins + 32};
   uint32_t* lidx = s.misc + kMiscWords;
   const int row = blockIdx.x, t = threadIdx.x;
-  const int n = row_count(kv_len, row, S, L_cap);
-  int32_t* out = indices + (size_t)row * k;
-  if (n <= k) { write_all<NT>(out, n, k); return; }
   const float* src = scores + (size_t)row * L_cap;
+  int32_t* out = indices + (size_t)row * k;
 
-  // ---- the whole row into LDS, every load in flight before any store
+  // ---- the whole row into LDS, every load in flight before any store.
+  // With 16-byte rows the loads cover the L_cap-long row and go out before
+  // the row's length is known (no wait for kv_len).
   if (vec4) {
     constexpr int U = kResKeys / 4 / NT;
-    const int n4 = (n + 3) / 4;                 // 4*n4 <= L_cap since L_cap % 4 == 0
+    const int L4 = L_cap / 4;                   // L_cap % 4 == 0
     const float4* src4 = reinterpret_cast<const float4*>(src);
     float4* row4 = reinterpret_cast<float4*>(rowf);
     float4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i4 = u * NT + t;
-      v[u] = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = i4 < L4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const int n = row_count(kv_len, row, S, L_cap);
+    if (n <= k) { write_all<NT>(out, n, k); return; }
+    const int n4 = (n + 3) / 4;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i4 = u * NT + t;
       if (i4 < n4) row4[i4] = v[u];
     }
   } else {
+    const int n = row_count(kv_len, row, S, L_cap);
+    if (n <= k) { write_all<NT>(out, n, k); return; }
     constexpr int U = 8;
     for (int b0 = 0; b0 < n; b0 += U * NT) {
       float v[U];
@@ -533,6 +538,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
       }
     }
   }
+  const int n = row_count(kv_len, row, S, L_cap);
   // The sample threshold's two histograms: hist, and the list area, which
   // is free until the candidates are listed.
   uint32_t* h1 = lidx;

@@ -172,3 +172,19 @@ def test_topk_ties_across_chunks_keep_lowest_indices(dsa):
     got = _check(dsa, torch.from_numpy(sc), [L], k, what="ties across chunks")
     tied = np.flatnonzero(sc[0, 0, :L - S + 1] == 2.0)
     assert np.array_equal(got[0, 0], tied[:k])
+
+
+def test_topk_resident_rows_unaligned_short_and_at_capacity(dsa):
+    # Few rows of at most 32768 keys: rows whose length is not a multiple of
+    # 4 (element loads), rows short enough for the whole row to be the
+    # threshold sample, rows with k close to their length and heavy ties
+    # (candidate counts around the list capacity of 4096), and k = 1.
+    r = rng(18)
+    sc = torch.from_numpy(r.standard_normal((1, 8, 2101)).astype(np.float32))
+    _check(dsa, sc, [2101], 2000, what="resident short, L%4=1")
+    sc = torch.from_numpy(r.standard_normal((2, 8, 30001)).astype(np.float32))
+    _check(dsa, sc, [30001, 15000], 2048, what="resident ragged, L%4=1")
+    sc = integer_scores(r, (1, 4, 4097), -30, 30)
+    _check(dsa, sc, [4097], 4000, what="resident near capacity")
+    sc = torch.from_numpy(r.standard_normal((2, 8, 32768)).astype(np.float32))
+    _check(dsa, sc, [32768, 9000], 1, what="resident k=1, ragged")
