@@ -30,8 +30,10 @@
 // vector ALU work per chunk is the head-weighted sums alone.
 //
 // Decode (indexer_score_kernel): a workgroup of 4 waves x 1 pair copies one
-// run of keys into LDS, then scores it; a decode step has too few keys per
-// workgroup to stream.
+// run of keys into LDS, then scores it.  Long decode contexts (more key runs
+// than two per CU) use the streaming kernel in a decode shape instead, 4
+// waves x 1 pair streaming up to four runs: the next run's copy overlaps the
+// current run's MFMAs, and the query operands are read once per four runs.
 //
 // The XCD-aware renumbering dispatches the token blocks that share a key
 // range consecutively on one XCD and deals key ranges to the XCDs in turn,
@@ -546,6 +548,18 @@ void launch_stream(const IndexerLaunch& a, hipStream_t st) {
       a.kv_len, a.S, a.H, a.L_cap, a.keys_per_wg, a.scores);
 }
 
+// Long decode contexts: the streaming kernel with 4 waves x 1 token pair
+// (the 8 tokens of a decode step) and decode-sized runs, two workgroups per
+// CU (64 KB of LDS each).
+template <typename T, int DI>
+void launch_stream_decode(const IndexerLaunch& a, hipStream_t st) {
+  constexpr int R = 32768 / (2 * DI);
+  dim3 grid(a.tok_blocks, a.key_blocks, a.B);
+  hipLaunchKernelGGL((indexer_stream_kernel<T, DI, 1, 4, R, 2, false>), grid, dim3(4 * kWave), 0,
+                     st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
+                     a.L_cap, a.keys_per_wg, a.scores);
+}
+
 template <typename T, int DI, int PAIRS, int WAVES, int KR>
 void launch_resident(const IndexerLaunch& a, hipStream_t st) {
   dim3 grid(a.tok_blocks, a.key_blocks, a.B);
@@ -562,14 +576,17 @@ void launch_idx_d(const IndexerLaunch& a, hipStream_t st) {
   switch (a.D_idx) {
     case 32:
       if (a.prefill) launch_stream<T, 32>(a, st);
+      else if (a.stream_decode) launch_stream_decode<T, 32>(a, st);
       else launch_resident<T, 32, 1, 4, kDecodeRun<32>>(a, st);
       break;
     case 64:
       if (a.prefill) launch_stream<T, 64>(a, st);
+      else if (a.stream_decode) launch_stream_decode<T, 64>(a, st);
       else launch_resident<T, 64, 1, 4, kDecodeRun<64>>(a, st);
       break;
     default:
       if (a.prefill) launch_stream<T, 128>(a, st);
+      else if (a.stream_decode) launch_stream_decode<T, 128>(a, st);
       else launch_resident<T, 128, 1, 4, kDecodeRun<128>>(a, st);
       break;
   }
@@ -625,18 +642,29 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
     }
     a.keys_per_wg = (int)(best_rpw * a.tile);
   } else {
-    // Decode (S <= 8): 4 waves x 1 token pair, one key run per workgroup;
-    // ~512 workgroups (2 per CU: at 8 x 32K keys, 64 keys each measured
-    // 4.1 us against 4.9 us for 32), runs of whole 32-key chunks.
+    // Decode (S <= 8): 4 waves x 1 token pair.  Up to two runs per CU: one
+    // key run per workgroup, ~512 workgroups (at 8 x 32K keys, 64 keys each
+    // measured 4.1 us against 4.9 us for 32 and 5.5 us for a full run of
+    // 256), runs of whole 32-key chunks.  More runs: stream up to four runs
+    // per workgroup (at 8 x 256K keys: 10.5 us for four runs, 11.1 us for
+    // two, 12.6-13.1 us for one-run workgroups).
     a.pairs = 1;
     a.waves = 4;
     a.tile = 32768 / (2 * D_idx);
     a.tok_blocks = (S + 7) / 8;
-    const long long want = ((long long)max_kv_len * B * a.tok_blocks + 511) / 512;
-    long long kpw = ((want + 31) / 32) * 32;
-    if (kpw < 32) kpw = 32;
-    if (kpw > a.tile) kpw = a.tile;
-    a.keys_per_wg = (int)kpw;
+    const long long runs = ((long long)max_kv_len + a.tile - 1) / a.tile * B * a.tok_blocks;
+    if (runs > 2LL * kNumCUs) {
+      a.stream_decode = true;
+      long long rpw = (runs + kNumCUs - 1) / kNumCUs;
+      if (rpw > 4) rpw = 4;
+      a.keys_per_wg = (int)(rpw * a.tile);
+    } else {
+      const long long want = ((long long)max_kv_len * B * a.tok_blocks + 511) / 512;
+      long long kpw = ((want + 31) / 32) * 32;
+      if (kpw < 32) kpw = 32;
+      if (kpw > a.tile) kpw = a.tile;
+      a.keys_per_wg = (int)kpw;
+    }
   }
   // Key blocks rounded up to a multiple of 8 for the XCD renumbering; the
   // extra blocks start past max_kv_len and exit at once.

@@ -19,6 +19,7 @@ struct IndexerLaunch {
   int B, S, H, D_idx, L_cap;
   bool bf16;
   bool prefill;     // S > 8: 8-wave workgroups streaming key runs
+  bool stream_decode;  // long decode context: 4-wave workgroups streaming key runs
   int pairs;        // token pairs per wave (1 or 2)
   int waves;        // waves per workgroup
   int tile;         // keys per LDS buffer

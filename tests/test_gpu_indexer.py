@@ -50,6 +50,28 @@ def test_indexer_small_exact(dsa, case):
     _check(scores, x, S, str(case))
 
 
+# Decode shapes with more key runs than two per CU, which stream up to four
+# runs per workgroup: every D_idx, partial token blocks (S < 8), ragged
+# kv_len (one sequence of a single token) and ragged last runs.
+LONG_DECODE = [
+    (2, 3, 16, 64, 100000, [100000, 37001], "bf16"),
+    (1, 8, 4, 32, 300000, None, "bf16"),
+    (3, 1, 7, 128, 30000, [30000, 1, 17777], "f16"),
+]
+
+
+@pytest.mark.parametrize("case", LONG_DECODE, ids=lambda c: f"B{c[0]}S{c[1]}H{c[2]}D{c[3]}L{c[4]}{c[6]}")
+def test_indexer_long_decode_streams_exact(dsa, case):
+    B, S, H, Di, L, kv, dt = case
+    say(f"indexer long decode {case}")
+    w = scaled(SPEC_DECODE_32K, B=B, S=S, H_idx=H, D_idx=Di, L=L, H_q=2, H_kv=1, D=64,
+               idx_dtype=dt, seed=2000 + L)
+    x = make_inputs(w, kv_len=kv)
+    scores = run_indexer(dsa, upload(x), L)
+    torch.cuda.synchronize()
+    _check(scores, x, S, str(case))
+
+
 @pytest.mark.parametrize("wl", [TINY_DECODE, SPEC_DECODE_32K, DECODE_256K], ids=lambda w: w.name)
 def test_indexer_full_size_all_rows(dsa, wl):
     say(f"indexer full {wl.name}")
