@@ -916,27 +916,35 @@ __global__ __launch_bounds__(kChunkThreads) void topk_collect_kernel(
 }
 
 // KC: exact selection and ordered emission, one workgroup per row.
-// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | chunk prefix offsets
-// [chunks + 1] | chunk pool offsets [chunks]; the fallback's sel/tie
-// segments reuse the list area.
+// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | select histograms
+// [nh kRelBins] | chunk prefix offsets [chunks + 1] | chunk pool offsets
+// [chunks]; the fallback's sel/tie segments reuse the list area and its
+// histogram the first select histogram.  Up to kPreHistChunks chunks per row
+// there are three select histograms, zeroed while the slot loads are in
+// flight (three barriers per select level instead of five); beyond, one,
+// zeroed per level.
+constexpr int kPreHistChunks = 2048;
+__host__ __device__ inline int finish_hists(int chunks) { return chunks <= kPreHistChunks ? 3 : 1; }
 __host__ inline size_t finish_lds_bytes(int chunks) {
-  return (size_t)(2 * kMultiCap + 2 * chunks + 1) * 4;
+  return (size_t)(2 * kMultiCap + finish_hists(chunks) * kRelBins + 2 * chunks + 1) * 4;
 }
 static_assert(kMultiCap >= kSegWords, "fallback segments must fit the list area");
+static_assert(kRelBins >= kBins, "the fallback histogram fits a select histogram");
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
     int k, int chunk, int chunks, MultiWs m, int32_t* __restrict__ indices) {
   constexpr int NT = kFinishThreads;
-  __shared__ uint32_t hist[kRelBins];        // kBins for the fallback, kRelBins for the list
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t misc[kMiscWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-  Lds s{hist, scratch, misc};
   uint32_t* lkey = dyn;
   uint32_t* lidx = dyn + kMultiCap;
-  uint32_t* pre = dyn + 2 * kMultiCap;          // [chunks + 1]
+  uint32_t* hist = dyn + 2 * kMultiCap;         // [nh * kRelBins]
+  const int nh = finish_hists(chunks);          // grid-uniform
+  uint32_t* pre = hist + nh * kRelBins;         // [chunks + 1]
   uint32_t* poff = pre + chunks + 1;            // [chunks]
+  Lds s{hist, scratch, misc};
   const int row = blockIdx.x, t = threadIdx.x;
   // With at most kSpecSlots slots per row, every slot is loaded first, before
   // the state and the counts are known: slot positions are fixed, so these
@@ -951,6 +959,10 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       const int i = g * NT + t;
       if (i < chunks * kSlotCap) se[g] = slots[i];
     }
+  }
+  if (nh == 3) {                                // ordered before the select by the scan's barrier
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+    for (int i = t; i < 3 * kRelBins / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   const int n = row_count(kv_len, row, S, L_cap);
   int32_t* out = indices + (size_t)row * k;
@@ -1034,8 +1046,12 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
       if (lane_id() == kWave - 1) atomicMax(&misc[11], span);
       __syncthreads();
       uint32_t T, take;
-      radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
-                           misc[11], hist, scratch, misc, T, take);
+      if (nh == 3)
+        radix_select_rel_pre<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
+                                 misc[11], hist, scratch, misc + 4, T, take);
+      else
+        radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
+                             misc[11], hist, scratch, misc, T, take);
       emit_ordered<NT>(lkey, lidx, (int)total, T, take, out, scratch);
       return;
     }

@@ -188,3 +188,11 @@ def test_topk_resident_rows_unaligned_short_and_at_capacity(dsa):
     _check(dsa, sc, [4097], 4000, what="resident near capacity")
     sc = torch.from_numpy(r.standard_normal((2, 8, 32768)).astype(np.float32))
     _check(dsa, sc, [32768, 9000], 1, what="resident k=1, ragged")
+
+
+def test_topk_very_long_rows(dsa):
+    # Few rows of 4.5M keys: more than 2048 chunks per row, where the finish
+    # kernel keeps a single select histogram and zeroes it per level.
+    r = rng(19)
+    sc = torch.from_numpy(r.standard_normal((1, 2, 4_500_000)).astype(np.float32))
+    _check(dsa, sc, [4_500_000], 2048, what="4.5M keys")
