@@ -170,8 +170,12 @@ struct AttnCfg {
 };
 
 // DENSE: key slot j is key j (the auxiliary keys), no index list.
+// INT8 caches run three waves per SIMD (at most 168 registers): measured
+// faster there than two waves with wider prefetch.
 template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads)
+__attribute__((amdgpu_waves_per_eu(std::is_same<KVT, int8_t>::value ? 3 : 1)))
+void attn_kernel(AttnParams p) {
   using Cfg = AttnCfg<D, QT, KVT, MQK, MPV>;
   constexpr int Q4 = Cfg::kQuarter;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kLds];
@@ -228,61 +232,64 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int dt = 0; dt < Cfg::kDTiles; ++dt) o[dt] = f32x4{};
 
-  for (int t0 = k0 + kTile * wave; t0 < k1; t0 += kTile * kAttnWaves) {
-    // ---- this lane's two key rows (row c16 of each half tile); fetch the
-    // entries of the wave's next tile now, they are needed one tile later.
-    const int ia = next_a, ib = next_b;
-    {
-      const int ja = t0 + kTile * kAttnWaves + c16, jb = ja + 16;
-      next_a = ja < k1 ? (DENSE ? ja : idx_row[ja]) : -1;
-      next_b = jb < k1 ? (DENSE ? jb : idx_row[jb]) : -1;
-    }
-    const bool va = ia >= 0 && ia < live;
-    const bool vb = ib >= 0 && ib < live;
-    // K and V rows are loaded coalesced: lane l reads row l/4 of each half
-    // tile, chunks 4c + l%4, so four consecutive lanes cover 64 contiguous
-    // bytes of one row and the texture addresser merges them (rows
-    // themselves are scattered).  K then moves into the MFMA layout -- lane
-    // c16 + 16 g4 holds chunks 4c + g4 of row c16, which load lane
-    // 4 c16 + g4 read -- by lane permutes; V goes to LDS as loaded.
-    // INT8 rows (128 bytes) keep the MFMA layout for the loads: lane
-    // c16 + 16 g4 reads the 32-byte quarter g4 of row c16 (measured faster
-    // than the coalesced form there).
-    constexpr bool kCoal = Cfg::kCoalesced;
-    const int lrow = kCoal ? l >> 2 : c16, lq = kCoal ? l & 3 : g4;
-    const int ia_l = kCoal ? __shfl(ia, lrow, kWave) : ia;
-    const int ib_l = kCoal ? __shfl(ib, lrow, kWave) : ib;
-    const bool va_l = ia_l >= 0 && ia_l < live;
-    const bool vb_l = ib_l >= 0 && ib_l < live;
-    const KVT* krow_a = kbase + (size_t)(va_l ? ia_l : 0) * kv_row_stride;
-    const KVT* krow_b = kbase + (size_t)(vb_l ? ib_l : 0) * kv_row_stride;
-    const KVT* vrow_a = vbase + (size_t)(va_l ? ia_l : 0) * kv_row_stride;
-    const KVT* vrow_b = vbase + (size_t)(vb_l ? ib_l : 0) * kv_row_stride;
-    constexpr int E = Cfg::kChunkElems;
-    KVT kra[Q4], krb[Q4], vra[Q4], vrb[Q4];
-    if constexpr (kCoal) {
-      KVT kla[Q4], klb[Q4];
-      load_perm<KVT, E, Q4>(krow_a, lq, kla);
-      load_perm<KVT, E, Q4>(krow_b, lq, klb);
-      load_perm<KVT, E, Q4>(vrow_a, lq, vra);
-      load_perm<KVT, E, Q4>(vrow_b, lq, vrb);
-      lane_gather(kla, 4 * c16 + g4, kra);
-      lane_gather(klb, 4 * c16 + g4, krb);
-    } else {
-      load_perm<KVT, E, Q4>(krow_a, lq, kra);
-      load_perm<KVT, E, Q4>(krow_b, lq, krb);
-      load_perm<KVT, E, Q4>(vrow_a, lq, vra);
-      load_perm<KVT, E, Q4>(vrow_b, lq, vrb);
-    }
+  // K rows of a tile are loaded one tile ahead of their use: the K rows
+  // (and INT8 scales) of the wave's next tile are requested before the
+  // current tile is computed, and the index-list entries two tiles ahead.
+  // V rows are requested when their tile starts; they are first needed
+  // after the QK product and the softmax, which cover their latency.
+  // K and V rows are loaded coalesced: lane l reads row l/4 of each half
+  // tile, chunks 4c + l%4, so four consecutive lanes cover 64 contiguous
+  // bytes of one row and the texture addresser merges them (rows
+  // themselves are scattered).  K then moves into the MFMA layout -- lane
+  // c16 + 16 g4 holds chunks 4c + g4 of row c16, which load lane
+  // 4 c16 + g4 read -- by lane permutes; V goes to LDS as loaded.
+  // INT8 rows (128 bytes) keep the MFMA layout for the loads: lane
+  // c16 + 16 g4 reads the 32-byte quarter g4 of row c16 (measured faster
+  // than the coalesced form there).
+  constexpr bool kCoal = Cfg::kCoalesced;
+  constexpr int E = Cfg::kChunkElems;
+  const int lrow = kCoal ? l >> 2 : c16, lq = kCoal ? l & 3 : g4;
+  struct TileRegs {
+    KVT k0[Q4], k1[Q4];                   // K rows of half tiles a and b, as loaded
+    int ra, rb;                           // the rows this lane loads (-1: none)
+    float sc;                             // INT8: this lane's k or v scale
+  };
+  // Row of entry e as loaded by this lane, clamped to a valid row.
+  auto load_row = [&](int e) { return kCoal ? __shfl(e, lrow, kWave) : e; };
+  // Request the K rows of the tile whose entries (this lane's rows c16 and
+  // c16 + 16) are ia, ib.
+  auto issue = [&](int ia, int ib, TileRegs& r) {
+    const int ia_l = load_row(ia), ib_l = load_row(ib);
+    r.ra = ia_l >= 0 && ia_l < live ? ia_l : 0;
+    r.rb = ib_l >= 0 && ib_l < live ? ib_l : 0;
+    load_perm<KVT, E, Q4>(kbase + (size_t)r.ra * kv_row_stride, lq, r.k0);
+    load_perm<KVT, E, Q4>(kbase + (size_t)r.rb * kv_row_stride, lq, r.k1);
     // INT8: lane l fetches one scale of key (l % 32): k_scale for l < 32,
     // v_scale above (lane l holds that key's index as ia or ib).
-    float my_scale = 0.0f;
+    r.sc = 0.0f;
     if constexpr (Cfg::kInt8) {
       const int si = (l & 16) ? ib : ia;
-      const bool sok = (l & 16) ? vb : va;
+      const bool sok = si >= 0 && si < live;
       const float* sp = (l < 32) ? ksc : vsc;
-      if (sok) my_scale = sp[(size_t)si * p.H_kv];
+      if (sok) r.sc = sp[(size_t)si * p.H_kv];
     }
+  };
+  // Compute one tile from its entries and loaded rows.
+  auto compute = [&](int ia, int ib, const TileRegs& r) {
+    const bool va = ia >= 0 && ia < live;
+    const bool vb = ib >= 0 && ib < live;
+    KVT vra[Q4], vrb[Q4];
+    load_perm<KVT, E, Q4>(vbase + (size_t)r.ra * kv_row_stride, lq, vra);
+    load_perm<KVT, E, Q4>(vbase + (size_t)r.rb * kv_row_stride, lq, vrb);
+    KVT kra[Q4], krb[Q4];
+    if constexpr (kCoal) {
+      lane_gather(r.k0, 4 * c16 + g4, kra);
+      lane_gather(r.k1, 4 * c16 + g4, krb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Q4; ++i) { kra[i] = r.k0[i]; krb[i] = r.k1[i]; }
+    }
+    const float my_scale = r.sc;
     // Validity of keys 4*g4 + i (half a) and 16 + 4*g4 + i (half b): lanes
     // 0..15 hold rows 0..15 of each half.
     const uint32_t bits_a = ((uint32_t)__ballot(va) >> (4 * g4)) & 0xFu;
@@ -429,6 +436,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  constexpr int kStep = kTile * kAttnWaves;     // keys between a wave's tiles
+  auto entry = [&](int j) { return j < k1 ? (DENSE ? j : idx_row[j]) : -1; };
+  const int t_first = k0 + kTile * wave;
+  int ia = next_a, ib = next_b;                 // this tile's entries
+  int na = entry(t_first + kStep + c16), nb = entry(t_first + kStep + 16 + c16);
+  TileRegs ra, rb;
+  if constexpr (Cfg::kF32Path || Cfg::kInt8) {
+    // One register set, loaded right before use: FP32 rows are twice as
+    // wide, and a second set would cost INT8 a wave per SIMD (3 -> 2),
+    // measured 7% slower on the batched INT8 decode.
+    for (int t0 = t_first; t0 < k1; t0 += kStep) {
+      issue(ia, ib, ra);
+      const int fa = entry(t0 + 2 * kStep + c16), fb = entry(t0 + 2 * kStep + 16 + c16);
+      compute(ia, ib, ra);
+      ia = na; ib = nb; na = fa; nb = fb;
+    }
+  } else {
+  if (t_first < k1) issue(ia, ib, ra);
+  // Two tiles per trip, the register sets swapping roles.
+  for (int t0 = t_first; t0 < k1; t0 += 2 * kStep) {
+    if (t0 + kStep < k1) issue(na, nb, rb);
+    int fa = entry(t0 + 2 * kStep + c16), fb = entry(t0 + 2 * kStep + 16 + c16);
+    compute(ia, ib, ra);
+    ia = na; ib = nb; na = fa; nb = fb;
+    if (t0 + kStep >= k1) break;
+    if (t0 + 2 * kStep < k1) issue(na, nb, ra);
+    fa = entry(t0 + 3 * kStep + c16); fb = entry(t0 + 3 * kStep + 16 + c16);
+    compute(ia, ib, rb);
+    ia = na; ib = nb; na = fa; nb = fb;
+  }
   }
 
   // ---- merge the 4 waves' states in LDS
