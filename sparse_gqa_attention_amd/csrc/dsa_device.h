@@ -30,20 +30,6 @@ __device__ __forceinline__ T ld_vec(const void* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
-// Loads that bypass the non-coherent per-CU cache: used to read what other
-// workgroups of the same grid published with device-scope atomics/fences.
-__device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Store that is coherent at device scope on its own (written through the
-// per-XCD L2), so that publishing it to other workgroups needs no L2
-// writeback -- only a wait for the store to complete (wait_vmem).
-__device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Wait until every vector memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
