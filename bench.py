@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "a24b4ff2535579dc",
-    "spec_decode_32k": {"attention": 18085992, "indexer": 5431067, "topk": 1304666},
-    "decode_256k": {"attention": 20302967, "indexer": 42128761, "topk": 9760508},
-    "prefill_128k": {"attention": 3453792559, "indexer": 1141506516, "topk": 1156553868},
-    "int8_batched_decode_64k": {"attention": 1158779457},
+    "sources": "e82f80802b45f04e",
+    "spec_decode_32k": {"attention": 18111434, "indexer": 5434862, "topk": 1316837},
+    "decode_256k": {"attention": 20328946, "indexer": 42208480, "topk": 9746204},
+    "prefill_128k": {"attention": 3446618998, "indexer": 1141510813, "topk": 1156618462},
+    "int8_batched_decode_64k": {"attention": 1144306797},
 }
 
 
