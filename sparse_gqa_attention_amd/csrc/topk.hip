@@ -498,27 +498,31 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   const float* src = scores + (size_t)row * L_cap;
   int32_t* out = indices + (size_t)row * k;
 
-  // ---- the whole row into LDS, every load in flight before any store.
-  // With 16-byte rows the loads cover the L_cap-long row and go out before
-  // the row's length is known (no wait for kv_len).
+  // ---- the whole row into LDS, every load in flight at once.  With
+  // 16-byte rows the loads are direct global -> LDS copies that cover the
+  // L_cap-long row and go out before the row's length is known (no wait for
+  // kv_len).
   if (vec4) {
+    // direct global -> LDS copies: a wave's 64 lanes fill 1 KB of the row
+    // at a time (lane l's 16 bytes at the wave's base + 16 l)
     constexpr int U = kResKeys / 4 / NT;
     const int L4 = L_cap / 4;                   // L_cap % 4 == 0
     const float4* src4 = reinterpret_cast<const float4*>(src);
     float4* row4 = reinterpret_cast<float4*>(rowf);
-    float4 v[U];
+    const int wbase = t - lane_id();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i4 = u * NT + t;
-      v[u] = i4 < L4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i4 < L4)
+        __builtin_amdgcn_global_load_lds((const void*)(src4 + i4),
+                                         (__attribute__((address_space(3))) void*)(row4 + u * NT + wbase),
+                                         16, 0, 0);
     }
     const int n = row_count(kv_len, row, S, L_cap);
-    if (n <= k) { write_all<NT>(out, n, k); return; }
-    const int n4 = (n + 3) / 4;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = u * NT + t;
-      if (i4 < n4) row4[i4] = v[u];
+    if (n <= k) {
+      wait_vmem();                              // no copy may land after the workgroup ends
+      write_all<NT>(out, n, k);
+      return;
     }
   } else {
     const int n = row_count(kv_len, row, S, L_cap);
@@ -543,6 +547,10 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   // is free until the candidates are listed.
   uint32_t* h1 = lidx;
   for (int i = t; i < kBins; i += NT) { s.hist[i] = 0; h1[i] = 0; }
+  // Every lane reads keys that other waves copied: each wave waits for its
+  // own copies (the compiler would only wait before this wave's LDS reads),
+  // then the barrier.
+  wait_vmem();
   __syncthreads();
 
   if (k <= kResCap) {
