@@ -204,6 +204,10 @@ __device__ __forceinline__ float head_sum(const float (&wv)[16], const f32x16& a
 // ------------------------------------------------------------------ prefill
 
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any record count used
+// Cache policy of the streamed score stores: non-temporal (streaming), so
+// that the scores do not push the key-state runs, which every token block
+// of a key group reads, out of L2 (measured about 4% faster at 2048 x 128K).
+constexpr int kScoreStorePolicy = 2;
 
 // Raw buffer resource (stride 0) over `bytes` bytes at p.  The fields pass
 // through readfirstlane so that the descriptor lives in scalar registers:
@@ -327,7 +331,7 @@ __device__ __forceinline__ void score_full_run(
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs,
-                                            off[p] + 128u * c, 0, 0);
+                                            off[p] + 128u * c, 0, kScoreStorePolicy);
     if (!PREFETCH && c + 1 < R / 32) {
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st)
@@ -363,7 +367,7 @@ __device__ __forceinline__ void stream_stage(
     for (int p = 0; p < PAIRS; ++p) {
       const uint32_t off = key_ok ? row_off[p] + 4u * (uint32_t)jc : kDropOffset;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs, off, 0,
-                                            0);
+                                            kScoreStorePolicy);
     }
   }
 }
