@@ -737,7 +737,11 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 #pragma unroll
         for (int u = 0; u < V; ++u) {
           const int i4 = b4 + u * NT + t;
-          const float4 q = i4 < n4 ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (i4 < n4) {                        // streamed once: non-temporal
+            const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src4 + i4));
+            q = make_float4(r[0], r[1], r[2], r[3]);
+          }
           x[4 * u + 0] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
         }
 #pragma unroll
