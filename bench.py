@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "e82f80802b45f04e",
-    "spec_decode_32k": {"attention": 18111434, "indexer": 5434862, "topk": 1316837},
-    "decode_256k": {"attention": 20328946, "indexer": 42208480, "topk": 9746204},
-    "prefill_128k": {"attention": 3446618998, "indexer": 1141510813, "topk": 1156618462},
-    "int8_batched_decode_64k": {"attention": 1144306797},
+    "sources": "502e5e6616fe3fea",
+    "spec_decode_32k": {"attention": 18111821, "indexer": 5435138, "topk": 1311834},
+    "decode_256k": {"attention": 20328702, "indexer": 42208383, "topk": 9750242},
+    "prefill_128k": {"attention": 3447561789, "indexer": 1125391818, "topk": 1090556038},
+    "int8_batched_decode_64k": {"attention": 1143874452},
 }
 
 
