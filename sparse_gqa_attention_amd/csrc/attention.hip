@@ -275,12 +275,36 @@ void attn_kernel(AttnParams p) {
     }
   };
   // Compute one tile from its entries and loaded rows.
+  // 16-bit V rows that go to LDS unconverted are read whole cache lines at a
+  // time: eight consecutive lanes cover 128 contiguous bytes of one row, so
+  // an instruction touches 8 lines instead of 16 half lines.  Instruction k
+  // of a half tile covers rows 8 (k / LPR) + l / 8, bytes 128 (k % LPR) +
+  // 16 (l % 8) (LPR: 128-byte lines per row).
+  constexpr bool kVLines = kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kLPR = kRowBytes / 128 > 0 ? kRowBytes / 128 : 1;
+  constexpr int kVI = 16 * kRowBytes / 1024;    // 16-byte loads per lane per half tile
   auto compute = [&](int ia, int ib, const TileRegs& r) {
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
-    KVT vra[Q4], vrb[Q4];
-    load_perm<KVT, E, Q4>(vbase + (size_t)r.ra * kv_row_stride, lq, vra);
-    load_perm<KVT, E, Q4>(vbase + (size_t)r.rb * kv_row_stride, lq, vrb);
+    KVT vra[kVLines ? 1 : Q4], vrb[kVLines ? 1 : Q4];
+    u32x4 vline[kVLines ? 2 * kVI : 1];
+    if constexpr (kVLines) {
+      static_assert(kRowBytes % 128 == 0 && kVI * 1024 == 16 * kRowBytes, "whole lines per row");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kVI; ++k) {
+          const int e = __shfl(h == 0 ? ia : ib, 8 * (k / kLPR) + (l >> 3), kWave);
+          const int row = e >= 0 && e < live ? e : 0;
+          vline[h * kVI + k] = ld_vec<u32x4>((const char*)(vbase + (size_t)row * kv_row_stride) +
+                                             128 * (k % kLPR) + 16 * (l & 7));
+        }
+      }
+    } else {
+      load_perm<KVT, E, Q4>(vbase + (size_t)r.ra * kv_row_stride, lq, vra);
+      load_perm<KVT, E, Q4>(vbase + (size_t)r.rb * kv_row_stride, lq, vrb);
+    }
     KVT kra[Q4], krb[Q4];
     if constexpr (kCoal) {
       lane_gather(r.k0, 4 * c16 + g4, kra);
@@ -320,7 +344,17 @@ void attn_kernel(AttnParams p) {
     }
 
     // ---- V rows into this wave's LDS tile (converted to the PV operand type)
-    {
+    if constexpr (kVLines) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kVI; ++k) {
+          MPV* dst = vt + (size_t)(16 * h + 8 * (k / kLPR) + (l >> 3)) * Cfg::kVStride +
+                     (128 * (k % kLPR) + 16 * (l & 7)) / 2;
+          *reinterpret_cast<u32x4*>(dst) = vline[h * kVI + k];
+        }
+      }
+    } else {
       MPV va_c[Q4], vb_c[Q4];
 #pragma unroll
       for (int i = 0; i < Q4; ++i) { va_c[i] = cvt<MPV>(vra[i]); vb_c[i] = cvt<MPV>(vrb[i]); }
