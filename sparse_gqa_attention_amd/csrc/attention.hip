@@ -280,8 +280,11 @@ void attn_kernel(AttnParams p) {
   // an instruction touches 8 lines instead of 16 half lines.  Instruction k
   // of a half tile covers rows 8 (k / LPR) + l / 8, bytes 128 (k % LPR) +
   // 16 (l % 8) (LPR: 128-byte lines per row).
-  constexpr bool kVLines = kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value;
-  constexpr int kRowBytes = D * 2;
+  // INT8 rows of 128 bytes are read the same way and converted on the way
+  // to LDS.
+  constexpr int kRowBytes = D * (int)sizeof(KVT);
+  constexpr bool kVLines = kRowBytes % 128 == 0 &&
+      ((kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value) || Cfg::kInt8);
   constexpr int kLPR = kRowBytes / 128 > 0 ? kRowBytes / 128 : 1;
   constexpr int kVI = 16 * kRowBytes / 1024;    // 16-byte loads per lane per half tile
   auto compute = [&](int ia, int ib, const TileRegs& r) {
@@ -349,9 +352,24 @@ void attn_kernel(AttnParams p) {
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int k = 0; k < kVI; ++k) {
+          constexpr int kEl = 16 / (int)sizeof(KVT);   // elements per 16-byte load
           MPV* dst = vt + (size_t)(16 * h + 8 * (k / kLPR) + (l >> 3)) * Cfg::kVStride +
-                     (128 * (k % kLPR) + 16 * (l & 7)) / 2;
-          *reinterpret_cast<u32x4*>(dst) = vline[h * kVI + k];
+                     (128 * (k % kLPR) + 16 * (l & 7)) / (int)sizeof(KVT);
+          if constexpr (std::is_same<MPV, KVT>::value) {
+            *reinterpret_cast<u32x4*>(dst) = vline[h * kVI + k];
+          } else {
+            KVT raw[kEl];
+            __builtin_memcpy(raw, &vline[h * kVI + k], 16);
+            MPV cv[kEl];
+#pragma unroll
+            for (int i = 0; i < kEl; ++i) cv[i] = cvt<MPV>(raw[i]);
+#pragma unroll
+            for (int i = 0; i < kEl * (int)sizeof(MPV) / 16; ++i) {
+              u32x4 w;
+              __builtin_memcpy(&w, &cv[i * 16 / (int)sizeof(MPV)], 16);
+              reinterpret_cast<u32x4*>(dst)[i] = w;
+            }
+          }
         }
       }
     } else {
