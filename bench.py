@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "502e5e6616fe3fea",
-    "spec_decode_32k": {"attention": 18111821, "indexer": 5435138, "topk": 1311834},
-    "decode_256k": {"attention": 20328702, "indexer": 42208383, "topk": 9750242},
-    "prefill_128k": {"attention": 3447561789, "indexer": 1125391818, "topk": 1090556038},
-    "int8_batched_decode_64k": {"attention": 1143874452},
+    "sources": "7ef6be2399ad3a11",
+    "spec_decode_32k": {"attention": 18131135, "indexer": 5435138, "topk": 1311834},
+    "decode_256k": {"attention": 20348088, "indexer": 42208303, "topk": 9750264},
+    "prefill_128k": {"attention": 3460333837, "indexer": 1125396908, "topk": 1091115774},
+    "int8_batched_decode_64k": {"attention": 1173032371},
 }
 
 
