@@ -204,10 +204,13 @@ __device__ __forceinline__ float head_sum(const float (&wv)[16], const f32x16& a
 // ------------------------------------------------------------------ prefill
 
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any record count used
-// Cache policy of the streamed score stores: non-temporal (streaming), so
-// that the scores do not push the key-state runs, which every token block
-// of a key group reads, out of L2 (measured about 4% faster at 2048 x 128K).
-constexpr int kScoreStorePolicy = 2;
+// Cache policy of the streamed score stores (SPOL template arguments):
+// prefill writes them non-temporal (streaming), so that a gigabyte of scores
+// does not push the key-state runs, which every token block of a key group
+// reads, out of the caches (prefill_128k layer 1143 -> 1076 us); long decode
+// contexts keep ordinary stores, since the top-k reads the scores back at
+// once (decode_256k 39.1 -> 38.5 us).
+constexpr int kStoreStreaming = 2, kStoreDefault = 0;
 
 // Raw buffer resource (stride 0) over `bytes` bytes at p.  The fields pass
 // through readfirstlane so that the descriptor lives in scalar registers:
@@ -296,7 +299,7 @@ __device__ __forceinline__ void copy_full_run(const T* __restrict__ src, uint4* 
 // work per chunk is the head-weighted sums alone.  Every chunk issues
 // exactly PAIRS buffer stores (all lanes in range: a full run has no key
 // past its end).
-template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH, int SPOL>
 __device__ __forceinline__ void score_full_run(
     const uint4* __restrict__ cur, int jr, const FullRunLane<T, DI, NT>& ln,
     const typename vec8<T>::type (&a)[PAIRS][DI / 16], const float (&wv)[PAIRS][16],
@@ -331,7 +334,7 @@ __device__ __forceinline__ void score_full_run(
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs,
-                                            off[p] + 128u * c, 0, kScoreStorePolicy);
+                                            off[p] + 128u * c, 0, SPOL);
     if (!PREFETCH && c + 1 < R / 32) {
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st)
@@ -346,7 +349,7 @@ __device__ __forceinline__ void score_full_run(
 // in `cur`.  The copy is issued untracked: the wait for it is the caller's.
 // Every chunk issues exactly PAIRS buffer stores.  Full runs take the
 // unrolled paths; the last, partial run of a range the general ones.
-template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH, int SPOL>
 __device__ __forceinline__ void stream_stage(
     const uint4* __restrict__ cur, uint4* __restrict__ nxt, const T* __restrict__ ks_b,
     int jn, int jn_end, int jr, int jr_end, int wave, int l, const FullRunLane<T, DI, NT>& ln,
@@ -355,7 +358,7 @@ __device__ __forceinline__ void stream_stage(
   if (jn_end - jn == R) copy_full_run<T, DI, NT, R>(ks_b + (size_t)jn * DI, nxt, wave, ln);
   else if (jn < jn_end) copy_key_rows<T, DI, NT, true>(ks_b, jn, jn_end, nxt, wave, l);
   if (jr_end - jr == R) {
-    score_full_run<T, DI, PAIRS, NT, R, PREFETCH>(cur, jr, ln, a, wv, rs, row_off);
+    score_full_run<T, DI, PAIRS, NT, R, PREFETCH, SPOL>(cur, jr, ln, a, wv, rs, row_off);
     return;
   }
   const int half = l >> 5, col = l & 31;
@@ -367,7 +370,7 @@ __device__ __forceinline__ void stream_stage(
     for (int p = 0; p < PAIRS; ++p) {
       const uint32_t off = key_ok ? row_off[p] + 4u * (uint32_t)jc : kDropOffset;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(head_sum(wv[p], acc[p])), rs, off, 0,
-                                            kScoreStorePolicy);
+                                            SPOL);
     }
   }
 }
@@ -376,7 +379,7 @@ __device__ __forceinline__ void stream_stage(
 // Two stages per trip, the buffers swapping roles.  The wait before a stage
 // covers the copy issued at the start of the previous one: after it, that
 // stage (a full run of R keys) issued PAIRS * R / 32 stores.
-template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH>
+template <typename T, int DI, int PAIRS, int NT, int R, bool PREFETCH, int SPOL>
 __device__ __forceinline__ void stream_keys(
     uint4* __restrict__ b0, uint4* __restrict__ b1, const T* __restrict__ ks_b, int j_begin,
     int j_end, int wave, int l, const FullRunLane<T, DI, NT>& ln,
@@ -386,13 +389,13 @@ __device__ __forceinline__ void stream_keys(
   int jr = j_begin;
   while (true) {
     int jr_end = min(jr + R, j_end);
-    stream_stage<T, DI, PAIRS, NT, R, PREFETCH>(b0, b1, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+    stream_stage<T, DI, PAIRS, NT, R, PREFETCH, SPOL>(b0, b1, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
                                       wave, l, ln, a, wv, rs, row_off);
     if (jr_end >= j_end) break;
     wait_vm_then_barrier<kStoresPerRun>();
     jr = jr_end;
     jr_end = min(jr + R, j_end);
-    stream_stage<T, DI, PAIRS, NT, R, PREFETCH>(b1, b0, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
+    stream_stage<T, DI, PAIRS, NT, R, PREFETCH, SPOL>(b1, b0, ks_b, jr_end, min(jr_end + R, j_end), jr, jr_end,
                                       wave, l, ln, a, wv, rs, row_off);
     if (jr_end >= j_end) break;
     wait_vm_then_barrier<kStoresPerRun>();
@@ -403,7 +406,7 @@ __device__ __forceinline__ void stream_keys(
 // R keys per LDS buffer (two buffers, 64 KB per workgroup: two workgroups
 // per CU).  Byte offsets within a wave's 4 score rows stay below 2^31 for
 // L_cap <= kIndexerMaxLcap.
-template <typename T, int DI, int PAIRS, int WAVES, int R, int WPE, bool PREFETCH>
+template <typename T, int DI, int PAIRS, int WAVES, int R, int WPE, bool PREFETCH, int SPOL>
 __global__ __launch_bounds__(WAVES * kWave, WPE) void indexer_stream_kernel(
     const T* __restrict__ q_idx, const float* __restrict__ w_idx,
     const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
@@ -459,8 +462,8 @@ __global__ __launch_bounds__(WAVES * kWave, WPE) void indexer_stream_kernel(
 
   wait_vmem();              // this wave's share of the first run has landed
   __syncthreads();          // ... and every other wave's
-  stream_keys<T, DI, PAIRS, NT, R, PREFETCH>(buf0, buf1, ks_b, j_begin, j_end, wave, l, ln, a, wv, rs,
-                                   row_off);
+  stream_keys<T, DI, PAIRS, NT, R, PREFETCH, SPOL>(buf0, buf1, ks_b, j_begin, j_end, wave, l, ln, a,
+                                                   wv, rs, row_off);
 }
 
 // ------------------------------------------------------------------ decode
@@ -547,7 +550,9 @@ void launch_stream(const IndexerLaunch& a, hipStream_t st) {
   using C = StreamCfg<DI>;
   dim3 grid(a.tok_blocks, a.key_blocks, a.B);
   hipLaunchKernelGGL(
-      (indexer_stream_kernel<T, DI, C::kPairs, C::kWaves, C::kRun, C::kWpe, C::kPrefetch>), grid,
+      (indexer_stream_kernel<T, DI, C::kPairs, C::kWaves, C::kRun, C::kWpe, C::kPrefetch,
+                             kStoreStreaming>),
+      grid,
       dim3(C::kWaves * kWave), 0, st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state,
       a.kv_len, a.S, a.H, a.L_cap, a.keys_per_wg, a.scores);
 }
@@ -559,7 +564,8 @@ template <typename T, int DI>
 void launch_stream_decode(const IndexerLaunch& a, hipStream_t st) {
   constexpr int R = 32768 / (2 * DI);
   dim3 grid(a.tok_blocks, a.key_blocks, a.B);
-  hipLaunchKernelGGL((indexer_stream_kernel<T, DI, 1, 4, R, 2, false>), grid, dim3(4 * kWave), 0,
+  hipLaunchKernelGGL((indexer_stream_kernel<T, DI, 1, 4, R, 2, false, kStoreDefault>), grid,
+                     dim3(4 * kWave), 0,
                      st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
                      a.L_cap, a.keys_per_wg, a.scores);
 }
