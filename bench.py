@@ -34,11 +34,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "7ef6be2399ad3a11",
-    "spec_decode_32k": {"attention": 18131135, "indexer": 5435138, "topk": 1311834},
-    "decode_256k": {"attention": 20348088, "indexer": 42208303, "topk": 9750264},
-    "prefill_128k": {"attention": 3460333837, "indexer": 1125396908, "topk": 1091115774},
-    "int8_batched_decode_64k": {"attention": 1173032371},
+    "sources": "ee2824fe31051418",
+    "spec_decode_32k": {"attention": 18131240, "indexer": 5435130, "topk": 1311834},
+    "decode_256k": {"attention": 20351610, "indexer": 42209348, "topk": 9750384},
+    "prefill_128k": {"attention": 3462397461, "indexer": 1125397123, "topk": 1091127127},
+    "int8_batched_decode_64k": {"attention": 1172406442},
 }
 
 
