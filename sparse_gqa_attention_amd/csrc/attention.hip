@@ -249,6 +249,23 @@ void attn_kernel(AttnParams p) {
   constexpr bool kCoal = Cfg::kCoalesced;
   constexpr int E = Cfg::kChunkElems;
   const int lrow = kCoal ? l >> 2 : c16, lq = kCoal ? l & 3 : g4;
+  // 16-bit V rows that go to LDS unconverted are read whole cache lines at a
+  // time: eight consecutive lanes cover 128 contiguous bytes of one row, so
+  // an instruction touches 8 lines instead of 16 half lines.  Instruction k
+  // of a half tile covers rows 8 (k / LPR) + l / 8, bytes 128 (k % LPR) +
+  // 16 (l % 8) (LPR: 128-byte lines per row).
+  // INT8 rows of 128 bytes are read the same way and converted on the way
+  // to LDS.  16-bit K rows are read the same way too and pass through the
+  // wave's LDS tile into the MFMA layout (instead of lane permutes).
+  constexpr int kRowBytes = D * (int)sizeof(KVT);
+  constexpr bool kVLines = kRowBytes % 128 == 0 &&
+      ((kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value) || Cfg::kInt8);
+  constexpr bool kKLines = kRowBytes % 128 == 0 && kCoal && sizeof(KVT) == 2 && !Cfg::kF32Path;
+  constexpr int kLPR = kRowBytes / 128 > 0 ? kRowBytes / 128 : 1;
+  constexpr int kVI = 16 * kRowBytes / 1024;    // 16-byte loads per lane per half tile
+  // Row (of half tile h) and byte offset within it of this lane's load k.
+  auto line_row = [&](int h, int k) { return 16 * h + 8 * (k / kLPR) + (l >> 3); };
+  auto line_off = [&](int k) { return 128 * (k % kLPR) + 16 * (l & 7); };
   struct TileRegs {
     KVT k0[Q4], k1[Q4];                   // K rows of half tiles a and b, as loaded
     int ra, rb;                           // the rows this lane loads (-1: none)
@@ -262,8 +279,25 @@ void attn_kernel(AttnParams p) {
     const int ia_l = load_row(ia), ib_l = load_row(ib);
     r.ra = ia_l >= 0 && ia_l < live ? ia_l : 0;
     r.rb = ib_l >= 0 && ib_l < live ? ib_l : 0;
-    load_perm<KVT, E, Q4>(kbase + (size_t)r.ra * kv_row_stride, lq, r.k0);
-    load_perm<KVT, E, Q4>(kbase + (size_t)r.rb * kv_row_stride, lq, r.k1);
+    if constexpr (kKLines) {
+      static_assert(kVI * 16 == Q4 * (int)sizeof(KVT), "a half tile's lines fill k0 / k1");
+      u32x4 kl[2 * kVI];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kVI; ++k) {
+          const int e = __shfl(h == 0 ? ia : ib, line_row(0, k), kWave);
+          const int row = e >= 0 && e < live ? e : 0;
+          kl[h * kVI + k] = ld_vec<u32x4>((const char*)(kbase + (size_t)row * kv_row_stride) +
+                                          line_off(k));
+        }
+      }
+      __builtin_memcpy(r.k0, &kl[0], sizeof(r.k0));
+      __builtin_memcpy(r.k1, &kl[kVI], sizeof(r.k1));
+    } else {
+      load_perm<KVT, E, Q4>(kbase + (size_t)r.ra * kv_row_stride, lq, r.k0);
+      load_perm<KVT, E, Q4>(kbase + (size_t)r.rb * kv_row_stride, lq, r.k1);
+    }
     // INT8: lane l fetches one scale of key (l % 32): k_scale for l < 32,
     // v_scale above (lane l holds that key's index as ia or ib).
     r.sc = 0.0f;
@@ -275,18 +309,6 @@ void attn_kernel(AttnParams p) {
     }
   };
   // Compute one tile from its entries and loaded rows.
-  // 16-bit V rows that go to LDS unconverted are read whole cache lines at a
-  // time: eight consecutive lanes cover 128 contiguous bytes of one row, so
-  // an instruction touches 8 lines instead of 16 half lines.  Instruction k
-  // of a half tile covers rows 8 (k / LPR) + l / 8, bytes 128 (k % LPR) +
-  // 16 (l % 8) (LPR: 128-byte lines per row).
-  // INT8 rows of 128 bytes are read the same way and converted on the way
-  // to LDS.
-  constexpr int kRowBytes = D * (int)sizeof(KVT);
-  constexpr bool kVLines = kRowBytes % 128 == 0 &&
-      ((kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value) || Cfg::kInt8);
-  constexpr int kLPR = kRowBytes / 128 > 0 ? kRowBytes / 128 : 1;
-  constexpr int kVI = 16 * kRowBytes / 1024;    // 16-byte loads per lane per half tile
   auto compute = [&](int ia, int ib, const TileRegs& r) {
     const bool va = ia >= 0 && ia < live;
     const bool vb = ib >= 0 && ib < live;
@@ -309,7 +331,38 @@ void attn_kernel(AttnParams p) {
       load_perm<KVT, E, Q4>(vbase + (size_t)r.rb * kv_row_stride, lq, vrb);
     }
     KVT kra[Q4], krb[Q4];
-    if constexpr (kCoal) {
+    if constexpr (kKLines) {
+      // lines -> rows of the wave's LDS tile -> lane c16 + 16 g4 reads dims
+      // [32 st + 8 g4, + 8) of row c16 (half a) and 16 + c16 (half b): the
+      // MFMA A layout, in the D order the query was loaded in
+      char* tile = reinterpret_cast<char*>(vt);
+      constexpr int kRS = Cfg::kVStride * (int)sizeof(MPV);     // tile row stride, bytes
+      static_assert(kRS >= kRowBytes, "K rows fit the tile's rows");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kVI; ++k) {
+          u32x4 w;
+          __builtin_memcpy(&w, (h == 0 ? (const char*)r.k0 : (const char*)r.k1) + 16 * k, 16);
+          *reinterpret_cast<u32x4*>(tile + line_row(h, k) * kRS + line_off(k)) = w;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int st = 0; st < Q4 / 8; ++st) {
+        const u32x4 wa = *reinterpret_cast<const u32x4*>(tile + c16 * kRS + 2 * (32 * st + 8 * g4));
+        const u32x4 wb =
+            *reinterpret_cast<const u32x4*>(tile + (16 + c16) * kRS + 2 * (32 * st + 8 * g4));
+        __builtin_memcpy(&kra[8 * st], &wa, 16);
+        __builtin_memcpy(&krb[8 * st], &wb, 16);
+      }
+      // the V rows reuse the tile: every K read of this wave is done first
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if constexpr (kCoal) {
       lane_gather(r.k0, 4 * c16 + g4, kra);
       lane_gather(r.k1, 4 * c16 + g4, krb);
     } else {
