@@ -10,9 +10,10 @@ Inputs are seeded and synthetic and already resident in HBM when the timed
 region starts.  By default one step is captured as a HIP graph (through
 torch.cuda.CUDAGraph) and replayed, as a decode step is in a serving loop;
 --eager times plain launches.  HIP events on the launch stream time K step
-replays, then K replays of a graph of each stage alone; the stage with the
-longest time is the dominant one, and its algorithmic bytes per call divided
-by its average duration is the roofline `achieved` figure.
+replays (after K untimed ones), then K replays of a graph of each stage
+alone; the stage with the longest time is the dominant one, and its
+algorithmic bytes per call divided by its average duration is the roofline
+`achieved` figure.
 The CPU baseline times the FP64 oracle on the host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -326,7 +327,10 @@ def main():
             torch.cuda.synchronize()
             run_step = graphs["step"].replay
             run_stage = {st: graphs[st].replay for st in list(stages) + list(extra_fns)}
-            for _ in range(3):
+            # As many untimed replays as timed ones: the first replays of a
+            # step made of long memory-bound kernels (the INT8 batched
+            # decode) ran about 3% slower than steady state.
+            for _ in range(max(3, args.steps)):
                 run_step()
             torch.cuda.synchronize()
             mode = "hip_graph"

@@ -9,9 +9,10 @@
 // gfx950 design.  A workgroup (4 waves) owns one (row, KV head g, key split).
 // Each wave walks 32-key tiles of the split's selected-index list.  The
 // logits are formed transposed, S^T = K . Q^T, with v_mfma_f32_16x16x32:
-//   * A operand = K rows: lane l loads a contiguous quarter of the row of key
-//     (l % 16) straight from HBM with 16-byte loads (the d <-> k-slot
-//     permutation is free because Q uses the same one);
+//   * A operand = K rows: lane c16 + 16 g4 holds quarter g4 (in a d <-> k-slot
+//     permutation that is free because Q uses the same one) of the row of
+//     key c16; the rows arrive by line-wide 16-byte loads staged through the
+//     wave's LDS tile (or, for rows shorter than a line, by lane permutes);
 //   * B operand = Q^T: the R <= 16 query heads of group g (zero-padded),
 //     converted once to the MFMA type and kept in registers.
 // S^T leaves each lane with 4 keys of one head, which is exactly the B
@@ -237,15 +238,15 @@ void attn_kernel(AttnParams p) {
   // current tile is computed, and the index-list entries two tiles ahead.
   // V rows are requested when their tile starts; they are first needed
   // after the QK product and the softmax, which cover their latency.
-  // K and V rows are loaded coalesced: lane l reads row l/4 of each half
-  // tile, chunks 4c + l%4, so four consecutive lanes cover 64 contiguous
-  // bytes of one row and the texture addresser merges them (rows
-  // themselves are scattered).  K then moves into the MFMA layout -- lane
-  // c16 + 16 g4 holds chunks 4c + g4 of row c16, which load lane
-  // 4 c16 + g4 read -- by lane permutes; V goes to LDS as loaded.
-  // INT8 rows (128 bytes) keep the MFMA layout for the loads: lane
-  // c16 + 16 g4 reads the 32-byte quarter g4 of row c16 (measured faster
-  // than the coalesced form there).
+  // Rows whose length is a whole number of 128-byte lines (16-bit and
+  // INT8 at D 128, 16-bit at D 64) are read a line per eight lanes (see
+  // below).  Otherwise K and V rows are loaded coalesced: lane l reads row
+  // l/4 of each half tile, chunks 4c + l%4, so four consecutive lanes cover
+  // 64 contiguous bytes of one row (rows themselves are scattered), and K
+  // moves into the MFMA layout -- lane c16 + 16 g4 holds chunks 4c + g4 of
+  // row c16, which load lane 4 c16 + g4 read -- by lane permutes; INT8 rows
+  // of 64 bytes keep the MFMA layout for the loads: lane c16 + 16 g4 reads
+  // the quarter g4 of row c16.
   constexpr bool kCoal = Cfg::kCoalesced;
   constexpr int E = Cfg::kChunkElems;
   const int lrow = kCoal ? l >> 2 : c16, lq = kCoal ? l & 3 : g4;
@@ -256,11 +257,13 @@ void attn_kernel(AttnParams p) {
   // 16 (l % 8) (LPR: 128-byte lines per row).
   // INT8 rows of 128 bytes are read the same way and converted on the way
   // to LDS.  16-bit K rows are read the same way too and pass through the
-  // wave's LDS tile into the MFMA layout (instead of lane permutes).
+  // wave's LDS tile into the MFMA layout (instead of lane permutes), and so
+  // are INT8 K rows of 128 bytes.
   constexpr int kRowBytes = D * (int)sizeof(KVT);
   constexpr bool kVLines = kRowBytes % 128 == 0 &&
       ((kCoal && sizeof(KVT) == 2 && std::is_same<MPV, KVT>::value) || Cfg::kInt8);
-  constexpr bool kKLines = kRowBytes % 128 == 0 && kCoal && sizeof(KVT) == 2 && !Cfg::kF32Path;
+  constexpr bool kKLines = kRowBytes % 128 == 0 &&
+      ((kCoal && sizeof(KVT) == 2 && !Cfg::kF32Path) || Cfg::kInt8);
   constexpr int kLPR = kRowBytes / 128 > 0 ? kRowBytes / 128 : 1;
   constexpr int kVI = 16 * kRowBytes / 1024;    // 16-byte loads per lane per half tile
   // Row (of half tile h) and byte offset within it of this lane's load k.
@@ -332,9 +335,10 @@ void attn_kernel(AttnParams p) {
     }
     KVT kra[Q4], krb[Q4];
     if constexpr (kKLines) {
-      // lines -> rows of the wave's LDS tile -> lane c16 + 16 g4 reads dims
-      // [32 st + 8 g4, + 8) of row c16 (half a) and 16 + c16 (half b): the
-      // MFMA A layout, in the D order the query was loaded in
+      // lines -> rows of the wave's LDS tile -> lane c16 + 16 g4 reads the
+      // chunks c of E elements at dims (4 c + g4) E of row c16 (half a) and
+      // 16 + c16 (half b): the MFMA A layout, in the D order the query was
+      // loaded in
       char* tile = reinterpret_cast<char*>(vt);
       constexpr int kRS = Cfg::kVStride * (int)sizeof(MPV);     // tile row stride, bytes
       static_assert(kRS >= kRowBytes, "K rows fit the tile's rows");
@@ -350,13 +354,18 @@ void attn_kernel(AttnParams p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int kCB = E * (int)sizeof(KVT);             // chunk bytes: 16 or 32
+      static_assert(kCB % 16 == 0, "chunks of whole 16-byte reads");
 #pragma unroll
-      for (int st = 0; st < Q4 / 8; ++st) {
-        const u32x4 wa = *reinterpret_cast<const u32x4*>(tile + c16 * kRS + 2 * (32 * st + 8 * g4));
-        const u32x4 wb =
-            *reinterpret_cast<const u32x4*>(tile + (16 + c16) * kRS + 2 * (32 * st + 8 * g4));
-        __builtin_memcpy(&kra[8 * st], &wa, 16);
-        __builtin_memcpy(&krb[8 * st], &wb, 16);
+      for (int c = 0; c < Q4 / E; ++c) {
+#pragma unroll
+        for (int b = 0; b < kCB / 16; ++b) {
+          const int off = (4 * c + g4) * kCB + 16 * b;
+          const u32x4 wa = *reinterpret_cast<const u32x4*>(tile + c16 * kRS + off);
+          const u32x4 wb = *reinterpret_cast<const u32x4*>(tile + (16 + c16) * kRS + off);
+          __builtin_memcpy(&kra[c * E + b * (16 / (int)sizeof(KVT))], &wa, 16);
+          __builtin_memcpy(&krb[c * E + b * (16 / (int)sizeof(KVT))], &wb, 16);
+        }
       }
       // the V rows reuse the tile: every K read of this wave is done first
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
