@@ -42,6 +42,8 @@ COMBOS = [
     ("f16", "i8", "f16", 64, 16, 1),
     ("bf16", "f16", "f32", 64, 12, 2),
     ("bf16", "i8", "f32", 64, 10, 2),
+    ("f16", "i8", "bf16", 128, 12, 2),
+    ("f16", "bf16", "bf16", 64, 8, 2),
 ]
 
 
