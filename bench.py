@@ -35,11 +35,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "ee2824fe31051418",
-    "spec_decode_32k": {"attention": 18131240, "indexer": 5435130, "topk": 1311834},
-    "decode_256k": {"attention": 20351610, "indexer": 42209348, "topk": 9750384},
-    "prefill_128k": {"attention": 3462397461, "indexer": 1125397123, "topk": 1091127127},
-    "int8_batched_decode_64k": {"attention": 1172406442},
+    "sources": "6de9ab8ee0843ab3",
+    "spec_decode_32k": {"attention": 18138345, "indexer": 5435126, "topk": 1311835},
+    "decode_256k": {"attention": 20355332, "indexer": 42208399, "topk": 9750247},
+    "prefill_128k": {"attention": 3428960650, "indexer": 1125388769, "topk": 1090533865},
+    "int8_batched_decode_64k": {"attention": 1154571104},
 }
 
 
