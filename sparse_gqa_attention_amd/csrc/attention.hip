@@ -796,6 +796,15 @@ void plan_attention(AttnLaunch& a, bool decode) {
   kps = ((kps + kTile - 1) / kTile) * kTile;
   if (kps < 128) kps = 128;
   long long ns = (a.k + kps - 1) / kps;
+  // With one tile per wave, a grid beyond two workgroups per CU (the
+  // residency of the 16-bit D=128 kernel) runs a second dispatch round of
+  // latency-bound workgroups; two tiles per wave (the second tile's loads
+  // overlap the first's compute) in one round are faster there.
+  constexpr long long kOneRound = 2LL * 256;      // 256 CUs
+  if (kps == 128 && rows_kv * ns > kOneRound) {
+    kps = 256;
+    ns = (a.k + kps - 1) / kps;
+  }
   if (ns > max_split) {
     ns = max_split;
     kps = (a.k + max_split - 1) / max_split;

@@ -77,6 +77,15 @@ def test_attention_many_splits_and_short_rows(dsa, decode):
     _run_case(dsa, combo, B=3, S=8, L=3000, k=1000, kv_len=[3000, 900, 40], decode=decode, seed=32)
 
 
+@pytest.mark.parametrize("decode", [True, False], ids=["decode", "prefill"])
+def test_attention_wide_batch_two_tiles_per_wave(dsa, decode):
+    # 4 x 8 rows x 2 KV heads with 1500 keys: 128-key splits would need 768
+    # workgroups, so the decode plan takes 256-key splits (two tiles per wave).
+    combo = ("bf16", "f16", "bf16", 128, 24, 2)
+    _run_case(dsa, combo, B=4, S=8, L=3000, k=1500, kv_len=[3000, 1700, 900, 40], decode=decode,
+              seed=35)
+
+
 def test_attention_rising_max_with_huge_value_scale(dsa):
     """Pages' worked example: logits 0 then 88 in a later tile/split, V scale 2^120."""
     L, k, D = 200, 160, 64
