@@ -668,10 +668,11 @@ struct StreamCfg {
   static_assert(kRegionA >= 2 * kSegWords, "fallback segments must fit region A");
 };
 
-template <int NT, int CAP>
+// VEC4: rows start 16-byte aligned (L_cap % 4 == 0), read with 16-byte loads.
+template <int NT, int CAP, bool VEC4>
 __global__ __launch_bounds__(NT) void topk_stream_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int vec4, int32_t* __restrict__ indices) {
+    int k, int32_t* __restrict__ indices) {
   using Cfg = StreamCfg<NT, CAP>;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   Lds s{lds, lds + kBins, lds + kBins + 32};
@@ -688,17 +689,32 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
     uint32_t* sample = regionA;
     const int cnt = n <= kSample ? n : kSample;
     constexpr int U = kSample / NT;
+    constexpr int V = kStreamLoads;
+    // The row's first stream step goes out with the sample, so that every
+    // workgroup's HBM traffic continues while it computes the threshold.
+    // All these loads are unconditional (indices clamped into the row), so
+    // the sample's wait leaves the stream loads in flight.
     float v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = u * NT + t;
-      v[u] = i < cnt ? src[n <= kSample ? i : sample_pos<kSample>(i, n)] : 0.0f;
+      v[u] = src[i < cnt ? (n <= kSample ? i : sample_pos<kSample>(i, n)) : 0];
+    }
+    const float4* src4 = reinterpret_cast<const float4*>(src);
+    const int n4 = VEC4 ? n / 4 : 0;
+    float4 first[V];
+    if (VEC4) {
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        // beyond the row: index 0 (L_cap >= 4); the stream masks those lanes
+        const int i4 = u * NT + t;
+        const f32x4 r = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(src4 + (i4 < n4 ? i4 : 0)));
+        first[u] = make_float4(r[0], r[1], r[2], r[3]);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = u * NT + t;
-      if (i < cnt) sample[i] = score_key(v[u]);
-    }
+    for (int u = 0; u < U; ++u) sample[u * NT + t] = score_key(v[u]);   // read below cnt only
     for (int i = t; i < kBins; i += NT) { s.hist[i] = 0u; bm[i] = 0u; }   // bm: free until emission
     __syncthreads();
     uint32_t T_lo;
@@ -723,24 +739,24 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
         }
     };
     int done = 0;
-    if (vec4) {
+    if (VEC4) {
       // Hits are tested on floats: x >= f_lo <=> score_key(x) >= T_lo
       // (score_key is order-preserving and gives -0.0 the key of +0.0;
       // denormals are preserved in comparisons).  Only hits become keys.
       const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
-      const float4* src4 = reinterpret_cast<const float4*>(src);
-      const int n4 = n / 4;
-      constexpr int V = kStreamLoads;
       for (int b4 = 0; b4 < n4; b4 += V * NT) {
         float x[4 * V];
         uint32_t hm = 0;
 #pragma unroll
         for (int u = 0; u < V; ++u) {
           const int i4 = b4 + u * NT + t;
-          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (i4 < n4) {                        // streamed once: non-temporal
-            const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src4 + i4));
-            q = make_float4(r[0], r[1], r[2], r[3]);
+          float4 q = first[u];                  // step 0: loaded with the sample
+          if (b4 > 0) {
+            q = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i4 < n4) {                      // streamed once: non-temporal
+              const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src4 + i4));
+              q = make_float4(r[0], r[1], r[2], r[3]);
+            }
           }
           x[4 * u + 0] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
         }
@@ -1114,16 +1130,22 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
     opt_in_lds(topk_resident_kernel<kResThreads>, kResLds);
-    opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap>, StreamPlan::kLds);
+    opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap, true>, StreamPlan::kLds);
+    opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap, false>, StreamPlan::kLds);
     opt_in_lds(topk_finish_kernel, finish_lds_bytes(kMaxChunks));
     lds_opt_in = true;
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
   switch (p.kind) {
     case kPlanStream:
-      hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap>), dim3(p.rows),
-                         dim3(kStreamThreads), StreamPlan::kLds, st, scores, kv_len, S, L_cap, k,
-                         vec4, indices);
+      if (vec4)
+        hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap, true>), dim3(p.rows),
+                           dim3(kStreamThreads), StreamPlan::kLds, st, scores, kv_len, S, L_cap,
+                           k, indices);
+      else
+        hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap, false>), dim3(p.rows),
+                           dim3(kStreamThreads), StreamPlan::kLds, st, scores, kv_len, S, L_cap,
+                           k, indices);
       return;
     case kPlanResident:
       hipLaunchKernelGGL((topk_resident_kernel<kResThreads>), dim3(p.rows), dim3(kResThreads), kResLds, st,
