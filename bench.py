@@ -35,11 +35,11 @@ METRIC = "µs/layer + achieved HBM GB/s for sparse GQA decode at 32K–256K ctx"
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "6de9ab8ee0843ab3",
-    "spec_decode_32k": {"attention": 18138345, "indexer": 5435126, "topk": 1311835},
-    "decode_256k": {"attention": 20355332, "indexer": 42208399, "topk": 9750247},
-    "prefill_128k": {"attention": 3428960650, "indexer": 1125388769, "topk": 1090533865},
-    "int8_batched_decode_64k": {"attention": 1154571104},
+    "sources": "c5d1d07dedca146b",
+    "spec_decode_32k": {"attention": 18138325, "indexer": 5435081, "topk": 1298523},
+    "decode_256k": {"attention": 20355511, "indexer": 42208577, "topk": 9777949},
+    "prefill_128k": {"attention": 3430403310, "indexer": 1125393242, "topk": 1089186349},
+    "int8_batched_decode_64k": {"attention": 1155072974},
 }
 
 
