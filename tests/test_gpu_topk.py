@@ -190,6 +190,19 @@ def test_topk_resident_rows_unaligned_short_and_at_capacity(dsa):
     _check(dsa, sc, [32768, 9000], 1, what="resident k=1, ragged")
 
 
+def test_topk_streaming_rows_unaligned_and_ragged(dsa):
+    # The many-rows plan with row lengths that are not a multiple of 4
+    # (element loads, no 16-byte path), ragged sequences, a sequence whose
+    # rows hold fewer keys than k, and heavy ties.
+    r = rng(20)
+    sc = torch.from_numpy(r.standard_normal((2, 130, 5001)).astype(np.float32))
+    _check(dsa, sc, [5001, 3333], 512, what="stream, L%4=1, ragged")
+    sc = integer_scores(r, (3, 64, 9002), -15, 15)
+    _check(dsa, sc, [9002, 600, 64], 700, what="stream, L%4=2, short rows, ties")
+    sc = torch.from_numpy(r.standard_normal((1, 129, 20000)).astype(np.float32))
+    _check(dsa, sc, [20000], 2048, what="stream, L%4=0")
+
+
 def test_topk_very_long_rows(dsa):
     # Few rows of 4.5M keys: more than 2048 chunks per row, where the finish
     # kernel keeps a single select histogram and zeroes it per level.
