@@ -168,8 +168,8 @@ def cpu_baseline(w, x, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs the "
-              f"hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs "
+              f"the hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     import sparse_gqa_attention_amd as dsa
