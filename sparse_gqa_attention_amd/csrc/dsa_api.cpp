@@ -211,7 +211,8 @@ dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, in
     CHECK(check_ptr(workspace, "workspace"));
   }
   (void)hipGetLastError();
-  dsa::launch_topk(p, scores, kv_len, S, L_cap, k, indices, workspace, (hipStream_t)stream);
+  dsa::launch_topk(p, scores, kv_len, S, L_cap, max_kv_len, k, indices, workspace,
+                   (hipStream_t)stream);
   return hip_result("dsa_topk");
 }
 

@@ -44,6 +44,8 @@
 //    in the chunk's own slots (or a block of the row's pool), KC (one
 //    workgroup per row) gathers the chunks in order, selects and emits.
 //    Kernel boundaries order the three.
+#include <cmath>
+
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -60,16 +62,12 @@ constexpr int kResKeys = 32768;        // longest row the resident plan holds
 constexpr int kResCap = 4096;          // candidate list; the select's histogram follows it
 constexpr int kResSample = 2048;       // sample of a resident row (already in LDS)
 constexpr int kRowCap = 4096;
-constexpr int kMultiCap = 8192;
-static_assert(kMultiCap < 65536 && kResCap < 65536, "ordered emission packs counts in 16 bits");
+static_assert(kResCap < 65536, "ordered emission packs counts in 16 bits");
 static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits the row area");
-constexpr int kMultiSample = 4096;     // sample of the threshold kernel
-constexpr int kChunkThreads = 256;
-constexpr int kChunkKeysPerThread = 8;
 constexpr int kStreamLoads = 4;        // 16-byte loads per lane in flight (streaming plan)
 static_assert(4 * kStreamLoads <= 32, "one hit bit per key of a lane's step");
 
-enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanMulti = 2 };
+enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanSplit = 2 };
 
 // Radix levels: key bits [31:21], [20:10], [9:0].
 __device__ __forceinline__ int lvl_shift(int lvl) { return lvl == 0 ? 21 : (lvl == 1 ? 10 : 0); }
@@ -110,7 +108,9 @@ constexpr int kTieSmall = 64;     // ties resolved by one wave without a radix p
 constexpr int kMiscWords = 16 + kTieSmall;
 
 // The bin holding the need-th largest key of a 2048-bin histogram:
-// misc[0] = bin, misc[1] = keys in higher bins.  Block-wide.
+// misc[0] = bin, misc[1] = keys in higher bins.  Block-wide.  Each thread
+// reads its BPT bins once into registers (a second pass of LDS reads behind
+// the finder's conditional LDS writes would run as a serial chain).
 template <int NT>
 __device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* scratch,
                            uint32_t* misc) {
@@ -118,17 +118,22 @@ __device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* scratc
   static_assert(BPT * NT == kBins, "block size must divide the bin count");
   const int t = threadIdx.x;
   if (t == 0) { misc[0] = 0; misc[1] = 0; }   // ordered before the finder by the scan's barriers
+  uint32_t h[BPT];
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) local += hist[kBins - 1 - (t * BPT + i)];
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = hist[kBins - 1 - (t * BPT + i)];
+    local += h[i];
+  }
   uint32_t total;
   uint32_t before = block_exclusive_scan<NT>(local, scratch, &total);
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    const int bin = kBins - 1 - (t * BPT + i);
-    const uint32_t h = hist[bin];
-    if (before < need && need <= before + h) { misc[0] = (uint32_t)bin; misc[1] = before; }
-    before += h;
+    if (before < need && need <= before + h[i]) {
+      misc[0] = (uint32_t)(kBins - 1 - (t * BPT + i));
+      misc[1] = before;
+    }
+    before += h[i];
   }
   __syncthreads();
 }
@@ -176,8 +181,8 @@ constexpr int kRelBits = 12;
 constexpr int kRelBins = 1 << kRelBits;
 
 template <int NT>
-__device__ void select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t* scratch,
-                               uint32_t* misc) {
+__device__ uint32_t select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t* scratch,
+                                   uint32_t* misc) {
   constexpr int BPT = kRelBins / NT;
   static_assert(BPT * NT == kRelBins, "block size must divide the bin count");
   const int t = threadIdx.x;
@@ -200,6 +205,7 @@ __device__ void select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t* sc
     before += h[i];
   }
   __syncthreads();
+  return total;
 }
 
 template <int NT, typename KeyOf>
@@ -237,7 +243,7 @@ __device__ void radix_select_rel(KeyOf key_of, int count, uint32_t need, uint32_
 template <int NT>
 __device__ void emit_ordered(const uint32_t* lkey, const uint32_t* lidx, int m, uint32_t T,
                              uint32_t take, int32_t* out, uint32_t* scratch) {
-  // m <= kMultiCap < 2^16 (multi plan), m <= kResCap (resident plan)
+  // m <= kListCap < 2^16 (split plan), m <= kResCap (resident plan)
   const int per = (m + NT - 1) / NT;
   const int i0 = min(threadIdx.x * per, m), i1 = min(i0 + per, m);
   uint32_t gt = 0, eq = 0;
@@ -806,284 +812,409 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
                        regionA + kSegWords, out, s);
 }
 
-// ====================================================================== multi plan
-enum { kModeAll = 0, kModeList = 1, kModeExact = 2 };
+// ====================================================================== split plan
+// Few rows (B*S < 128) of any length.  Each row is cut into chunks of CH keys.
+//
+// K1, topk_chunk_kernel: one 256-thread workgroup per (chunk, row).  Every
+// workgroup of a row draws the same sample of the row and computes the same
+// sample threshold T_lo (a kernel of its own, or a hand-off between
+// workgroups, costs more than recomputing it).  The sample is spread over the
+// host bound max_kv_len, so its loads go out together with the chunk's own,
+// before the row's length is known; a row much shorter than that bound draws
+// a second sample over its own length.  The workgroup lists the chunk's keys
+// >= T_lo, in index order, in the chunk's slots and writes the chunk's
+// record (count, T_lo, largest sampled key).
+//
+// K2, topk_select_kernel: one workgroup per row.  The first `spec` slots of
+// every chunk are stored interleaved so that lane t of K2 loads, coalesced,
+// the E consecutive entries it owns (chunk t / (spec / E), entries
+// E (t % (spec / E)) + [0, E)); lanes therefore hold the whole candidate list
+// in index order in registers, in one memory round with the chunk records.
+// The exact selection runs on relative radix digits of key - T_lo
+// (histograms in LDS), and one block scan emits the kept indices in order.
+// Rows with a chunk of more than `spec` candidates take a general path that
+// gathers the list into LDS.
+//
+// Exactness: the list holds every key >= T_lo.  When it holds at least k keys
+// and no chunk overflowed its slots, the row's k-th largest key is >= T_lo,
+// so every key that can be selected is listed and the selection on the list
+// equals the selection on the row.  Otherwise (a threshold above the k-th
+// key, a chunk with more candidates than slots, a list longer than LDS holds)
+// K2 selects exactly from the whole row.
+constexpr int kChunkThreads = 256;
+static_assert(kChunkThreads == kSampleBlock, "lane t takes element t of every sample block");
+constexpr int kSelThreads = 512;
+constexpr int kListCap = 8192;          // candidates the general path holds in LDS
+static_assert(kListCap < 65536, "ordered emission packs counts in 16 bits");
+constexpr int kSpecMax = 16384;         // entries the fast path holds (kSelThreads x 32)
+constexpr int kMaxSplitChunks = 2048;   // chunks per row (L_cap <= 2^24 with CH = 8192)
+constexpr int kMinSample = 1024;        // smaller valid samples are drawn again over the row
+static_assert(kListCap >= 2 * kSegWords, "fallback segments fit the list area");
+static_assert(kRelBins >= kBins, "the fallback histogram fits a select histogram");
 
-// Candidates of chunk c of a row are kept in index order: in the chunk's
-// own slots when there are at most kSlotCap of them, else in a block of the
-// row's pool reserved with one atomic.  Meta[c] = (count, pool offset or
-// kNoPool).  A pool that would overflow flags the row for the exact path.
-constexpr int kSlotCap = 64;
-constexpr uint32_t kNoPool = 0xFFFFFFFFu;
-// Chunks of 256..2048 keys: at most 2^24 / 2048 per row (a chunk below 2048
-// keys only when the row has at most 1024 of them).
-constexpr int kMaxChunks = 8192;
-constexpr int kSpecSlots = 16384;      // slots per row the finish kernel loads up front
-
-struct MultiWs {
-  uint32_t* state;   // [rows][4]: T_lo, mode, pool count, pool overflow flag
-  uint2* meta;       // [rows][chunks]: (candidates, pool offset | kNoPool)
-  uint2* slots;      // [rows][chunks][kSlotCap]: (key, index)
-  uint2* pool;       // [rows][kMultiCap]: (key, index)
+struct SplitWs {
+  uint4* meta;       // [rows][nch_ws]: (candidates, T_lo, largest sampled key, 0)
+  uint2* slots;      // [rows][nch_ws][cap]: (key, index)
 };
 
-__host__ __device__ inline MultiWs carve(void* ws, int rows, int chunks) {
-  MultiWs m;
-  m.state = (uint32_t*)ws;
-  m.meta = (uint2*)(m.state + (size_t)rows * 4);
-  m.slots = m.meta + (size_t)rows * chunks;
-  m.pool = m.slots + (size_t)rows * chunks * kSlotCap;
-  return m;
-}
-__host__ inline size_t multi_ws_bytes(int rows, int chunks) {
-  return (size_t)rows * 4 * 4 +
-         (size_t)rows * ((size_t)chunks * (1 + kSlotCap) + kMultiCap) * sizeof(uint2);
+__host__ __device__ inline SplitWs split_carve(void* ws, int rows, int nch_ws) {
+  SplitWs w;
+  w.meta = (uint4*)ws;
+  w.slots = (uint2*)(w.meta + (size_t)rows * nch_ws);
+  return w;
 }
 
-constexpr int kStateThreads = 1024;
-constexpr int kFinishThreads = 1024;
+// Slot of candidate r of a chunk: the first `spec` interleaved for the fast
+// path's lane-contiguous, coalesced loads (pair p = r / 2 at 16-byte position
+// (p % (E/2)) (spec / E) + p / (E/2)), the rest in order.
+__device__ __forceinline__ int slot_of(int r, int spec, int e_log2, int tpc_log2) {
+  if (r >= spec) return r;
+  const int p = r >> 1, ph = (1 << (e_log2 - 1)) - 1;
+  return 2 * (((p & ph) << tpc_log2) + (p >> (e_log2 - 1))) + (r & 1);
+}
 
-// KA: threshold estimate and list reset, one workgroup per row.
-__global__ __launch_bounds__(kStateThreads) void topk_threshold_kernel(
+// First key of sample block u of a row sampled over [0, span): NS / 256
+// blocks of 256 consecutive keys, consecutive when span <= NS, else spread
+// evenly over [0, span).
+template <int NS>
+__device__ __forceinline__ int sample_block_base(int u, int span) {
+  constexpr int NB = NS / kSampleBlock;
+  return span > NS ? (int)((uint32_t)(u * (span - kSampleBlock)) / (uint32_t)(NB - 1))
+                   : u * kSampleBlock;
+}
+// Sampled keys below n (sampling over [0, span)).
+template <int NS>
+__device__ __forceinline__ int sample_valid(int n, int span) {
+  constexpr int NB = NS / kSampleBlock;
+  const int m = min(n, span);
+  int v = 0;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) v += min(max(m - sample_block_base<NS>(u, span), 0), kSampleBlock);
+  return v;
+}
+
+// K1.  U keys per lane (lane t owns keys jl = c CH + U t + [0, U)).
+template <int U, int NS, bool VEC>
+__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, MultiWs m) {
-  constexpr int NT = kStateThreads;
+    int span, int k, int nch_ws, int cap, int spec, int e_log2, int tpc_log2, SplitWs w) {
+  constexpr int NT = kChunkThreads;
+  constexpr int CH = U * NT;
+  constexpr int NB = NS / kSampleBlock;        // sample keys per lane
   __shared__ uint32_t h0[kBins], h1[kBins];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t misc[4];
-  __shared__ uint32_t sample[kMultiSample];
-  const int row = blockIdx.x, t = threadIdx.x;
-  const int n = row_count(kv_len, row, S, L_cap);
-  uint32_t* st = m.state + row * 4;
-  uint32_t mode = kModeAll, T_lo = 0;
-  if (n > k) {
-    if (k <= kMultiCap) {
-      const float* src = scores + (size_t)row * L_cap;
-      const int cnt = n <= kMultiSample ? n : kMultiSample;
-      constexpr int U = kMultiSample / NT;
-      float v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = u * NT + t;
-        v[u] = i < cnt ? src[n <= kMultiSample ? i : sample_pos<kMultiSample>(i, n)] : 0.0f;
-      }
-      for (int i = t; i < kBins; i += NT) { h0[i] = 0u; h1[i] = 0u; }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = u * NT + t;
-        if (i < cnt) sample[i] = score_key(v[u]);
-      }
-      __syncthreads();
-      radix_lower_bound_pre<NT>([&](int i) { return sample[i]; }, cnt,
-                                (uint32_t)(n <= kMultiSample ? k : sample_rank(k, n, kMultiSample)),
-                                h0, h1, scratch, misc, T_lo);
-      mode = kModeList;
-    } else {
-      mode = kModeExact;
-    }
-  }
-  if (t == 0) { st[0] = T_lo; st[1] = mode; st[2] = 0; st[3] = 0; }
-}
+  __shared__ uint32_t misc[8];
+  __shared__ __attribute__((aligned(16))) float chunk[CH];   // lane t's keys at U t + [0, U)
+  const int c = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+  const float* src = scores + (size_t)row * L_cap;
+  const int jl = c * CH + U * t;
 
-// KB: candidates of one chunk, in index order.  Lane t owns the U
-// consecutive keys j0 + U t + [0, U), so a block scan of the per-lane counts
-// gives every candidate its rank in the chunk.
-template <int U, bool VEC>
-__global__ __launch_bounds__(kChunkThreads) void topk_collect_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int chunk, int chunks, MultiWs m) {
-  __shared__ uint32_t scratch[32];
-  __shared__ uint32_t pool_base;
-  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
-  uint32_t* st = m.state + row * 4;
-  if (st[1] != kModeList) return;
-  const uint32_t T_lo = st[0];
-  const int n = row_count(kv_len, row, S, L_cap);
-  const int j0 = c * chunk, j1 = min(j0 + chunk, n);
-  if (j0 >= j1) return;
-  const float* src = scores + (size_t)row * L_cap + j0 + U * t;
-  const int lim = j1 - j0 - U * t;          // keys of this lane inside the row: min(U, lim)
+  // ---- chunk keys and the sample: every load in flight before kv_len is known
   float v[U];
-  if (VEC && lim >= U) {                    // 16-byte aligned: L_cap % 4 == 0, U % 4 == 0
+  if (VEC && jl + U <= L_cap) {                // rows 16-byte aligned (L_cap % 4 == 0)
 #pragma unroll
-    for (int u4 = 0; u4 < U / 4; ++u4) {
-      const float4 q = reinterpret_cast<const float4*>(src)[u4];
-      v[4 * u4] = q.x; v[4 * u4 + 1] = q.y; v[4 * u4 + 2] = q.z; v[4 * u4 + 3] = q.w;
+    for (int q = 0; q < U / 4; ++q) {
+      const float4 x = reinterpret_cast<const float4*>(src + jl)[q];
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = u < lim ? src[u] : 0.0f;
+    for (int u = 0; u < U; ++u) v[u] = jl + u < L_cap ? src[jl + u] : 0.0f;
   }
-  uint32_t key[U];
-  uint32_t hits = 0, cnt = 0;
+  float sv[NB];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    key[u] = score_key(v[u]);
-    const bool hit = u < lim && key[u] >= T_lo;
-    hits |= (uint32_t)hit << u;
-    cnt += hit ? 1u : 0u;
+  for (int u = 0; u < NB; ++u) {
+    const int p = sample_block_base<NS>(u, span) + t;
+    sv[u] = src[p < span ? p : 0];             // span <= L_cap
   }
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan<kChunkThreads>(cnt, scratch, &total);
-  uint2* dst = m.slots + ((size_t)row * chunks + c) * kSlotCap;
-  uint32_t poff = kNoPool;
-  if (total > (uint32_t)kSlotCap) {
-    if (t == 0) pool_base = atomicAdd(&st[2], total);
-    __syncthreads();
-    poff = pool_base;
-    if (poff + total > (uint32_t)kMultiCap) {      // the row's list is too long
-      if (t == 0) st[3] = 1u;
-      return;
+  for (int i = t; i < kBins; i += NT) { h0[i] = 0u; h1[i] = 0u; }
+  if (t == 0) misc[4] = 0u;
+  const int b = row / S;
+  int n = kv_len[b] - S + row % S + 1;
+  n = max(0, min(n, min(L_cap, gridDim.x * CH)));
+  if (n <= k || c * CH >= n) return;           // K2 handles the row / nothing to list here
+  int sspan = span;
+  int nsv = sample_valid<NS>(n, span);
+  if (nsv < kMinSample && nsv < n) {
+    // a row much shorter than the bound: sample its own length instead
+    sspan = n;
+    nsv = sample_valid<NS>(n, n);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int p = sample_block_base<NS>(u, n) + t;
+      sv[u] = src[p < n ? p : 0];
     }
-    dst = m.pool + (size_t)row * kMultiCap + poff;
   }
+  const int slim = min(n, sspan);
+
+  // ---- sample threshold: two radix levels (key bits [31:21], [20:10]); the
+  // largest sampled key sizes the select kernel's digits
+  uint32_t sk[NB];
+  uint32_t smax = 0u, sok = 0u;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (hits >> u & 1u) dst[pos++] = make_uint2(key[u], (uint32_t)(j0 + U * t + u));
-  if (t == 0) m.meta[(size_t)row * chunks + c] = make_uint2(total, poff);
+  for (int u = 0; u < NB; ++u) {
+    sk[u] = score_key(sv[u]);
+    if (sample_block_base<NS>(u, sspan) + t < slim) {
+      sok |= 1u << u;
+      smax = max(smax, sk[u]);
+    }
+  }
+  smax = wave_inclusive_max_u32(smax);
+  __syncthreads();                             // histograms zeroed
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if ((sok >> u) & 1u) atomicAdd(&h0[sk[u] >> 21], 1u);
+  if (lane_id() == kWave - 1) atomicMax(&misc[4], smax);
+  __syncthreads();
+  uint32_t need = (uint32_t)(nsv == n ? k : sample_rank(k, n, nsv));
+  select_bin<NT>(h0, need, scratch, misc);
+  const uint32_t b0 = misc[0];
+  need -= misc[1];
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (((sok >> u) & 1u) && (sk[u] >> 21) == b0) atomicAdd(&h1[(sk[u] >> 10) & 0x7FFu], 1u);
+  __syncthreads();
+  select_bin<NT>(h1, need, scratch, misc + 2);
+  const uint32_t T_lo = (b0 << 21) | (misc[2] << 10);
+
+  // ---- candidates of the chunk, in index order.  Tested on floats:
+  // x >= f_lo <=> score_key(x) >= T_lo (score_key is order-preserving and
+  // gives -0.0 the key of +0.0).  A threshold inside the -inf bin has a NaN
+  // pattern and no hits; K2 then selects from the whole row.
+  const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
+  uint32_t hits = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) hits |= (uint32_t)(jl + u < n && v[u] >= f_lo) << u;
+  // The lane's keys go to LDS so that the write loop visits its hits only
+  // (a key picked by a per-lane bit index cannot be read from registers).
+  // Each lane reads back only what it wrote itself: no barrier.
+#pragma unroll
+  for (int q = 0; q < U / 4; ++q)
+    reinterpret_cast<float4*>(chunk + U * t)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<NT>((uint32_t)__popc(hits), scratch, &total);
+  if (total <= (uint32_t)cap) {
+    uint2* dst = w.slots + ((size_t)row * nch_ws + c) * cap;
+    for (uint32_t hm = hits; hm; hm &= hm - 1) {
+      const int u = __builtin_ctz(hm);
+      dst[slot_of((int)pos, spec, e_log2, tpc_log2)] =
+          make_uint2(score_key(chunk[U * t + u]), (uint32_t)(jl + u));
+      ++pos;
+    }
+  }
+  if (t == 0) w.meta[(size_t)row * nch_ws + c] = make_uint4(total, T_lo, misc[4], 0u);
 }
 
-// KC: exact selection and ordered emission, one workgroup per row.
-// Dynamic LDS: keys[kMultiCap] | indices[kMultiCap] | select histograms
-// [nh kRelBins] | chunk prefix offsets [chunks + 1] | chunk pool offsets
-// [chunks]; the fallback's sel/tie segments reuse the list area and its
-// histogram the first select histogram.  Up to kPreHistChunks chunks per row
-// there are three select histograms, zeroed while the slot loads are in
-// flight (three barriers per select level instead of five); beyond, one,
-// zeroed per level.
-constexpr int kPreHistChunks = 2048;
-__host__ __device__ inline int finish_hists(int chunks) { return chunks <= kPreHistChunks ? 3 : 1; }
-__host__ inline size_t finish_lds_bytes(int chunks) {
-  return (size_t)(2 * kMultiCap + finish_hists(chunks) * kRelBins + 2 * chunks + 1) * 4;
-}
-static_assert(kMultiCap >= kSegWords, "fallback segments must fit the list area");
-static_assert(kRelBins >= kBins, "the fallback histogram fits a select histogram");
+// K2.  Dynamic LDS: keys[kListCap] | indices[kListCap] | three select
+// histograms [3 kRelBins] | chunk prefix offsets [kMaxSplitChunks + 1].
+// Each select histogram is followed by kWave spare bins: entries that must
+// not count add to their lane's spare bin, so the atomics need no branches.
+constexpr int kHistStride = kRelBins + kWave;
+constexpr size_t kSelLds = (size_t)(2 * kListCap + 3 * kHistStride + kMaxSplitChunks + 1) * 4;
 
-__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
+// Exact k-th largest of the keys held by the lanes (E per lane, valid bits
+// in `vm`), all >= base: relative radix digits of key - base, the first
+// level on the bits below the bit length of `range` (keys beyond base +
+// range share the top bin).  Returns false when the k-th key falls in that
+// shared top bin or the keys number fewer than `need`; else T and take
+// (how many keys equal to T are kept).  hA, hB, hC: zeroed kRelBins each.
+template <int NT, int E>
+__device__ bool select_regs(const uint32_t (&key)[E], uint32_t vm, uint32_t base, uint32_t range,
+                            uint32_t need, uint32_t* hA, uint32_t* hB, uint32_t* hC,
+                            uint32_t* scratch, uint32_t* misc, uint32_t& T, uint32_t& take) {
+  const int top = range ? 32 - __clz(range) : 0;
+  const int shA = top > kRelBits ? top - kRelBits : 0;
+  const uint32_t spare = kRelBins + lane_id();
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint32_t d = min((key[j] - base) >> shA, (uint32_t)(kRelBins - 1));
+    atomicAdd(&hA[((vm >> j) & 1u) ? d : spare], 1u);
+  }
+  __syncthreads();
+  const uint32_t m = select_bin_rel<NT>(hA, need, scratch, misc);
+  const uint32_t bA = misc[0];
+  if (m < need || bA == kRelBins - 1) return false;
+  need -= misc[1];
+  uint32_t prefix = base + (bA << shA);
+  if (shA > 0) {
+    const int shB = shA > kRelBits ? shA - kRelBits : 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool in = ((vm >> j) & 1u) && ((key[j] - base) >> shA) == bA;
+      atomicAdd(&hB[in ? (key[j] - prefix) >> shB : spare], 1u);
+    }
+    __syncthreads();
+    select_bin_rel<NT>(hB, need, scratch, misc + 2);
+    need -= misc[3];
+    prefix += misc[2] << shB;
+    if (shB > 0) {                             // shB <= 8: the last level
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const bool in = ((vm >> j) & 1u) && key[j] >= prefix && key[j] - prefix < (1u << shB);
+        atomicAdd(&hC[in ? key[j] - prefix : spare], 1u);
+      }
+      __syncthreads();
+      select_bin_rel<NT>(hC, need, scratch, misc + 4);
+      need -= misc[5];
+      prefix += misc[4];
+    }
+  }
+  T = prefix;
+  take = need;
+  return true;
+}
+
+template <int E>
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int chunk, int chunks, MultiWs m, int32_t* __restrict__ indices) {
-  constexpr int NT = kFinishThreads;
+    int k, int CH, int nch, int nch_ws, int cap, int spec, int e_log2, int tpc_log2,
+    int mode, SplitWs w, int32_t* __restrict__ indices) {
+  constexpr int NT = kSelThreads;
+  constexpr int P = E / 2;                      // (key, index) pairs per lane, one uint4 each
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t misc[kMiscWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   uint32_t* lkey = dyn;
-  uint32_t* lidx = dyn + kMultiCap;
-  uint32_t* hist = dyn + 2 * kMultiCap;         // [nh * kRelBins]
-  const int nh = finish_hists(chunks);          // grid-uniform
-  uint32_t* pre = hist + nh * kRelBins;         // [chunks + 1]
-  uint32_t* poff = pre + chunks + 1;            // [chunks]
-  Lds s{hist, scratch, misc};
+  uint32_t* lidx = dyn + kListCap;
+  uint32_t* hA = dyn + 2 * kListCap;
+  uint32_t* hB = hA + kHistStride;
+  uint32_t* hC = hB + kHistStride;
+  uint32_t* pre = hC + kHistStride;             // [kMaxSplitChunks + 1]
   const int row = blockIdx.x, t = threadIdx.x;
-  // With at most kSpecSlots slots per row, every slot is loaded first, before
-  // the state and the counts are known: slot positions are fixed, so these
-  // loads overlap the count scan (slots past a chunk's count are ignored).
-  constexpr int SG = kSpecSlots / NT;
-  const bool spec = chunks * kSlotCap <= kSpecSlots;      // grid-uniform
-  const uint2* slots = m.slots + (size_t)row * chunks * kSlotCap;
-  uint2 se[SG];
-  if (spec) {
-#pragma unroll
-    for (int g = 0; g < SG; ++g) {
-      const int i = g * NT + t;
-      if (i < chunks * kSlotCap) se[g] = slots[i];
-    }
-  }
-  if (nh == 3) {                                // ordered before the select by the scan's barrier
-    uint4* h4 = reinterpret_cast<uint4*>(hist);
-    for (int i = t; i < 3 * kRelBins / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  const int n = row_count(kv_len, row, S, L_cap);
   int32_t* out = indices + (size_t)row * k;
-  const uint32_t* st = m.state + row * 4;
-  const uint32_t mode = st[1];
-  if (mode == kModeAll) { write_all<NT>(out, n, k); return; }
   const float* src = scores + (size_t)row * L_cap;
-  if (mode == kModeList && st[3] == 0u) {
-    // candidate key span; whether any chunk listed into the pool (both
-    // ordered by the scan's barrier)
-    if (t == 0) { misc[11] = 0; misc[12] = 0; }
-    // chunk counts -> prefix offsets (lane t sums chunks [cpt t, cpt (t+1)))
-    const int nch = (n + chunk - 1) / chunk;
-    const int cpt = (nch + NT - 1) / NT;
-    const int c0 = min(t * cpt, nch), c1 = min(c0 + cpt, nch);
-    const uint2* meta = m.meta + (size_t)row * chunks;
-    uint32_t local = 0;
-    for (int c = c0; c < c1; ++c) local += meta[c].x;
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<NT>(local, scratch, &total);
-    for (int c = c0; c < c1; ++c) {
-      const uint2 mc = meta[c];
-      pre[c] = run;
-      poff[c] = mc.y;
-      run += mc.x;
-      if (mc.y != kNoPool) misc[12] = 1u;
-    }
-    if (t == 0) pre[nch] = total;
-    __syncthreads();
-    if (total >= (uint32_t)k && total <= (uint32_t)kMultiCap) {
-      const uint2* pool = m.pool + (size_t)row * kMultiCap;
-      const uint32_t T_lo = st[0];
-      uint32_t span = 0;                     // largest key - T_lo of this lane
-      if (spec) {
-        // slot r of chunk c goes to list entry pre[c] + r
+  const uint4* meta = w.meta + (size_t)row * nch_ws;
+  const uint2* slots = w.slots + (size_t)row * nch_ws * cap;
+  // mode 0: fast path first (lane t owns chunk c's entries E u + [0, E); the
+  // host guarantees nch * spec <= NT * E), 1: general path, 2: exact only
+  const bool fast = mode == 0;
+  const bool exact_only = mode == 2;
+  const int c = t >> tpc_log2, u = t & ((1 << tpc_log2) - 1);
+
+  // ---- one memory round: the lane's entries, its chunk's record, chunk 0's
+  // record (T_lo and the largest sampled key of the row), kv_len
+  uint4 ent[P];
+  uint4 mine = make_uint4(0u, 0u, 0u, 0u), m0 = mine;
+  if (fast && c < nch) {
+    mine = meta[c];
+    const uint4* cs = reinterpret_cast<const uint4*>(slots + (size_t)c * cap);
 #pragma unroll
-        for (int g = 0; g < SG; ++g) {
-          const int i = g * NT + t;
-          const int c = i / kSlotCap, r = i % kSlotCap;
-          if (c < nch && poff[c] == kNoPool && (uint32_t)r < pre[c + 1] - pre[c]) {
-            lkey[pre[c] + r] = se[g].x;
-            lidx[pre[c] + r] = se[g].y;
-            span = max(span, se[g].x - T_lo);
-          }
-        }
+    for (int q = 0; q < P; ++q) ent[q] = cs[(q << tpc_log2) + u];
+  }
+  if (!exact_only && nch > 0) m0 = meta[0];
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(hA);
+    static_assert(kHistStride % 4 == 0, "histograms zeroed in 16-byte stores");
+    for (int i = t; i < 3 * kHistStride / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (t == 0) { misc[8] = 0u; misc[9] = 0u; }
+  const int b = row / S;
+  int n = kv_len[b] - S + row % S + 1;
+  n = max(0, min(n, min(L_cap, nch * CH)));
+  if (n <= k) { write_all<NT>(out, n, k); return; }
+  const int nch_row = (n + CH - 1) / CH;
+  const uint32_t T_lo = m0.y;
+  __syncthreads();                              // histograms and flags zeroed
+
+  if (fast) {
+    const uint32_t cnt = c < nch_row ? mine.x : 0u;
+    const int r0 = E * u;
+    uint32_t key[E], vm = 0u;
+#pragma unroll
+    for (int q = 0; q < P; ++q) { key[2 * q] = ent[q].x; key[2 * q + 1] = ent[q].z; }
+    if ((uint32_t)r0 < cnt) vm = cnt - r0 >= (uint32_t)E ? 0xFFFFFFFFu >> (32 - E) : (1u << (cnt - r0)) - 1u;
+    // a chunk beyond its speculative slots (or its capacity) leaves the fast path
+    if (cnt > (uint32_t)spec && u == 0) atomicOr(&misc[8], 1u);
+    const uint32_t range = m0.z > T_lo ? m0.z - T_lo : 0u;
+    uint32_t T = 0, take = 0;
+    // misc[8] is read after the first level's barrier
+    const bool ok = select_regs<NT, E>(key, vm, T_lo, range, (uint32_t)k, hA, hB, hC, scratch,
+                                       misc, T, take) && misc[8] == 0u;
+    if (ok) {
+      // ---- ordered emission: entries are in index order across lanes
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if ((vm >> j) & 1u) { gt += key[j] > T ? 1u : 0u; eq += key[j] == T ? 1u : 0u; }
+      uint32_t total;
+      const uint32_t before = block_exclusive_scan<NT>(gt | (eq << 16), scratch, &total);
+      uint32_t g = before & 0xFFFFu, e = before >> 16;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const bool v = (vm >> j) & 1u;
+        const bool above = v && key[j] > T, tie = v && key[j] == T;
+        const uint32_t slot = g + (e < take ? e : take);
+        if (above || (tie && e < take)) out[slot] = (int32_t)((j & 1) ? ent[j >> 1].w : ent[j >> 1].y);
+        g += above ? 1u : 0u;
+        e += tie ? 1u : 0u;
       }
-      if (!spec || misc[12] != 0u) {
-        // gather in index order: entry i belongs to the chunk c with
-        // pre[c] <= i < pre[c + 1] (only pooled chunks' entries when the
-        // slots are already placed)
-        constexpr int G = kMultiCap / NT;    // entries per lane; all loads in flight first
-        uint2 e[G];
-        uint32_t want = 0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const int i = g * NT + t;
-          if (i < (int)total) {
-            int lo = 0, hi = nch - 1;
-            while (lo < hi) {
-              const int mid = (lo + hi + 1) >> 1;
-              if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
-            }
-            const uint32_t r = (uint32_t)i - pre[lo];
-            if (!spec || poff[lo] != kNoPool) {
-              e[g] = poff[lo] == kNoPool ? slots[(size_t)lo * kSlotCap + r] : pool[poff[lo] + r];
-              want |= 1u << g;
-            }
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const int i = g * NT + t;
-          if (want >> g & 1u) {
-            lkey[i] = e[g].x;
-            lidx[i] = e[g].y;
-            span = max(span, e[g].x - T_lo);
-          }
-        }
-      }
-      span = wave_inclusive_max_u32(span);
-      if (lane_id() == kWave - 1) atomicMax(&misc[11], span);
-      __syncthreads();
-      uint32_t T, take;
-      if (nh == 3)
-        radix_select_rel_pre<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
-                                 misc[11], hist, scratch, misc + 4, T, take);
-      else
-        radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)total, (uint32_t)k, T_lo,
-                             misc[11], hist, scratch, misc, T, take);
-      emit_ordered<NT>(lkey, lidx, (int)total, T, take, out, scratch);
       return;
     }
+    __syncthreads();                            // misc, scratch and histograms are reused below
   }
+
+  if (!exact_only) {
+    // ---- general path: chunk counts -> prefix offsets, the list gathered
+    // into LDS in index order (chunks past the row's end were not written by
+    // this call and count 0)
+    constexpr int CPT = kMaxSplitChunks / NT;
+    uint32_t cl[CPT], local = 0, over = 0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int ci = CPT * t + q;
+      cl[q] = ci < nch_row ? meta[ci].x : 0u;
+      local += cl[q];
+      over |= cl[q] > (uint32_t)cap ? 1u : 0u;
+    }
+    if (t == 0) { misc[10] = 0u; misc[11] = 0u; }
+    uint32_t m;
+    uint32_t run = block_exclusive_scan<NT>(local, scratch, &m);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int ci = CPT * t + q;
+      if (ci < nch_row) pre[ci] = run;
+      run += cl[q];
+    }
+    if (t == 0) pre[nch_row] = m;
+    if (over) misc[10] = 1u;
+    __syncthreads();
+    if (misc[10] == 0u && m >= (uint32_t)k && m <= (uint32_t)kListCap) {
+      constexpr int G = kListCap / NT;           // entries per lane; all loads in flight first
+      uint2 x[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = g * NT + t;
+        if (i < (int)m) {
+          int lo = 0, hi = nch_row - 1;          // chunk of entry i: pre[lo] <= i < pre[lo + 1]
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+          }
+          x[g] = slots[(size_t)lo * cap + slot_of(i - (int)pre[lo], spec, e_log2, tpc_log2)];
+        }
+      }
+      uint32_t kmax = 0u;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = g * NT + t;
+        if (i < (int)m) {
+          lkey[i] = x[g].x;
+          lidx[i] = x[g].y;
+          kmax = max(kmax, x[g].x);
+        }
+      }
+      kmax = wave_inclusive_max_u32(kmax);
+      if (lane_id() == kWave - 1) atomicMax(&misc[11], kmax);
+      __syncthreads();
+      uint32_t T, take;
+      radix_select_rel<NT>([&](int i) { return lkey[i]; }, (int)m, (uint32_t)k, T_lo,
+                           misc[11] - T_lo, hA, scratch, misc, T, take);
+      emit_ordered<NT>(lkey, lidx, (int)m, T, take, out, scratch);
+      return;
+    }
+    __syncthreads();                            // misc and the list area are reused below
+  }
+  Lds s{hA, scratch, misc};
   select_exact_row<NT>([&](int j) { return score_key(src[j]); }, n, k, dyn, dyn + kSegWords,
                        out, s);
 }
@@ -1100,39 +1231,102 @@ using StreamPlan = StreamCfg<kStreamThreads, kRowCap>;
 }  // namespace
 
 TopkPlan plan_topk(int B, int S, int L_cap, int k) {
-  (void)k;
   TopkPlan p{};
   p.rows = B * S;
   const long long rows = p.rows;
   if (rows >= 128) {
     p.kind = kPlanStream;
-  } else if (L_cap <= kResKeys) {
+    return p;
+  }
+  if (L_cap <= kResKeys) {
     p.kind = kPlanResident;
+    return p;
+  }
+  p.kind = kPlanSplit;
+  // About one chunk workgroup per CU over all rows, 1024..8192 keys each
+  // (8192-key chunks keep L_cap <= 2^24 within kMaxSplitChunks per row).
+  const long long want = (rows * L_cap + 255) / 256;
+  int ch = 1024;
+  while (ch < want && ch < 8192) ch *= 2;
+  p.chunk = ch;
+  p.chunks = (L_cap + ch - 1) / ch;
+  p.sample = L_cap <= 65536 ? 2048 : 4096;
+  p.exact_only = k > kListCap ? 1 : 0;
+  // Expected candidates per chunk of a full row: the sample threshold sits
+  // at sample rank r = ceil(1.2 e + 4 sqrt(e)) + 8, e = k * sample / L_cap.
+  double per_chunk;
+  if (L_cap <= p.sample) {
+    per_chunk = (double)ch * k / L_cap;
   } else {
-    p.kind = kPlanMulti;
+    const double e = (double)k * p.sample / L_cap;
+    double r = std::ceil(1.2 * e + 4.0 * std::sqrt(e)) + 8.0;
+    if (r > p.sample) r = p.sample;
+    per_chunk = (double)ch * r / p.sample;
   }
-  if (p.kind == kPlanMulti) {
-    // ~1024 chunk workgroups in all, at most 8 keys per thread each.
-    long long want = ((long long)L_cap * rows + 1023) / 1024;
-    int ch = 256;
-    while (ch < want && ch < kChunkKeysPerThread * kChunkThreads) ch *= 2;
-    p.chunk = ch;
-    p.chunks = (L_cap + ch - 1) / ch;
-    if (p.chunks > kMaxChunks) p.chunks = kMaxChunks;     // unreachable for L_cap <= 2^24
-    p.ws_bytes = multi_ws_bytes(p.rows, p.chunks);
+  // Slots: a whole chunk's worth while that stays within 256 MiB (no chunk
+  // can overflow), else four times the expectation (an overflowing chunk
+  // sends its row to the exact selection over the whole row).
+  const size_t full = (size_t)rows * p.chunks * ch * sizeof(uint2);
+  if (full <= ((size_t)256 << 20)) {
+    p.cap = ch;
+  } else {
+    int cap = (int)((4.0 * per_chunk + 64.0 + 63.0) / 64.0) * 64;
+    p.cap = cap < ch ? cap : ch;
   }
+  // Speculative slots per chunk: a power of two >= 1.5 times the expectation,
+  // E = spec * chunks / kSelThreads entries per lane (8, 16 or 32; a lane's
+  // entries lie in one chunk).  Beyond kSpecMax entries per row there is no
+  // fast path (spec = 0).
+  int spec = 32;
+  while (spec < 1.5 * per_chunk + 32.0 && spec < p.cap) spec *= 2;
+  if (spec > p.cap) spec = p.cap;
+  int e = 8;
+  while ((long long)e * kSelThreads < (long long)spec * p.chunks && e < 32) e *= 2;
+  if ((long long)spec * p.chunks > (long long)e * kSelThreads || spec < e) spec = 0;
+  p.spec = spec;
+  p.entries = e;
+  p.ws_bytes = (size_t)p.rows * p.chunks * (sizeof(uint4) + (size_t)p.cap * sizeof(uint2));
   return p;
 }
 
+namespace {
+int ilog2(int x) { int l = 0; while ((1 << (l + 1)) <= x) ++l; return l; }
+
+template <int U, int NS>
+void launch_chunk(bool vec, dim3 grid, hipStream_t st, const float* scores, const int32_t* kv_len,
+                  int S, int L_cap, int span, int k, int nch_ws, int cap, int spec, int el,
+                  int tl, SplitWs w) {
+  if (vec)
+    hipLaunchKernelGGL((topk_chunk_kernel<U, NS, true>), grid, dim3(kChunkThreads), 0, st, scores,
+                       kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w);
+  else
+    hipLaunchKernelGGL((topk_chunk_kernel<U, NS, false>), grid, dim3(kChunkThreads), 0, st, scores,
+                       kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w);
+}
+template <int NS>
+void launch_chunk_ns(int U, bool vec, dim3 grid, hipStream_t st, const float* scores,
+                     const int32_t* kv_len, int S, int L_cap, int span, int k, int nch_ws, int cap,
+                     int spec, int el, int tl, SplitWs w) {
+  switch (U) {
+    case 4: launch_chunk<4, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
+    case 8: launch_chunk<8, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
+    case 16: launch_chunk<16, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
+    default: launch_chunk<32, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
+  }
+}
+}  // namespace
+
 void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, int S,
-                 int L_cap, int k, int32_t* indices, void* ws, hipStream_t st) {
+                 int L_cap, int max_kv_len, int k, int32_t* indices, void* ws, hipStream_t st) {
   if (p.rows == 0) return;
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
     opt_in_lds(topk_resident_kernel<kResThreads>, kResLds);
     opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap, true>, StreamPlan::kLds);
     opt_in_lds(topk_stream_kernel<kStreamThreads, kRowCap, false>, StreamPlan::kLds);
-    opt_in_lds(topk_finish_kernel, finish_lds_bytes(kMaxChunks));
+    opt_in_lds(topk_select_kernel<8>, kSelLds);
+    opt_in_lds(topk_select_kernel<16>, kSelLds);
+    opt_in_lds(topk_select_kernel<32>, kSelLds);
     lds_opt_in = true;
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
@@ -1152,35 +1346,40 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
                          scores, kv_len, S, L_cap, k, vec4, indices);
       return;
     default: {
-      MultiWs m = carve(ws, p.rows, p.chunks);
-      hipLaunchKernelGGL(topk_threshold_kernel, dim3(p.rows), dim3(kStateThreads), 0, st, scores,
-                         kv_len, S, L_cap, k, m);
-      const dim3 cg(p.chunks, p.rows);
-      switch (p.chunk / kChunkThreads) {
-        case 1:
-          hipLaunchKernelGGL((topk_collect_kernel<1, false>), cg, dim3(kChunkThreads), 0, st,
-                             scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+      SplitWs w = split_carve(ws, p.rows, p.chunks);
+      // chunks covering the runtime bound; K2 treats rows as at most this long
+      const int nch = (max_kv_len + p.chunk - 1) / p.chunk;
+      // slot interleave of the fast path (spec = 0: none; the general path
+      // then reads every slot in order)
+      const int spec = p.spec > 0 ? p.spec : 1 << 30;
+      const int el = p.spec > 0 ? ilog2(p.entries) : 1;
+      const int tl = p.spec > 0 ? ilog2(p.spec / p.entries) : 0;
+      if (nch > 0 && !p.exact_only) {
+        const dim3 grid(nch, p.rows);
+        if (p.sample == 2048)
+          launch_chunk_ns<2048>(p.chunk / kChunkThreads, vec4, grid, st, scores, kv_len, S, L_cap,
+                                max_kv_len, k, p.chunks, p.cap, spec, el, tl, w);
+        else
+          launch_chunk_ns<4096>(p.chunk / kChunkThreads, vec4, grid, st, scores, kv_len, S, L_cap,
+                                max_kv_len, k, p.chunks, p.cap, spec, el, tl, w);
+      }
+      const int ex = p.exact_only ? 2 : (p.spec > 0 ? 0 : 1);
+      switch (p.entries) {
+        case 8:
+          hipLaunchKernelGGL((topk_select_kernel<8>), dim3(p.rows), dim3(kSelThreads), kSelLds, st,
+                             scores, kv_len, S, L_cap, k, p.chunk, nch, p.chunks, p.cap, spec, el,
+                             tl, ex, w, indices);
           break;
-        case 2:
-          hipLaunchKernelGGL((topk_collect_kernel<2, false>), cg, dim3(kChunkThreads), 0, st,
-                             scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
-          break;
-        case 4:
-          if (vec4) hipLaunchKernelGGL((topk_collect_kernel<4, true>), cg, dim3(kChunkThreads), 0,
-                                       st, scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
-          else hipLaunchKernelGGL((topk_collect_kernel<4, false>), cg, dim3(kChunkThreads), 0, st,
-                                  scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
+        case 16:
+          hipLaunchKernelGGL((topk_select_kernel<16>), dim3(p.rows), dim3(kSelThreads), kSelLds, st,
+                             scores, kv_len, S, L_cap, k, p.chunk, nch, p.chunks, p.cap, spec, el,
+                             tl, ex, w, indices);
           break;
         default:
-          if (vec4) hipLaunchKernelGGL((topk_collect_kernel<8, true>), cg, dim3(kChunkThreads), 0,
-                                       st, scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
-          else hipLaunchKernelGGL((topk_collect_kernel<8, false>), cg, dim3(kChunkThreads), 0, st,
-                                  scores, kv_len, S, L_cap, p.chunk, p.chunks, m);
-          break;
+          hipLaunchKernelGGL((topk_select_kernel<32>), dim3(p.rows), dim3(kSelThreads), kSelLds, st,
+                             scores, kv_len, S, L_cap, k, p.chunk, nch, p.chunks, p.cap, spec, el,
+                             tl, ex, w, indices);
       }
-      hipLaunchKernelGGL(topk_finish_kernel, dim3(p.rows), dim3(kFinishThreads),
-                         finish_lds_bytes(p.chunks), st, scores, kv_len, S, L_cap, k, p.chunk,
-                         p.chunks, m, indices);
     }
   }
 }

@@ -115,7 +115,7 @@ def test_topk_prefill_128k_shape(dsa):
 
 def test_topk_k_beyond_list_capacity_uses_exact_fallback(dsa):
     r = rng(14)
-    # row plan (many rows) and multi plan (few long rows), k above the list capacity
+    # streaming plan (many rows) and split plan (few long rows), k above the list capacity
     _check(dsa, integer_scores(r, (1, 130, 12000), -50, 50), [12000], 5000, what="row k>cap")
     _check(dsa, torch.from_numpy(r.standard_normal((1, 4, 40000)).astype(np.float32)), [40000],
            9000, what="multi k>cap")
@@ -127,10 +127,12 @@ def _sample_positions(n, sample=8192, block=256):
                            for b in range(nb)])
 
 
-@pytest.mark.parametrize("B,S,L,k,sample", [(1, 8, 30000, 2048, 2048),     # LDS-resident rows
-                                            (1, 8, 40000, 2048, 4096),     # multi plan
-                                            (1, 130, 40000, 2048, 8192)])  # streaming rows
-def test_topk_sample_heavy_rows_use_exact_fallback(dsa, B, S, L, k, sample):
+@pytest.mark.parametrize("B,S,L,k,sample,over", [
+    (1, 8, 30000, 2048, 2048, "row"),        # LDS-resident rows: sample over each row
+    (1, 8, 40000, 2048, 2048, "bound"),      # split plan: sample over the bound max_kv_len
+    (1, 8, 300000, 2048, 4096, "bound"),     # split plan, longer rows: a larger sample
+    (1, 130, 40000, 2048, 8192, "row")])     # streaming rows
+def test_topk_sample_heavy_rows_use_exact_fallback(dsa, B, S, L, k, sample, over):
     # White-box: large scores exactly at the keys the threshold sample reads,
     # so fewer than k keys reach the estimated threshold and the exact
     # fallback must produce the result.
@@ -138,18 +140,44 @@ def test_topk_sample_heavy_rows_use_exact_fallback(dsa, B, S, L, k, sample):
     sc = r.integers(-100, 100, size=(B, S, L)).astype(np.float32)
     for s in range(S):
         n = L - S + s + 1
-        pos = _sample_positions(n, sample)
+        pos = _sample_positions(n if over == "row" else L, sample)
+        pos = pos[pos < n]
         sc[0, s, pos] = 1000.0 + r.integers(0, 50, size=pos.shape[0])
-    _check(dsa, torch.from_numpy(sc), [L], k, what=f"sample-heavy/{sample}")
+    _check(dsa, torch.from_numpy(sc), [L], k, what=f"sample-heavy/{sample}/{over}")
+
+
+def test_topk_split_rows_far_below_the_bound_resample(dsa):
+    # Rows much shorter than max_kv_len: the sample spread over the bound
+    # leaves them too few valid keys, so their chunk workgroups sample again
+    # over the row itself (and a row at most k long just lists every key).
+    r = rng(21)
+    L, k = 262144, 2048
+    sc = torch.from_numpy(np.round(r.standard_normal((4, 2, L)) * 2100).astype(np.float32))
+    _check(dsa, sc, [L, 3000, 70001, 2049], k, what="split, short rows under a long bound")
+
+
+def test_topk_split_chunk_overflow_falls_back_to_exact(dsa):
+    # 100 rows of 400000 keys: whole-chunk slots would exceed the workspace
+    # budget, so chunks get a few times their expected candidate count.  With
+    # the top keys packed into each row's most recent 12000 positions those
+    # chunks overflow and the row is selected exactly from the whole row.
+    r = rng(22)
+    B, S, L, k = 1, 100, 400000, 2048
+    sc = r.standard_normal((B, S, L)).astype(np.float32)
+    for s in range(S):
+        n = L - S + s + 1
+        sc[0, s, n - 12000:n] += 6.0
+    _check(dsa, torch.from_numpy(sc), [L], k, rows=[(0, 0), (0, 57), (0, 99)],
+           what="split, overflowing chunks")
 
 
 @pytest.mark.parametrize("B,S,L,k,span", [(1, 8, 262144, 2048, 3000),    # last chunks overflow their slots
                                           (2, 4, 100000, 1500, 40000)])  # spread over many chunks
 def test_topk_recency_clustered_candidates(dsa, B, S, L, k, span):
     # Scores with the top-k concentrated in the most recent `span` positions
-    # of each row: in the multi plan the chunks there hold far more
-    # candidates than their own slots, so their lists go to the row's pool
-    # while the older chunks keep theirs; the merged list must stay ordered.
+    # of each row: in the split plan the chunks there hold more candidates
+    # than the select kernel loads up front, so the row takes the general
+    # path that gathers every chunk's list in order.
     r = rng(16)
     sc = r.standard_normal((B, S, L)).astype(np.float32)
     kv = [L] * B
@@ -204,8 +232,9 @@ def test_topk_streaming_rows_unaligned_and_ragged(dsa):
 
 
 def test_topk_very_long_rows(dsa):
-    # Few rows of 4.5M keys: more than 2048 chunks per row, where the finish
-    # kernel keeps a single select histogram and zeroes it per level.
+    # Few rows of 4.5M keys: more chunks per row than the select kernel's
+    # registers hold, so it takes the general path (and, with more candidates
+    # than its LDS list holds, the exact selection over the whole row).
     r = rng(19)
     sc = torch.from_numpy(r.standard_normal((1, 2, 4_500_000)).astype(np.float32))
     _check(dsa, sc, [4_500_000], 2048, what="4.5M keys")
