@@ -7,7 +7,6 @@ in the HIP kernels of libdsa.so.  There is no fallback: if the library is not
 built, importing this module raises.
 """
 import ctypes
-import math
 import os
 
 import torch
@@ -224,10 +223,6 @@ def dsa_attention_prefill(q, k_cache, v_cache, indices, kv_len, out, k_scale=Non
     return _attention(LIB.dsa_attention_prefill, False, q, k_cache, v_cache, indices, kv_len,
                       out, k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream,
                       aux_k, aux_v)
-
-
-def default_softmax_scale(D):
-    return 1.0 / math.sqrt(D)
 
 
 # ------------------------------------------------------------------ cache append
