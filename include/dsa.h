@@ -170,6 +170,22 @@ dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of dsa_attention_decode, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * function and kernels as dsa_attention_decode; the split partials go to a
+ * built-in scratch array of 16 MiB per GPU (held by the library for the life
+ * of the process) instead of a caller workspace.  The call allocates and
+ * frees nothing.  Calls whose partials (dsa_attention_workspace_bytes(args,
+ * 1)) exceed 16 MiB are rejected with DSA_ERR_WORKSPACE_TOO_SMALL before any
+ * launch.  Every call on a GPU shares that GPU's scratch: calls that overlap
+ * in time on one GPU (several streams or threads) race and must be ordered
+ * by the caller.  The scratch holds no state between calls (every partial
+ * is written before it is read).
+ */
+dsa_status dsa_attention_decode_noalloc(const dsa_attention_args* args, void* stream);
+
+/*
  * KV-cache append (ORT PR #33997, file table: cache writes precede the
  * attention kernels; ORT PR #33802, Summary item 1: an INT8 KV cache with one
  * FP32 scale per token per KV head).  Writes the S new tokens of every

@@ -27,6 +27,7 @@
 // The 4 waves' (max, sum, O) states merge in LDS; with several key splits
 // the workgroup writes an unnormalised partial and attn_merge_kernel
 // combines the splits in a fixed order (deterministic).
+#include <mutex>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -813,6 +814,33 @@ void plan_attention(AttnLaunch& a, bool decode) {
   }
   a.nsplit = (int)ns;
   a.keys_per_split = (int)kps;
+}
+
+// ---------------------------------------------------------------- built-in scratch
+// Split partials of the allocation-free decode entry point: a file-scope
+// device array (each GPU the library runs on holds its own copy, at its own
+// address, until the process ends).  Host code never passes the array's
+// name to a kernel: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+float* attention_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) { *err = e; return nullptr; }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) { *err = e != hipSuccess ? e : hipErrorInvalidSymbol; return nullptr; }
+    addr[dev] = p;
+  }
+  *err = hipSuccess;
+  return static_cast<float*>(addr[dev]);
 }
 
 size_t attention_partials_bytes(const AttnLaunch& a) {

@@ -232,6 +232,25 @@ dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace
   return run_attention(args, workspace, workspace_bytes, stream, false);
 }
 
+dsa_status dsa_attention_decode_noalloc(const dsa_attention_args* args, void* stream) {
+  CHECK(validate_attention(args));
+  if ((long long)args->B * args->S == 0) return ok();
+  dsa::AttnLaunch l = make_attn(args, true);
+  const size_t need = dsa::attention_partials_bytes(l);
+  if (need > dsa::kAttnScratchBytes)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "decode partials need %zu bytes; the built-in scratch holds %zu", need,
+                dsa::kAttnScratchBytes);
+  if (need > 0) {
+    hipError_t e = hipSuccess;
+    l.part = dsa::attention_scratch(&e);
+    if (!l.part) return fail(DSA_ERR_HIP, "built-in scratch address: %s", hipGetErrorString(e));
+  }
+  (void)hipGetLastError();
+  dsa::launch_attention(l, (hipStream_t)stream);
+  return hip_result("dsa_attention_decode_noalloc");
+}
+
 dsa_status dsa_cache_append(const dsa_cache_append_args* a, void* stream) {
   if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->B < 0 || a->S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", a->B, a->S);

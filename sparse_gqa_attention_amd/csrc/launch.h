@@ -76,6 +76,10 @@ struct AttnLaunch {
 void plan_attention(AttnLaunch& a, bool decode);
 size_t attention_partials_bytes(const AttnLaunch& a);
 void launch_attention(const AttnLaunch& a, hipStream_t st);
+// Built-in scratch of the allocation-free decode entry point: its size, and
+// the current device's copy (device address; null with *err set on failure).
+constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+float* attention_scratch(hipError_t* err);
 
 // ---------------------------------------------------------------- cache append
 struct CacheAppendLaunch {

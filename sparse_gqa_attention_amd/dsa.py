@@ -21,8 +21,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
 
 EXPORTS = ("dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "dsa_attention_workspace_bytes",
-           "dsa_attention_decode", "dsa_attention_prefill", "dsa_cache_append",
-           "dsa_rmsnorm_rope")
+           "dsa_attention_decode", "dsa_attention_prefill", "dsa_attention_decode_noalloc",
+           "dsa_cache_append", "dsa_rmsnorm_rope")
 
 
 class DsaError(RuntimeError):
@@ -93,6 +93,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = i32
         f.argtypes = [ctypes.POINTER(AttentionArgs), vp, sz, vp]
+    lib.dsa_attention_decode_noalloc.restype = i32
+    lib.dsa_attention_decode_noalloc.argtypes = [ctypes.POINTER(AttentionArgs), vp]
     lib.dsa_rmsnorm_rope.restype = i32
     lib.dsa_rmsnorm_rope.argtypes = [ctypes.POINTER(RopeArgs), vp]
     lib.dsa_cache_append.restype = i32
@@ -223,6 +225,21 @@ def dsa_attention_prefill(q, k_cache, v_cache, indices, kv_len, out, k_scale=Non
     return _attention(LIB.dsa_attention_prefill, False, q, k_cache, v_cache, indices, kv_len,
                       out, k_scale, v_scale, softmax_scale, workspace, max_kv_len, stream,
                       aux_k, aux_v)
+
+
+def dsa_attention_decode_noalloc(q, k_cache, v_cache, indices, kv_len, out, k_scale=None,
+                                 v_scale=None, softmax_scale=0.0, max_kv_len=None, stream=None,
+                                 aux_k=None, aux_v=None):
+    """Decode form with the library's built-in scratch instead of a workspace; see include/dsa.h."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (indices, "indices"),
+                 (kv_len, "kv_len"), (out, "out")):
+        _gpu(t, n)
+    if aux_k is not None:
+        _gpu(aux_k, "aux_k"), _gpu(aux_v, "aux_v")
+    a = attention_args(q, k_cache, v_cache, indices, kv_len, out, k_scale, v_scale,
+                       softmax_scale, max_kv_len, aux_k, aux_v)
+    _check(LIB.dsa_attention_decode_noalloc(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 # ------------------------------------------------------------------ cache append

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_and_library_agree(dsa):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(LIBPATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -148,6 +148,21 @@ def test_attention_validation(dsa):
     assert L.dsa_attention_workspace_bytes(ctypes.byref(a), 0) == 0   # prefill: no workspace
     assert call(a, wsb=need - 1) == _status("WS")
     assert call(a, ws=None, wsb=need) == _status("INVALID")
+    assert call(_attn(dsa, B=0, q=None, out=None)) == 0
+
+
+def test_noalloc_attention_rejects_before_any_launch(dsa):
+    # The allocation-free decode validates like dsa_attention_decode and
+    # refuses partials beyond its built-in 16 MiB scratch, all on the host.
+    L = dsa.LIB
+    call = lambda a: L.dsa_attention_decode_noalloc(ctypes.byref(a), None)
+    assert call(_attn(dsa, D=96)) == _status("UNSUPPORTED")
+    assert call(_attn(dsa, q=MIS)) == _status("MISALIGNED")
+    big = _attn(dsa, B=6, S=8, H_q=16, H_kv=1, kv_dtype=3, k_scale=A16, v_scale=A16, k=65536,
+                L_cap=65536, max_kv_len=65536)          # 48 rows x 16 heads x 64 splits
+    assert L.dsa_attention_workspace_bytes(ctypes.byref(big), 1) > 16 << 20
+    assert call(big) == _status("WS")
+    assert "scratch" in dsa.dsa_last_error()
     assert call(_attn(dsa, B=0, q=None, out=None)) == 0
 
 
