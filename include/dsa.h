@@ -163,11 +163,37 @@ typedef struct {
   int32_t aux_len;
 } dsa_attention_args;
 
+/* Workspace bytes dsa_attention_decode (is_decode != 0) or _prefill needs
+ * for these arguments; depends on sizes and dtypes only (the pointers are not
+ * read and may be NULL); 0 when none is needed or the arguments are invalid. */
 size_t dsa_attention_workspace_bytes(const dsa_attention_args* args, int is_decode);
 dsa_status dsa_attention_decode(const dsa_attention_args* args, void* workspace,
                                 size_t workspace_bytes, void* stream);
 dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Launch plans (no device work).  Describes, as one line of "key=value"
+ * words, the kernels, grids and tiling that the call `op` would launch for
+ * these arguments -- the planning the call itself does, so tests and logs
+ * can see which plan runs without a profiler.
+ *   DSA_PLAN_INDEXER:  B, S, L_cap, max_kv_len, D_idx (as dsa_indexer_score)
+ *   DSA_PLAN_TOPK:     B, S, L_cap, max_kv_len, k    (as dsa_topk)
+ *   DSA_PLAN_ATTENTION_DECODE / _PREFILL: `attention` (its pointers are not
+ *                      read and may be NULL)
+ * Arguments an op does not use are ignored.  Writes at most buf_bytes - 1
+ * characters and a NUL to buf (NULL with buf_bytes 0 only measures).
+ * Returns the description's full length, or 0 for invalid arguments, with
+ * dsa_last_error() saying why.  Makes no HIP call.
+ */
+typedef enum {
+  DSA_PLAN_INDEXER = 0,
+  DSA_PLAN_TOPK = 1,
+  DSA_PLAN_ATTENTION_DECODE = 2,
+  DSA_PLAN_ATTENTION_PREFILL = 3
+} dsa_plan_op;
+size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k, int D_idx,
+                         const dsa_attention_args* attention, char* buf, size_t buf_bytes);
 
 /*
  * Allocation-free variant of dsa_attention_decode, for callers that cannot

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "../../include/dsa.h"
@@ -63,7 +64,8 @@ dsa_status hip_result(const char* what) {
 }
 
 // ------------------------------------------------------------------ attention
-dsa_status validate_attention(const dsa_attention_args* a) {
+// Shapes, dtypes and sizes (no pointers).
+dsa_status validate_attention_shape(const dsa_attention_args* a) {
   if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->B < 0 || a->S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", a->B, a->S);
   if (a->k < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 0", a->k);
@@ -96,7 +98,13 @@ dsa_status validate_attention(const dsa_attention_args* a) {
     if (a->aux_len > a->L_cap)
       return fail(DSA_ERR_INVALID_ARGUMENT, "aux_len=%d exceeds L_cap=%d", a->aux_len, a->L_cap);
   }
+  return DSA_OK;
+}
+
+dsa_status validate_attention(const dsa_attention_args* a) {
+  CHECK(validate_attention_shape(a));
   if ((long long)a->B * a->S == 0) return DSA_OK;
+  const int kd = a->kv_dtype;
   if (a->aux_len > 0) {
     CHECK(check_ptr(a->aux_k, "aux_k"));
     CHECK(check_ptr(a->aux_v, "aux_v"));
@@ -149,17 +157,8 @@ dsa_status run_attention(const dsa_attention_args* a, void* ws, size_t ws_bytes,
   return hip_result(decode ? "dsa_attention_decode" : "dsa_attention_prefill");
 }
 
-}  // namespace
-
-extern "C" {
-
-int dsa_abi_version(void) { return DSA_ABI_VERSION; }
-
-const char* dsa_last_error(void) { return g_last_error.c_str(); }
-
-dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* key_state,
-                             dsa_dtype idx_dtype, const int32_t* kv_len, int B, int S, int H_idx,
-                             int D_idx, int L_cap, int max_kv_len, float* scores, void* stream) {
+dsa_status validate_indexer_shape(int idx_dtype, int B, int S, int H_idx, int D_idx, int L_cap,
+                                  int max_kv_len) {
   if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
   if (L_cap < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "L_cap=%d must be >= 1", L_cap);
   if (L_cap > dsa::kIndexerMaxLcap)
@@ -171,6 +170,41 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* 
   if (H_idx < 1 || H_idx > 16) return fail(DSA_ERR_UNSUPPORTED, "H_idx=%d not in [1, 16]", H_idx);
   if (D_idx != 32 && D_idx != 64 && D_idx != 128)
     return fail(DSA_ERR_UNSUPPORTED, "D_idx=%d not in {32, 64, 128}", D_idx);
+  return DSA_OK;
+}
+
+dsa_status validate_topk_shape(int B, int S, int L_cap, int max_kv_len, int k) {
+  if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
+  if (L_cap < 1 || L_cap > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "L_cap=%d not in [1, 2^24]", L_cap);
+  if (k < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
+  if (max_kv_len < 0 || max_kv_len > L_cap)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
+  return DSA_OK;
+}
+
+// Appends printf-formatted text to out.
+void appendf(std::string& out, const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  out += buf;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* key_state,
+                             dsa_dtype idx_dtype, const int32_t* kv_len, int B, int S, int H_idx,
+                             int D_idx, int L_cap, int max_kv_len, float* scores, void* stream) {
+  CHECK(validate_indexer_shape(idx_dtype, B, S, H_idx, D_idx, L_cap, max_kv_len));
   if ((long long)B * S == 0 || max_kv_len == 0) return ok();
   CHECK(check_ptr(q_idx, "q_idx"));
   CHECK(check_ptr(w_idx, "w_idx"));
@@ -193,12 +227,7 @@ size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k) {
 dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, int L_cap,
                     int max_kv_len, int k, int32_t* indices, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  if (B < 0 || S < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d must be >= 0", B, S);
-  if (L_cap < 1 || L_cap > (1 << 24))
-    return fail(DSA_ERR_UNSUPPORTED, "L_cap=%d not in [1, 2^24]", L_cap);
-  if (k < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
-  if (max_kv_len < 0 || max_kv_len > L_cap)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "max_kv_len=%d outside [0, L_cap=%d]", max_kv_len, L_cap);
+  CHECK(validate_topk_shape(B, S, L_cap, max_kv_len, k));
   if ((long long)B * S == 0) return ok();
   CHECK(check_ptr(scores, "scores"));
   CHECK(check_ptr(kv_len, "kv_len"));
@@ -217,7 +246,7 @@ dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, in
 }
 
 size_t dsa_attention_workspace_bytes(const dsa_attention_args* args, int is_decode) {
-  if (validate_attention(args) != DSA_OK) return 0;
+  if (validate_attention_shape(args) != DSA_OK) return 0;     // pointers are not needed
   if ((long long)args->B * args->S == 0) return 0;
   return dsa::attention_partials_bytes(make_attn(args, is_decode != 0));
 }
@@ -230,6 +259,69 @@ dsa_status dsa_attention_decode(const dsa_attention_args* args, void* workspace,
 dsa_status dsa_attention_prefill(const dsa_attention_args* args, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   return run_attention(args, workspace, workspace_bytes, stream, false);
+}
+
+size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k, int D_idx,
+                         const dsa_attention_args* attention, char* buf, size_t buf_bytes) {
+  std::string d;
+  if (op == DSA_PLAN_INDEXER) {
+    if (validate_indexer_shape(DSA_BF16, B, S, 1, D_idx, L_cap, max_kv_len) != DSA_OK) return 0;
+    if ((long long)B * S == 0 || max_kv_len == 0) {
+      d = "op=indexer kernels=none";
+    } else {
+      const dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, max_kv_len);
+      const bool stream = l.prefill || l.stream_decode;
+      appendf(d, "op=indexer kernel=%s grid=%dx%dx%d threads=%d waves=%d token_pairs_per_wave=%d "
+                 "keys_per_buffer=%d keys_per_workgroup=%d",
+              stream ? "indexer_stream_kernel" : "indexer_score_kernel", l.tok_blocks, l.key_blocks,
+              B, 64 * l.waves, l.waves, l.pairs, l.tile, l.keys_per_wg);
+    }
+  } else if (op == DSA_PLAN_TOPK) {
+    if (validate_topk_shape(B, S, L_cap, max_kv_len, k) != DSA_OK) return 0;
+    const dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, k);
+    if (p.rows == 0) {
+      d = "op=topk kernels=none";
+    } else if (p.kind == 0) {
+      appendf(d, "op=topk plan=stream kernel=topk_stream_kernel grid=%d threads=1024 workspace=0",
+              p.rows);
+    } else if (p.kind == 1) {
+      appendf(d, "op=topk plan=resident kernel=topk_resident_kernel grid=%d threads=1024 "
+                 "workspace=0", p.rows);
+    } else {
+      const int nch = (max_kv_len + p.chunk - 1) / p.chunk;
+      appendf(d, "op=topk plan=split kernels=topk_chunk_kernel,topk_select_kernel "
+                 "chunk_grid=%dx%d chunk_threads=256 select_grid=%d select_threads=512 "
+                 "chunk=%d chunks=%d sample=%d slots=%d spec=%d entries=%d mode=%s workspace=%zu",
+              p.exact_only ? 0 : nch, p.rows, p.rows, p.chunk, p.chunks, p.sample, p.cap, p.spec,
+              p.entries, p.exact_only ? "exact" : (p.spec > 0 ? "fast" : "general"), p.ws_bytes);
+    }
+  } else if (op == DSA_PLAN_ATTENTION_DECODE || op == DSA_PLAN_ATTENTION_PREFILL) {
+    if (validate_attention_shape(attention) != DSA_OK) return 0;
+    const bool decode = op == DSA_PLAN_ATTENTION_DECODE;
+    if ((long long)attention->B * attention->S == 0) {
+      d = decode ? "op=attention_decode kernels=none" : "op=attention_prefill kernels=none";
+    } else {
+      const dsa::AttnLaunch l = make_attn(attention, decode);
+      const int rows = l.B * l.S;
+      const int splits = l.nsplit + (l.aux_len > 0 ? 1 : 0);
+      appendf(d, "op=%s kernel=attn_kernel grid=%dx%dx%d threads=256 keys_per_split=%d",
+              decode ? "attention_decode" : "attention_prefill", l.nsplit, l.H_kv, rows,
+              l.keys_per_split);
+      if (l.aux_len > 0) appendf(d, " aux_grid=1x%dx%d", l.H_kv, rows);
+      if (splits > 1) appendf(d, " merge_kernel=attn_merge_kernel merge_grid=%d", rows * l.H_q);
+      appendf(d, " workspace=%zu", dsa::attention_partials_bytes(l));
+    }
+  } else {
+    fail(DSA_ERR_INVALID_ARGUMENT, "op=%d is not a dsa_plan_op", op);
+    return 0;
+  }
+  if (buf && buf_bytes > 0) {
+    const size_t n = d.size() < buf_bytes - 1 ? d.size() : buf_bytes - 1;
+    memcpy(buf, d.data(), n);
+    buf[n] = '\0';
+  }
+  ok();
+  return d.size();
 }
 
 dsa_status dsa_attention_decode_noalloc(const dsa_attention_args* args, void* stream) {

@@ -22,7 +22,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
 EXPORTS = ("dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "dsa_attention_workspace_bytes",
            "dsa_attention_decode", "dsa_attention_prefill", "dsa_attention_decode_noalloc",
-           "dsa_cache_append", "dsa_rmsnorm_rope")
+           "dsa_describe_plan", "dsa_cache_append", "dsa_rmsnorm_rope")
+DSA_PLAN_INDEXER, DSA_PLAN_TOPK, DSA_PLAN_ATTENTION_DECODE, DSA_PLAN_ATTENTION_PREFILL = 0, 1, 2, 3
 
 
 class DsaError(RuntimeError):
@@ -95,6 +96,9 @@ def _load():
         f.argtypes = [ctypes.POINTER(AttentionArgs), vp, sz, vp]
     lib.dsa_attention_decode_noalloc.restype = i32
     lib.dsa_attention_decode_noalloc.argtypes = [ctypes.POINTER(AttentionArgs), vp]
+    lib.dsa_describe_plan.restype = sz
+    lib.dsa_describe_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(AttentionArgs), ctypes.c_char_p, sz]
     lib.dsa_rmsnorm_rope.restype = i32
     lib.dsa_rmsnorm_rope.argtypes = [ctypes.POINTER(RopeArgs), vp]
     lib.dsa_cache_append.restype = i32
@@ -240,6 +244,24 @@ def dsa_attention_decode_noalloc(q, k_cache, v_cache, indices, kv_len, out, k_sc
                        softmax_scale, max_kv_len, aux_k, aux_v)
     _check(LIB.dsa_attention_decode_noalloc(ctypes.byref(a), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ launch plans
+def dsa_describe_plan(op, B=0, S=0, L_cap=0, max_kv_len=None, k=0, D_idx=0, attention=None):
+    """The "key=value" description of the launches `op` would make (no device work)."""
+    mx = L_cap if max_kv_len is None else max_kv_len
+    ap = None if attention is None else ctypes.byref(attention)
+    n = LIB.dsa_describe_plan(op, B, S, L_cap, mx, k, D_idx, ap, None, 0)
+    if n == 0:
+        raise DsaError(1, LIB.dsa_last_error().decode())
+    buf = ctypes.create_string_buffer(n + 1)
+    LIB.dsa_describe_plan(op, B, S, L_cap, mx, k, D_idx, ap, buf, n + 1)
+    return buf.value.decode()
+
+
+def plan_fields(text):
+    """The description as a dict of its key=value words."""
+    return dict(w.split("=", 1) for w in text.split())
 
 
 # ------------------------------------------------------------------ cache append

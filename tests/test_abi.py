@@ -27,15 +27,15 @@ def dsa():
     return m
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_and_library_agree(dsa):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = ctypes.CDLL(LIBPATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -237,3 +237,59 @@ def test_error_text_is_thread_local_and_cleared(dsa):
     assert seen == [""]
     assert L.dsa_topk(None, None, 0, 1, 16, 16, 4, None, None, 0, None) == 0
     assert dsa.dsa_last_error() == ""
+
+
+def test_roofline_probe_library_exports_its_header():
+    import ctypes as C
+    header = os.path.join(ROOT, "include", "dsa_roofline.h")
+    lib = C.CDLL(os.path.join(ROOT, "sparse_gqa_attention_amd", "libdsa_roofline.so"))
+    names = declared_functions(header)
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dsa_roofline.h but not exported"
+    from sparse_gqa_attention_amd import roofline
+    assert sorted(roofline.EXPORTS) == names
+    assert lib.dsa_roofline_read(None, 0, None, None) == 2          # rejected, nothing launched
+    lib.dsa_roofline_mfma_flops.restype = C.c_double
+    assert lib.dsa_roofline_mfma_flops(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2
+
+
+def test_describe_plan_names_the_launches(dsa):
+    d, F = dsa.dsa_describe_plan, dsa.plan_fields
+    # 32K speculative decode: decode indexer, one LDS-resident top-k workgroup
+    # per row, 16 key splits per (row, KV head) and a split merge
+    f = F(d(dsa.DSA_PLAN_INDEXER, 1, 8, 32768, D_idx=64))
+    assert f["kernel"] == "indexer_score_kernel" and f["grid"] == "1x512x1"
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 32768, k=2048))
+    assert f["plan"] == "resident" and f["grid"] == "8" and f["workspace"] == "0"
+    a = _attn(dsa, q=None, k_cache=None, v_cache=None, indices=None, kv_len=None, out=None)
+    f = F(d(dsa.DSA_PLAN_ATTENTION_DECODE, attention=a))
+    assert f["grid"] == "16x2x8" and f["merge_grid"] == "192"
+    assert int(f["workspace"]) == L_attn_ws(dsa, a)
+    f = F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))
+    assert f["grid"] == "1x2x8" and "merge_grid" not in f and f["workspace"] == "0"
+    # 256K decode: the two-kernel split top-k on its fast path
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 262144, k=2048))
+    assert f["plan"] == "split" and f["chunk_grid"] == "32x8" and f["mode"] == "fast"
+    assert int(f["workspace"]) == dsa.dsa_topk_workspace_bytes(1, 8, 262144, 2048)
+    # the runtime bound sizes the chunk grid
+    f = F(d(dsa.DSA_PLAN_TOPK, 4, 8, 262144, max_kv_len=200000, k=2048))
+    assert f["chunk_grid"] == "25x32"
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 4, 262144, k=9000))
+    assert f["mode"] == "exact" and f["chunk_grid"] == "0x4"
+    # 128K prefill: streaming indexer, one top-k workgroup per row, one
+    # attention workgroup per (row, KV head)
+    f = F(d(dsa.DSA_PLAN_INDEXER, 1, 2048, 131072, D_idx=64))
+    assert f["kernel"] == "indexer_stream_kernel" and f["waves"] == "8"
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 2048, 131072, k=2048))
+    assert f["plan"] == "stream" and f["grid"] == "2048"
+    # invalid queries: 0, with the reason
+    with pytest.raises(dsa.DsaError):
+        d(7, 1, 1, 16)
+    with pytest.raises(dsa.DsaError):
+        d(dsa.DSA_PLAN_TOPK, 1, 8, 32768, k=0)
+    assert "k=0" in dsa.dsa_last_error()
+
+
+def L_attn_ws(dsa, a):
+    return dsa.LIB.dsa_attention_workspace_bytes(ctypes.byref(a), 1)
