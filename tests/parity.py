@@ -75,11 +75,18 @@ def assert_output_close(y, ref_f64, out_dtype, rel_gate=REL_RMSE_GATE,
     yf = to_f64(y)
     assert np.all(np.isfinite(yf)), f"{what}: non-finite output"
     r = round_f64(ref_f64, out_dtype)
+    err = np.abs(yf - r)
     bound = np.maximum(abs_gate, ulp(r, out_dtype))
-    over = np.abs(yf - r) > bound
+    over = err > bound
+    # elements beyond the literal max-abs gate (allowed only where one output
+    # ulp exceeds it, unless strict): reported on every call
+    n_abs = int((err > abs_gate).sum())
+    print(f"parity {what}: rel_rmse={rel:.3e} max_abs={mx:.3e} "
+          f"beyond {abs_gate:.0e}: {n_abs} of {err.size} (each within 1 ulp)", flush=True)
     assert rel <= rel_gate and not over.any(), (
         f"{what}: rel_rmse={rel:.3e} (gate {rel_gate:.0e}), max_abs={mx:.3e}, "
-        f"{int(over.sum())} element(s) beyond max({abs_gate:.0e}, 1 ulp)")
+        f"{int(over.sum())} element(s) beyond max({abs_gate:.0e}, 1 ulp), "
+        f"{n_abs} beyond {abs_gate:.0e}")
     if strict:
-        assert mx <= abs_gate, f"{what}: max_abs={mx:.3e} (gate {abs_gate:.0e})"
+        assert mx <= abs_gate, f"{what}: max_abs={mx:.3e} (gate {abs_gate:.0e}), {n_abs} beyond it"
     return rel, mx
