@@ -107,6 +107,24 @@ struct Lds {
 constexpr int kTieSmall = 64;     // ties resolved by one wave without a radix pass
 constexpr int kMiscWords = 16 + kTieSmall;
 
+// h[i] = hist[nbins - 1 - (t BPT + i)]: thread t's BPT bins, highest first
+// (16-byte LDS reads when BPT is a multiple of 4).
+template <int BPT>
+__device__ __forceinline__ void load_bins_desc(const uint32_t* hist, int nbins, int t,
+                                               uint32_t (&h)[BPT]) {
+  if constexpr (BPT % 4 == 0) {
+    const uint4* q = reinterpret_cast<const uint4*>(hist + nbins - BPT * (t + 1));
+#pragma unroll
+    for (int j = 0; j < BPT / 4; ++j) {
+      const uint4 v = q[BPT / 4 - 1 - j];
+      h[4 * j] = v.w; h[4 * j + 1] = v.z; h[4 * j + 2] = v.y; h[4 * j + 3] = v.x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) h[i] = hist[nbins - 1 - (t * BPT + i)];
+  }
+}
+
 // The bin holding the need-th largest key of a 2048-bin histogram:
 // misc[0] = bin, misc[1] = keys in higher bins.  Block-wide.  Each thread
 // reads its BPT bins once into registers (a second pass of LDS reads behind
@@ -119,12 +137,10 @@ __device__ void select_bin(const uint32_t* hist, uint32_t need, uint32_t* scratc
   const int t = threadIdx.x;
   if (t == 0) { misc[0] = 0; misc[1] = 0; }   // ordered before the finder by the scan's barriers
   uint32_t h[BPT];
+  load_bins_desc<BPT>(hist, kBins, t, h);
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = hist[kBins - 1 - (t * BPT + i)];
-    local += h[i];
-  }
+  for (int i = 0; i < BPT; ++i) local += h[i];
   uint32_t total;
   uint32_t before = block_exclusive_scan<NT>(local, scratch, &total);
 #pragma unroll
@@ -188,12 +204,10 @@ __device__ uint32_t select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t
   const int t = threadIdx.x;
   if (t == 0) { misc[0] = 0; misc[1] = 0; }
   uint32_t h[BPT];
+  load_bins_desc<BPT>(hist, kRelBins, t, h);
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = hist[kRelBins - 1 - (t * BPT + i)];
-    local += h[i];
-  }
+  for (int i = 0; i < BPT; ++i) local += h[i];
   uint32_t total;
   uint32_t before = block_exclusive_scan<NT>(local, scratch, &total);
 #pragma unroll
@@ -901,7 +915,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   constexpr int NT = kChunkThreads;
   constexpr int CH = U * NT;
   constexpr int NB = NS / kSampleBlock;        // sample keys per lane
-  __shared__ uint32_t h0[kBins], h1[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h0[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kBins];
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t misc[8];
   __shared__ __attribute__((aligned(16))) float chunk[CH];   // lane t's keys at U t + [0, U)
