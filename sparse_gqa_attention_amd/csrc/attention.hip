@@ -646,12 +646,15 @@ void attn_kernel(AttnParams p) {
 
 // Combine the key splits of one (row, head) in a fixed order (deterministic).
 // Thread t owns a float4 column chunk (t % (D/4)) and the splits
-// t / (D/4), + G, + 2G, ... (G = 256 / (D/4)).  Every partial-O load is
-// issued before the split maxima are known (they do not depend on them), so
-// the kernel waits on one round of memory latency; the G partial sums meet
-// in LDS.
+// t / (D/4), + G, + 2G, ... (G = 256 / (D/4)).  Lane i of every wave also
+// reads split i's (m, l) (at most 64 splits: one per lane), so all loads go
+// out together and the kernel waits on one round of memory latency.  Each
+// wave forms the maximum, the factors and L with lane shuffles (no LDS),
+// and the G partial sums meet in LDS behind a single barrier.  The sums run
+// in the same order in every wave, so the result does not depend on timing.
 constexpr int kMergeThreads = 256;
 constexpr int kMaxSplits = 64;
+static_assert(kMaxSplits <= kWave, "one split per lane");
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
@@ -659,10 +662,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   constexpr int C4 = D / 4;                 // float4 chunks per row
   constexpr int G = kMergeThreads / C4;     // split groups
   constexpr int Q = kMaxSplits / G;         // splits per thread at most
-  __shared__ float mm[kMaxSplits], ff[kMaxSplits], ll[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float4 acc[G][C4];
-  const int hrow = blockIdx.x, t = threadIdx.x;
-  const float* pml = part + (size_t)hrow * nsplit * 2;
+  const int hrow = blockIdx.x, t = threadIdx.x, lane = lane_id();
+  const float2* pml = reinterpret_cast<const float2*>(part) + (size_t)hrow * nsplit;
   const float4* po = (const float4*)(part + (size_t)2 * rows_h * nsplit) + (size_t)hrow * nsplit * C4;
   const int c = t % C4, g = t / C4;
   float4 ov[Q];
@@ -671,26 +673,24 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const int sp = g + q * G;
     ov[q] = sp < nsplit ? po[(size_t)sp * C4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (t < nsplit) { mm[t] = pml[2 * t]; ll[t] = pml[2 * t + 1]; }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mm[sp]);
-  if (t < nsplit) ff[t] = (M == -INFINITY || mm[t] == -INFINITY) ? 0.0f : exp_keep_subnormal(mm[t] - M);
-  __syncthreads();
+  const float2 ml = lane < nsplit ? pml[lane] : make_float2(-INFINITY, 0.0f);
+  float M = ml.x;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+  const float f = (ml.x == -INFINITY) ? 0.0f : exp_keep_subnormal(ml.x - M);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
-    const int sp = g + q * G;
-    if (sp < nsplit) {
-      const float f = ff[sp];
-      o.x += f * ov[q].x; o.y += f * ov[q].y; o.z += f * ov[q].z; o.w += f * ov[q].w;
-    }
+    const float fq = __shfl(f, g + q * G, kWave);   // 0 for splits >= nsplit
+    o.x += fq * ov[q].x; o.y += fq * ov[q].y; o.z += fq * ov[q].z; o.w += fq * ov[q].w;
   }
+  // L = sum of f * l over the splits (a fixed butterfly, all lanes active)
+  float L = f * ml.y;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) L += __shfl_xor(L, off, kWave);
   acc[g][c] = o;
   __syncthreads();
   if (t < C4) {
-    float L = 0.0f;
-    for (int q = 0; q < nsplit; ++q) L += ff[q] * ll[q];
     float4 r = acc[0][t];
 #pragma unroll
     for (int q = 1; q < G; ++q) {
