@@ -475,10 +475,12 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
             ri["out"] = torch.empty_like(ri["x"], dtype=rope_out)
             rope_sets.append(ri)
 
+        rope_jobs = [dict(x=ri["x"], gamma=ri["gamma"], cos_cache=ri["cos"], sin_cache=ri["sin"],
+                          kv_len=ri["kv_len"], out=ri["out"]) for ri in rope_sets]
+
         def rope_stage():
-            for ri in rope_sets:
-                dsa.dsa_rmsnorm_rope(ri["x"], ri["gamma"], ri["cos"], ri["sin"], ri["kv_len"],
-                                     ri["out"])
+            # the step's query, key and indexer-query heads in one launch
+            dsa.dsa_rmsnorm_rope_multi(rope_jobs)
         aux = {kk: v.to(dev) for kk, v in make_aux_inputs(
             B, S, w.H_kv, w.D, "f32" if w.kv_dtype == "f32" else "bf16", seed=24).items()}
         a_aux = dsa.attention_args(g0["q"], g0["k_cache"], g0["v_cache"], idx, g0["kv_len"], out,

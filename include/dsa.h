@@ -279,6 +279,20 @@ typedef struct {
 
 dsa_status dsa_rmsnorm_rope(const dsa_rmsnorm_rope_args* args, void* stream);
 
+/*
+ * The same operation on up to 4 independent tensors in one kernel launch:
+ * args points to `count` (1..4) argument blocks, each with the meaning,
+ * limits and results of dsa_rmsnorm_rope.  A decode step rotates its query
+ * heads, key heads and indexer query heads (different H and D), and this
+ * call gives them a single launch.  Every block is validated before anything
+ * is launched; a job with no rows is skipped.  A job's out may alias its own
+ * x, but no job may write memory that another job of the call reads or
+ * writes (the jobs run concurrently).  Errors: DSA_ERR_INVALID_ARGUMENT for
+ * count outside [1, 4] or a NULL args; otherwise as dsa_rmsnorm_rope, the
+ * message naming the job.
+ */
+dsa_status dsa_rmsnorm_rope_multi(const dsa_rmsnorm_rope_args* args, int32_t count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,8 @@ from .dsa import (DsaError, dsa_abi_version, dsa_last_error, dsa_indexer_score,
                   dsa_attention_prefill, dsa_attention_decode_noalloc, dsa_describe_plan,
                   plan_fields, DSA_PLAN_INDEXER, DSA_PLAN_TOPK, DSA_PLAN_ATTENTION_DECODE,
                   DSA_PLAN_ATTENTION_PREFILL, dsa_cache_append,
-                  cache_append_args, dsa_rmsnorm_rope, rope_args, EXPORTS, LIB)
+                  cache_append_args, dsa_rmsnorm_rope, dsa_rmsnorm_rope_multi, rope_args, EXPORTS,
+                  LIB)
 
 __all__ = ["DsaError", "dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "attention_args",
@@ -17,4 +18,5 @@ __all__ = ["DsaError", "dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_attention_prefill", "dsa_attention_decode_noalloc", "dsa_describe_plan",
            "plan_fields", "DSA_PLAN_INDEXER", "DSA_PLAN_TOPK", "DSA_PLAN_ATTENTION_DECODE",
            "DSA_PLAN_ATTENTION_PREFILL", "dsa_cache_append",
-           "cache_append_args", "dsa_rmsnorm_rope", "rope_args", "EXPORTS", "LIB"]
+           "cache_append_args", "dsa_rmsnorm_rope", "dsa_rmsnorm_rope_multi", "rope_args", "EXPORTS",
+           "LIB"]

@@ -391,33 +391,52 @@ dsa_status dsa_cache_append(const dsa_cache_append_args* a, void* stream) {
   return hip_result("dsa_cache_append");
 }
 
-dsa_status dsa_rmsnorm_rope(const dsa_rmsnorm_rope_args* a, void* stream) {
-  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->B < 0 || a->S < 0 || a->H < 0)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "B=%d S=%d H=%d must be >= 0", a->B, a->S, a->H);
-  if (a->D != 32 && a->D != 64 && a->D != 128)
-    return fail(DSA_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", a->D);
-  if (a->max_pos < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "max_pos=%d must be >= 1", a->max_pos);
-  if (!(a->eps >= 0.0f) || !std::isfinite(a->eps))
-    return fail(DSA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-  for (int d : {a->x_dtype, a->out_dtype})
-    if (d != DSA_F32 && d != DSA_F16 && d != DSA_BF16)
-      return fail(DSA_ERR_UNSUPPORTED, "dtype %s not in {F32, F16, BF16}", dtype_name(d));
-  if ((long long)a->B * a->S * a->H == 0) return ok();
-  CHECK(check_ptr(a->x, "x"));
-  CHECK(check_ptr(a->gamma, "gamma"));
-  CHECK(check_ptr(a->cos_cache, "cos_cache"));
-  CHECK(check_ptr(a->sin_cache, "sin_cache"));
-  CHECK(check_ptr(a->kv_len, "kv_len"));
-  CHECK(check_ptr(a->out, "out"));
-  dsa::RopeLaunch l{};
-  l.x = a->x; l.gamma = a->gamma; l.cos_cache = a->cos_cache; l.sin_cache = a->sin_cache;
-  l.kv_len = a->kv_len; l.out = a->out; l.x_dtype = a->x_dtype; l.out_dtype = a->out_dtype;
-  l.B = a->B; l.S = a->S; l.H = a->H; l.D = a->D; l.max_pos = a->max_pos;
-  l.eps = a->eps; l.interleaved = a->interleaved != 0;
+dsa_status dsa_rmsnorm_rope_multi(const dsa_rmsnorm_rope_args* args, int32_t count, void* stream) {
+  if (!args) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (count < 1 || count > dsa::kRopeMaxJobs)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "count=%d not in [1, %d]", count, dsa::kRopeMaxJobs);
+  dsa::RopeLaunch jobs[dsa::kRopeMaxJobs] = {};
+  long long blocks = 0;
+  for (int q = 0; q < count; ++q) {
+    const dsa_rmsnorm_rope_args* a = &args[q];
+    if (a->B < 0 || a->S < 0 || a->H < 0)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "job %d: B=%d S=%d H=%d must be >= 0", q, a->B, a->S,
+                  a->H);
+    if (a->D != 32 && a->D != 64 && a->D != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "job %d: head dim D=%d not in {32, 64, 128}", q, a->D);
+    if (a->max_pos < 1)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "job %d: max_pos=%d must be >= 1", q, a->max_pos);
+    if (!(a->eps >= 0.0f) || !std::isfinite(a->eps))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "job %d: eps must be finite and >= 0", q);
+    for (int d : {a->x_dtype, a->out_dtype})
+      if (d != DSA_F32 && d != DSA_F16 && d != DSA_BF16)
+        return fail(DSA_ERR_UNSUPPORTED, "job %d: dtype %s not in {F32, F16, BF16}", q,
+                    dtype_name(d));
+    const long long rows = (long long)a->B * a->S * a->H;
+    if (rows == 0) continue;
+    CHECK(check_ptr(a->x, "x"));
+    CHECK(check_ptr(a->gamma, "gamma"));
+    CHECK(check_ptr(a->cos_cache, "cos_cache"));
+    CHECK(check_ptr(a->sin_cache, "sin_cache"));
+    CHECK(check_ptr(a->kv_len, "kv_len"));
+    CHECK(check_ptr(a->out, "out"));
+    blocks += (rows * (a->D / 2) + 255) / 256;
+    if (blocks > INT32_MAX)
+      return fail(DSA_ERR_UNSUPPORTED, "the jobs need more than 2^31 - 1 workgroups");
+    dsa::RopeLaunch& l = jobs[q];
+    l.x = a->x; l.gamma = a->gamma; l.cos_cache = a->cos_cache; l.sin_cache = a->sin_cache;
+    l.kv_len = a->kv_len; l.out = a->out; l.x_dtype = a->x_dtype; l.out_dtype = a->out_dtype;
+    l.B = a->B; l.S = a->S; l.H = a->H; l.D = a->D; l.max_pos = a->max_pos;
+    l.eps = a->eps; l.interleaved = a->interleaved != 0;
+  }
+  if (blocks == 0) return ok();
   (void)hipGetLastError();
-  dsa::launch_rmsnorm_rope(l, (hipStream_t)stream);
-  return hip_result("dsa_rmsnorm_rope");
+  dsa::launch_rmsnorm_rope(jobs, count, (hipStream_t)stream);
+  return hip_result("dsa_rmsnorm_rope_multi");
+}
+
+dsa_status dsa_rmsnorm_rope(const dsa_rmsnorm_rope_args* a, void* stream) {
+  return dsa_rmsnorm_rope_multi(a, 1, stream);
 }
 
 }  // extern "C"

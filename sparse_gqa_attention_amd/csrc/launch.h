@@ -110,6 +110,9 @@ struct RopeLaunch {
   float eps;
   int interleaved;
 };
-void launch_rmsnorm_rope(const RopeLaunch& a, hipStream_t st);
+// Up to kRopeMaxJobs independent jobs in one launch (jobs without rows are
+// skipped).
+constexpr int kRopeMaxJobs = 4;
+void launch_rmsnorm_rope(const RopeLaunch* jobs, int n, hipStream_t st);
 
 }  // namespace dsa

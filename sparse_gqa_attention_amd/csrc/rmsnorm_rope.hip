@@ -16,7 +16,10 @@
 // pair, so the rotation needs no data exchange; the D/2 lanes of a head
 // vector (64 for D = 128; 32 or 16 for D = 64 or 32: 2 or 4 vectors per
 // wave) reduce the sum of squares with a segmented xor butterfly.  Rows
-// whose position falls outside the tables are not written.
+// whose position falls outside the tables are not written.  A decode step
+// rotates several tensors (query, key and indexer query heads, which differ
+// in head count and D): one launch takes up to kRopeMaxJobs of them, each a
+// contiguous range of workgroups, so a step pays one launch, not three.
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -26,18 +29,33 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 
-template <typename T>
-__device__ __forceinline__ float ld_f32(const void* p, size_t i) {
-  return to_f32(((const T*)p)[i]);
+struct RopeBatch {
+  RopeLaunch job[kRopeMaxJobs];
+  int first[kRopeMaxJobs + 1];   // first workgroup of each job; first[n] = grid size
+  int n;
+};
+
+// Dtypes are uniform over a workgroup (one job), so these branches do not
+// diverge.
+__device__ __forceinline__ float ld_any(const void* p, size_t i, int dt) {
+  if (dt == kF32) return ((const float*)p)[i];
+  if (dt == kF16) return to_f32(((const _Float16*)p)[i]);
+  return to_f32(((const __bf16*)p)[i]);
 }
 
-// P lanes (pairs) per head vector; InT / OutT: x and out dtypes.
-template <int P, typename InT, typename OutT>
-__global__ __launch_bounds__(kRopeThreads) void rmsnorm_rope_kernel(RopeLaunch a) {
+__device__ __forceinline__ void st_any(void* p, size_t i, float v, int dt) {
+  if (dt == kF32) ((float*)p)[i] = v;
+  else if (dt == kF16) ((_Float16*)p)[i] = from_f32<_Float16>(v);
+  else ((__bf16*)p)[i] = from_f32<__bf16>(v);
+}
+
+// Workgroup `blk` of job a, P lanes (pairs) per head vector.
+template <int P>
+__device__ __forceinline__ void rope_rows(const RopeLaunch& a, int blk) {
   constexpr int D = 2 * P;
   constexpr int kRowsPerBlock = kRopeThreads / P;
   const int i = threadIdx.x % P;                          // pair index
-  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / P;
+  const long long row = (long long)blk * kRowsPerBlock + threadIdx.x / P;
   const long long rows = (long long)a.B * a.S * a.H;
   const bool live_row = row < rows;
   const long long r = live_row ? row : 0;
@@ -48,8 +66,8 @@ __global__ __launch_bounds__(kRopeThreads) void rmsnorm_rope_kernel(RopeLaunch a
   const int da = a.interleaved ? 2 * i : i;
   const int db = a.interleaved ? 2 * i + 1 : i + P;
   const size_t base = (size_t)r * D;
-  const float xa = ld_f32<InT>(a.x, base + da);
-  const float xb = ld_f32<InT>(a.x, base + db);
+  const float xa = ld_any(a.x, base + da, a.x_dtype);
+  const float xb = ld_any(a.x, base + db, a.x_dtype);
   // sum of squares over the row's P lanes (xor offsets stay inside the row)
   float ss = fmaf(xa, xa, xb * xb);
 #pragma unroll
@@ -60,38 +78,42 @@ __global__ __launch_bounds__(kRopeThreads) void rmsnorm_rope_kernel(RopeLaunch a
   const float yb = xb * inv * a.gamma[db];
   const float c = a.cos_cache[(size_t)p * P + i];
   const float sn = a.sin_cache[(size_t)p * P + i];
-  OutT* out = (OutT*)a.out;
-  out[base + da] = from_f32<OutT>(ya * c - yb * sn);
-  out[base + db] = from_f32<OutT>(yb * c + ya * sn);
+  st_any(a.out, base + da, ya * c - yb * sn, a.out_dtype);
+  st_any(a.out, base + db, yb * c + ya * sn, a.out_dtype);
 }
 
-template <int P, typename InT>
-void launch_out(const RopeLaunch& a, hipStream_t st) {
-  const long long rows = (long long)a.B * a.S * a.H;
-  const dim3 grid((unsigned)((rows * P + kRopeThreads - 1) / kRopeThreads));
-  switch (a.out_dtype) {
-    case kF32: hipLaunchKernelGGL((rmsnorm_rope_kernel<P, InT, float>), grid, dim3(kRopeThreads), 0, st, a); break;
-    case kF16: hipLaunchKernelGGL((rmsnorm_rope_kernel<P, InT, _Float16>), grid, dim3(kRopeThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((rmsnorm_rope_kernel<P, InT, __bf16>), grid, dim3(kRopeThreads), 0, st, a); break;
-  }
-}
-
-template <int P>
-void launch_in(const RopeLaunch& a, hipStream_t st) {
-  switch (a.x_dtype) {
-    case kF32: launch_out<P, float>(a, st); break;
-    case kF16: launch_out<P, _Float16>(a, st); break;
-    default: launch_out<P, __bf16>(a, st); break;
-  }
+__global__ __launch_bounds__(kRopeThreads) void rmsnorm_rope_kernel(RopeBatch bt) {
+  const int blk = blockIdx.x;
+  // the job of this workgroup (a uniform choice among at most 4)
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kRopeMaxJobs; ++q) j += (q < bt.n && blk >= bt.first[q]) ? 1 : 0;
+  const RopeLaunch& a = bt.job[j];
+  const int local = blk - bt.first[j];
+  if (a.D == 32) rope_rows<16>(a, local);
+  else if (a.D == 64) rope_rows<32>(a, local);
+  else rope_rows<64>(a, local);
 }
 
 }  // namespace
 
-void launch_rmsnorm_rope(const RopeLaunch& a, hipStream_t st) {
-  if ((long long)a.B * a.S * a.H == 0) return;
-  if (a.D == 32) launch_in<16>(a, st);
-  else if (a.D == 64) launch_in<32>(a, st);
-  else launch_in<64>(a, st);
+void launch_rmsnorm_rope(const RopeLaunch* jobs, int n, hipStream_t st) {
+  RopeBatch bt{};
+  int blocks = 0;
+  bt.n = 0;
+  for (int q = 0; q < n && q < kRopeMaxJobs; ++q) {
+    const RopeLaunch& a = jobs[q];
+    const long long rows = (long long)a.B * a.S * a.H;
+    if (rows == 0) continue;                      // nothing to rotate: no workgroups
+    const int P = a.D / 2;
+    bt.job[bt.n] = a;
+    bt.first[bt.n] = blocks;
+    blocks += (int)((rows * P + kRopeThreads - 1) / kRopeThreads);
+    ++bt.n;
+  }
+  if (bt.n == 0) return;
+  for (int q = bt.n; q <= kRopeMaxJobs; ++q) bt.first[q] = blocks;
+  hipLaunchKernelGGL(rmsnorm_rope_kernel, dim3(blocks), dim3(kRopeThreads), 0, st, bt);
 }
 
 }  // namespace dsa

@@ -22,7 +22,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
 EXPORTS = ("dsa_abi_version", "dsa_last_error", "dsa_indexer_score",
            "dsa_topk_workspace_bytes", "dsa_topk", "dsa_attention_workspace_bytes",
            "dsa_attention_decode", "dsa_attention_prefill", "dsa_attention_decode_noalloc",
-           "dsa_describe_plan", "dsa_cache_append", "dsa_rmsnorm_rope")
+           "dsa_describe_plan", "dsa_cache_append", "dsa_rmsnorm_rope", "dsa_rmsnorm_rope_multi")
 DSA_PLAN_INDEXER, DSA_PLAN_TOPK, DSA_PLAN_ATTENTION_DECODE, DSA_PLAN_ATTENTION_PREFILL = 0, 1, 2, 3
 
 
@@ -101,6 +101,8 @@ def _load():
                                       ctypes.POINTER(AttentionArgs), ctypes.c_char_p, sz]
     lib.dsa_rmsnorm_rope.restype = i32
     lib.dsa_rmsnorm_rope.argtypes = [ctypes.POINTER(RopeArgs), vp]
+    lib.dsa_rmsnorm_rope_multi.restype = i32
+    lib.dsa_rmsnorm_rope_multi.argtypes = [ctypes.POINTER(RopeArgs), i32, vp]
     lib.dsa_cache_append.restype = i32
     lib.dsa_cache_append.argtypes = [ctypes.POINTER(CacheAppendArgs), vp]
     return lib
@@ -314,3 +316,18 @@ def dsa_rmsnorm_rope(x, gamma, cos_cache, sin_cache, kv_len, out, eps=1e-6, inte
     a = rope_args(x, gamma, cos_cache, sin_cache, kv_len, out, eps, interleaved)
     _check(LIB.dsa_rmsnorm_rope(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def dsa_rmsnorm_rope_multi(jobs, stream=None):
+    """Several dsa_rmsnorm_rope jobs in one launch; jobs: sequence of dicts with the keys
+    x, gamma, cos_cache, sin_cache, kv_len, out and optionally eps, interleaved.
+    Returns the list of outputs; see include/dsa.h."""
+    jobs = list(jobs)
+    arr = (RopeArgs * max(1, len(jobs)))()
+    for i, j in enumerate(jobs):
+        for n in ("x", "gamma", "cos_cache", "sin_cache", "kv_len", "out"):
+            _gpu(j[n], f"jobs[{i}].{n}")
+        arr[i] = rope_args(j["x"], j["gamma"], j["cos_cache"], j["sin_cache"], j["kv_len"],
+                           j["out"], j.get("eps", 1e-6), j.get("interleaved", False))
+    _check(LIB.dsa_rmsnorm_rope_multi(arr, len(jobs), _stream(stream)))
+    return [j["out"] for j in jobs]

@@ -35,7 +35,7 @@ def declared_functions(header=HEADER):
 
 def test_header_and_library_agree(dsa):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = ctypes.CDLL(LIBPATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -222,6 +222,25 @@ def test_rmsnorm_rope_validation(dsa):
     for kw, want in bad:
         assert call(_rope(dsa, **kw)) == _status(want), (kw, dsa.dsa_last_error())
     assert call(_rope(dsa, H=0, x=None, out=None)) == 0
+
+
+def test_rmsnorm_rope_multi_validation(dsa):
+    """Every job is validated (and named in the message) before any launch; the
+    count must lie in [1, 4]."""
+    L = dsa.LIB
+    def call(*jobs, count=None):
+        arr = (dsa.dsa.RopeArgs * max(1, len(jobs)))(*jobs)
+        return L.dsa_rmsnorm_rope_multi(arr, len(jobs) if count is None else count, None)
+    good = _rope(dsa, H=0, x=None, out=None)
+    assert call(good) == 0
+    assert call(good, good, good, good) == 0
+    assert call(good, count=0) == _status("INVALID")
+    assert call(good, good, good, good, good) == _status("INVALID")
+    assert L.dsa_rmsnorm_rope_multi(None, 1, None) == _status("INVALID")
+    assert call(good, _rope(dsa, D=96)) == _status("UNSUPPORTED")
+    assert "job 1" in dsa.dsa_last_error()
+    assert call(good, good, _rope(dsa, out=None)) == _status("INVALID")
+    assert "out" in dsa.dsa_last_error()
 
 
 def test_error_text_is_thread_local_and_cleared(dsa):

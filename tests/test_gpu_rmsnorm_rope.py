@@ -42,7 +42,11 @@ def _check(dsa, B, S, H, D, max_pos, kv_len, x_dtype, out_dtype, interleaved, se
     dsa.dsa_rmsnorm_rope(g["x"], g["gamma"], g["cos"], g["sin"], g["kv_len"], out, eps=1e-6,
                          interleaved=interleaved)
     torch.cuda.synchronize()
-    got = out.cpu().double().numpy()
+    return _compare(x, kv_len, out.cpu().double().numpy(), out_dtype, interleaved, in_place,
+                    max_flip_frac)
+
+
+def _compare(x, kv_len, got, out_dtype, interleaved, in_place=False, max_flip_frac=0.01):
     exact = ro.rmsnorm_rope(x["x"], x["gamma"], x["cos"], x["sin"], kv_len, 1e-6, interleaved)
     skipped = np.isnan(exact[:, :, 0, 0])
     for b, s in zip(*np.nonzero(skipped)):        # rows outside the tables stay untouched
@@ -95,3 +99,35 @@ def test_rope_workload_shapes_and_pages_rmse(dsa, H, S, L):
     rel = float(np.sqrt(np.sum((gv - e) ** 2) / np.sum(e ** 2)))
     say(f"rope H={H} S={S}: FP16 output relative RMSE vs exact {rel:.3e} (pages: 2.07e-4)")
     assert rel <= 1.1 * 2.07e-4
+
+
+def test_rope_multi_one_launch(dsa):
+    """dsa_rmsnorm_rope_multi: the query, key and indexer-query heads of a decode
+    step (different H, D and dtypes; one interleaved; one job with no rows) in
+    one launch, each against the oracle and bit-equal to its own single call."""
+    specs = [  # B, S, H, D, max_pos, kv_len, x_dtype, out_dtype, interleaved
+        (2, 8, 24, 128, 300, [300, 40], "bf16", "bf16", False),
+        (2, 8, 2, 128, 300, [300, 40], "bf16", "f16", False),
+        (2, 8, 0, 64, 300, [300, 40], "bf16", "bf16", False),
+        (2, 8, 16, 64, 300, [302, 40], "f32", "f16", True),
+    ]
+    jobs, singles, inputs = [], [], []
+    for i, (B, S, H, D, mp, kvl, xd, od, il) in enumerate(specs):
+        say(f"rope multi job {i}: B={B} S={S} H={H} D={D} x={xd} out={od} interleaved={il}")
+        x = make_rope_inputs(B, S, H, D, mp, xd, kvl, seed=40 + i)
+        g = {k: v.to(DEV) for k, v in x.items()}
+        out = torch.full((B, S, H, D), float("nan"), dtype=_T[od], device=DEV)
+        ref = torch.full((B, S, H, D), float("nan"), dtype=_T[od], device=DEV)
+        jobs.append(dict(x=g["x"], gamma=g["gamma"], cos_cache=g["cos"], sin_cache=g["sin"],
+                         kv_len=g["kv_len"], out=out, eps=1e-6, interleaved=il))
+        dsa.dsa_rmsnorm_rope(g["x"], g["gamma"], g["cos"], g["sin"], g["kv_len"], ref, eps=1e-6,
+                             interleaved=il)
+        singles.append(ref)
+        inputs.append(x)
+    dsa.dsa_rmsnorm_rope_multi(jobs)
+    torch.cuda.synchronize()
+    for i, (j, ref, x, sp) in enumerate(zip(jobs, singles, inputs, specs)):
+        assert torch.equal(j["out"].isnan(), ref.isnan()), i
+        assert torch.equal(torch.nan_to_num(j["out"]), torch.nan_to_num(ref)), i
+        if sp[2]:
+            _compare(x, sp[5], j["out"].cpu().double().numpy(), sp[7], sp[8])
