@@ -789,7 +789,7 @@ void plan_attention(AttnLaunch& a, bool decode) {
     return;
   }
   // Aim for ~3072 workgroups: a whole number of dispatch rounds whether the
-  // kernel fits 3 or 4 workgroups per CU (3072 = 256 CUs x 3 x 4), so no
+  // kernel fits 2, 3 or 4 workgroups per CU (3072 = 256 CUs x 12), so no
   // round runs partly empty.  At least 128 keys (one tile per wave) per
   // split, whole 32-key tiles, at most 64 splits (one merge lane per split).
   const long long rows_kv = (long long)a.B * a.S * a.H_kv;
@@ -797,12 +797,16 @@ void plan_attention(AttnLaunch& a, bool decode) {
   kps = ((kps + kTile - 1) / kTile) * kTile;
   if (kps < 128) kps = 128;
   long long ns = (a.k + kps - 1) / kps;
-  // With one tile per wave, a grid beyond two workgroups per CU (the
-  // residency of the 16-bit D=128 kernel) runs a second dispatch round of
+  // 16-bit caches at D = 128 fit two workgroups per CU and load each tile's
+  // K rows one tile ahead (two register sets).  With one tile per wave, a
+  // grid beyond two workgroups per CU runs a second dispatch round of
   // latency-bound workgroups; two tiles per wave (the second tile's loads
-  // overlap the first's compute) in one round are faster there.
+  // overlap the first's compute) in one round are faster there.  INT8 and
+  // FP32 caches load each tile just before use and D = 64 fits more
+  // workgroups per CU, so the rule is kept to the case it was measured on.
   constexpr long long kOneRound = 2LL * 256;      // 256 CUs
-  if (kps == 128 && rows_kv * ns > kOneRound) {
+  const bool two_sets_d128 = (a.kv_dtype == kF16 || a.kv_dtype == kBF16) && a.D == 128;
+  if (two_sets_d128 && kps == 128 && rows_kv * ns > kOneRound) {
     kps = 256;
     ns = (a.k + kps - 1) / kps;
   }
