@@ -60,6 +60,7 @@ struct AttnParams {
   int write_partial;  // write (m, l, O) partials instead of the output
   int part_stride;    // splits per (row, head) in the partial buffer
   int part_offset;    // first split index of this launch
+  int rows;           // B * S
 };
 
 __device__ __forceinline__ void store_out(void* out, size_t i, float v, int dt) {
@@ -174,15 +175,36 @@ struct AttnCfg {
 // DENSE: key slot j is key j (the auxiliary keys), no index list.
 // INT8 caches run three waves per SIMD (at most 168 registers): measured
 // faster there than two waves with wider prefetch.
-template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE>
+// WAVE_ROWS (prefill with many rows, one key split): each wave owns a whole
+// (row, KV head) and walks all of its tiles; workgroup j takes KV head
+// j % H_kv and rows 4 (j / H_kv) + wave.  Consecutive workgroups land on
+// consecutive XCDs, so with H_kv dividing 8 an XCD serves one KV head, and
+// its rows, all started together and walking their index-ordered lists at
+// one tile per step, read the same key region at the same time: the K/V
+// rows that several query rows selected are reused from that XCD's L2.
+// (With four waves sharing a row, a workgroup sweeps its list four times
+// faster, the dispatch rounds start at different times, and the region read
+// at once is larger than the L2.)  The waves never synchronise.
+template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE,
+          bool WAVE_ROWS = false>
 __global__ __launch_bounds__(kAttnThreads)
 __attribute__((amdgpu_waves_per_eu(std::is_same<KVT, int8_t>::value ? 3 : 1)))
 void attn_kernel(AttnParams p) {
   using Cfg = AttnCfg<D, QT, KVT, MQK, MPV>;
   constexpr int Q4 = Cfg::kQuarter;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kLds];
+  static_assert(!(WAVE_ROWS && DENSE), "whole-row waves walk an index list");
 
-  const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
+  const int wave = threadIdx.x / kWave;
+  int split, g, row;
+  if constexpr (WAVE_ROWS) {
+    split = 0;
+    g = (int)(blockIdx.x % (unsigned)p.H_kv);
+    row = (int)(blockIdx.x / (unsigned)p.H_kv) * kAttnWaves + wave;
+    if (row >= p.rows) return;                 // no barrier follows in this form
+  } else {
+    split = blockIdx.x; g = blockIdx.y; row = blockIdx.z;
+  }
   const int b = row / p.S, s = row % p.S;
   int kvl = p.kvl_const >= 0 ? p.kvl_const : p.kv_len[b];
   kvl = kvl < 0 ? 0 : (kvl > p.L_cap ? p.L_cap : kvl);
@@ -192,15 +214,17 @@ void attn_kernel(AttnParams p) {
   const int k0 = split * p.kps;
   const int k1 = min(p.k, k0 + p.kps);
 
-  const int wave = threadIdx.x / kWave;
   const int l = lane_id();
   const int g4 = l >> 4;        // lane group 0..3
   const int c16 = l & 15;       // head column / key row within a half tile
   // This lane's key-list entries of the wave's first tile, fetched right
   // away so that their latency overlaps the kv_len and query loads.
+  // Tiles of the wave: every kAttnWaves-th of the split, or all of the row.
+  constexpr int kStep = WAVE_ROWS ? kTile : kTile * kAttnWaves;   // keys between a wave's tiles
+  const int t_first = WAVE_ROWS ? k0 : k0 + kTile * wave;
   int next_a = -1, next_b = -1;
   {
-    const int ja = k0 + kTile * wave + c16, jb = ja + 16;
+    const int ja = t_first + c16, jb = ja + 16;
     if (ja < k1) next_a = DENSE ? ja : idx_row[ja];
     if (jb < k1) next_b = DENSE ? jb : idx_row[jb];
   }
@@ -553,9 +577,7 @@ void attn_kernel(AttnParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  constexpr int kStep = kTile * kAttnWaves;     // keys between a wave's tiles
   auto entry = [&](int j) { return j < k1 ? (DENSE ? j : idx_row[j]) : -1; };
-  const int t_first = k0 + kTile * wave;
   int ia = next_a, ib = next_b;                 // this tile's entries
   int na = entry(t_first + kStep + c16), nb = entry(t_first + kStep + 16 + c16);
   TileRegs ra, rb;
@@ -585,9 +607,32 @@ void attn_kernel(AttnParams p) {
   }
   }
 
-  // ---- merge the 4 waves' states in LDS
   float l_col = l_run + __shfl_xor(l_run, 16, kWave);
   l_col += __shfl_xor(l_col, 32, kWave);
+  if constexpr (WAVE_ROWS) {
+    // The wave's state is the row's: lane c16 + 16 g4 holds dims
+    // 16 dt + 4 g4 + [0, 4) of head c16 (the O^T accumulator layout).
+    if (c16 < R) {
+      const size_t hrow = (size_t)row * p.H_q + g * R + c16;
+      if (!p.write_partial) {
+#pragma unroll
+        for (int dt = 0; dt < Cfg::kDTiles; ++dt)
+          store_out4(p.out, hrow * D + 16 * dt + 4 * g4, o[dt], l_col, p.out_dtype);
+      } else {
+        const size_t slot = hrow * p.part_stride + p.part_offset + split;
+        float* po = p.part + (size_t)2 * p.rows * p.H_q * p.part_stride;
+#pragma unroll
+        for (int dt = 0; dt < Cfg::kDTiles; ++dt)
+          *reinterpret_cast<f32x4*>(&po[slot * D + 16 * dt + 4 * g4]) = o[dt];
+        if (g4 == 0) {
+          p.part[slot * 2 + 0] = m_run;
+          p.part[slot * 2 + 1] = l_col;
+        }
+      }
+    }
+    return;
+  }
+  // ---- merge the 4 waves' states in LDS
   __syncthreads();
   constexpr int OS = Cfg::kOStride;
   float* ob = (float*)smem;                                  // [waves][16][OS]
@@ -634,7 +679,7 @@ void attn_kernel(AttnParams p) {
     } else {
       const size_t slot = hrow * p.part_stride + p.part_offset + split;
       float* pml = p.part;
-      float* po = p.part + (size_t)2 * gridDim.z * p.H_q * p.part_stride;
+      float* po = p.part + (size_t)2 * p.rows * p.H_q * p.part_stride;
       *reinterpret_cast<f32x4*>(&po[slot * D + 4 * c]) = O;
       if (c == 0) {
         pml[slot * 2 + 0] = hb[16 + n];
@@ -654,6 +699,7 @@ void attn_kernel(AttnParams p) {
 // in the same order in every wave, so the result does not depend on timing.
 constexpr int kMergeThreads = 256;
 constexpr int kMaxSplits = 64;
+constexpr long long kWaveRowsMinPairs = 2LL * 256 * kAttnWaves;
 static_assert(kMaxSplits <= kWave, "one split per lane");
 
 template <int D>
@@ -713,11 +759,21 @@ AttnParams base_params(const AttnLaunch& a) {
   p.write_partial = a.nsplit > 1 || a.aux_len > 0;
   p.part_stride = a.nsplit + (a.aux_len > 0 ? 1 : 0);
   p.part_offset = 0;
+  p.rows = a.B * a.S;
   return p;
 }
 
 template <int D, typename QT, typename KVT, typename MQK, typename MPV, bool DENSE = false>
-void launch_kernel(const AttnParams& p, int nsplit, int H_kv, int rows, hipStream_t st) {
+void launch_kernel(const AttnParams& p, int nsplit, int H_kv, int rows, hipStream_t st,
+                   bool wave_rows = false) {
+  if constexpr (!DENSE) {
+    if (wave_rows) {
+      const dim3 grid((unsigned)(H_kv * ((rows + kAttnWaves - 1) / kAttnWaves)));
+      hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV, false, true>), grid,
+                         dim3(kAttnThreads), 0, st, p);
+      return;
+    }
+  }
   dim3 grid(nsplit, H_kv, rows);
   hipLaunchKernelGGL((attn_kernel<D, QT, KVT, MQK, MPV, DENSE>), grid, dim3(kAttnThreads), 0, st,
                      p);
@@ -729,15 +785,16 @@ void launch_main(const AttnLaunch& a, const AttnParams& p, hipStream_t st) {
   typedef _Float16 H;
   typedef __bf16 BH;
   const int rows = a.B * a.S;
-  if (a.kv_dtype == kF32) { launch_kernel<D, float, float, float, float>(p, a.nsplit, a.H_kv, rows, st); return; }
+  const bool wr = a.wave_rows != 0;
+  if (a.kv_dtype == kF32) { launch_kernel<D, float, float, float, float>(p, a.nsplit, a.H_kv, rows, st, wr); return; }
   if (a.q_dtype == kBF16) {
-    if (a.kv_dtype == kF16) launch_kernel<D, BH, H, H, H>(p, a.nsplit, a.H_kv, rows, st);
-    else if (a.kv_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH>(p, a.nsplit, a.H_kv, rows, st);
-    else launch_kernel<D, BH, int8_t, BH, BH>(p, a.nsplit, a.H_kv, rows, st);
+    if (a.kv_dtype == kF16) launch_kernel<D, BH, H, H, H>(p, a.nsplit, a.H_kv, rows, st, wr);
+    else if (a.kv_dtype == kBF16) launch_kernel<D, BH, BH, BH, BH>(p, a.nsplit, a.H_kv, rows, st, wr);
+    else launch_kernel<D, BH, int8_t, BH, BH>(p, a.nsplit, a.H_kv, rows, st, wr);
   } else {
-    if (a.kv_dtype == kF16) launch_kernel<D, H, H, H, H>(p, a.nsplit, a.H_kv, rows, st);
-    else if (a.kv_dtype == kBF16) launch_kernel<D, H, BH, H, BH>(p, a.nsplit, a.H_kv, rows, st);
-    else launch_kernel<D, H, int8_t, H, BH>(p, a.nsplit, a.H_kv, rows, st);
+    if (a.kv_dtype == kF16) launch_kernel<D, H, H, H, H>(p, a.nsplit, a.H_kv, rows, st, wr);
+    else if (a.kv_dtype == kBF16) launch_kernel<D, H, BH, H, BH>(p, a.nsplit, a.H_kv, rows, st, wr);
+    else launch_kernel<D, H, int8_t, H, BH>(p, a.nsplit, a.H_kv, rows, st, wr);
   }
 }
 
@@ -783,9 +840,13 @@ void launch_d(const AttnLaunch& a, hipStream_t st) {
 void plan_attention(AttnLaunch& a, bool decode) {
   // The merge combines at most 64 splits; auxiliary keys take one of them.
   const int max_split = a.aux_len > 0 ? 63 : 64;
+  a.wave_rows = 0;
   if (!decode || a.k <= 0) {
     a.nsplit = 1;
     a.keys_per_split = a.k > 0 ? a.k : 1;
+    // Whole-row waves once they fill a dispatch round (512 workgroups of 4
+    // rows at two per CU); fewer rows keep four waves per row for latency.
+    a.wave_rows = !decode && (long long)a.B * a.S * a.H_kv >= kWaveRowsMinPairs ? 1 : 0;
     return;
   }
   // Aim for ~3072 workgroups: a whole number of dispatch rounds whether the

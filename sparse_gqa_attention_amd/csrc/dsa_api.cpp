@@ -304,9 +304,16 @@ size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k,
       const dsa::AttnLaunch l = make_attn(attention, decode);
       const int rows = l.B * l.S;
       const int splits = l.nsplit + (l.aux_len > 0 ? 1 : 0);
-      appendf(d, "op=%s kernel=attn_kernel grid=%dx%dx%d threads=256 keys_per_split=%d",
-              decode ? "attention_decode" : "attention_prefill", l.nsplit, l.H_kv, rows,
-              l.keys_per_split);
+      if (l.wave_rows)
+        appendf(d, "op=%s kernel=attn_kernel schedule=wave_rows grid=%d threads=256 "
+                   "rows_per_workgroup=4 keys_per_split=%d",
+                decode ? "attention_decode" : "attention_prefill", l.H_kv * ((rows + 3) / 4),
+                l.keys_per_split);
+      else
+        appendf(d, "op=%s kernel=attn_kernel schedule=split grid=%dx%dx%d threads=256 "
+                   "keys_per_split=%d",
+                decode ? "attention_decode" : "attention_prefill", l.nsplit, l.H_kv, rows,
+                l.keys_per_split);
       if (l.aux_len > 0) appendf(d, " aux_grid=1x%dx%d", l.H_kv, rows);
       if (splits > 1) appendf(d, " merge_kernel=attn_merge_kernel merge_grid=%d", rows * l.H_q);
       appendf(d, " workspace=%zu", dsa::attention_partials_bytes(l));

@@ -70,6 +70,7 @@ struct AttnLaunch {
   const void* aux_k;  // auxiliary (not yet cached) K/V [B, aux_len, H_kv, D], or null
   const void* aux_v;
   int aux_dtype, aux_len;
+  int wave_rows;      // prefill: each wave owns a whole (row, KV head)
 };
 // nsplit/keys_per_split for the decode form; prefill uses nsplit = 1.  Set
 // aux_len first: auxiliary keys take one merge slot.

@@ -286,7 +286,8 @@ def test_describe_plan_names_the_launches(dsa):
     assert f["grid"] == "16x2x8" and f["merge_grid"] == "192"
     assert int(f["workspace"]) == L_attn_ws(dsa, a)
     f = F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))
-    assert f["grid"] == "1x2x8" and "merge_grid" not in f and f["workspace"] == "0"
+    assert f["schedule"] == "split" and f["grid"] == "1x2x8" and "merge_grid" not in f
+    assert f["workspace"] == "0"
     # 256K decode: the two-kernel split top-k on its fast path
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 262144, k=2048))
     assert f["plan"] == "split" and f["chunk_grid"] == "32x8" and f["mode"] == "fast"
@@ -296,12 +297,20 @@ def test_describe_plan_names_the_launches(dsa):
     assert f["chunk_grid"] == "25x32"
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 4, 262144, k=9000))
     assert f["mode"] == "exact" and f["chunk_grid"] == "0x4"
-    # 128K prefill: streaming indexer, one top-k workgroup per row, one
-    # attention workgroup per (row, KV head)
+    # 128K prefill: streaming indexer, one top-k workgroup per row
     f = F(d(dsa.DSA_PLAN_INDEXER, 1, 2048, 131072, D_idx=64))
     assert f["kernel"] == "indexer_stream_kernel" and f["waves"] == "8"
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 2048, 131072, k=2048))
     assert f["plan"] == "stream" and f["grid"] == "2048"
+    # ... and whole-row attention waves (4 rows per workgroup, KV head j % 2)
+    a = _attn(dsa, q=None, k_cache=None, v_cache=None, indices=None, kv_len=None, out=None,
+              S=2048, L_cap=131072, max_kv_len=131072, kv_dtype=2)
+    f = F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))
+    assert f["schedule"] == "wave_rows" and f["grid"] == "1024" and f["workspace"] == "0"
+    # 1024 (row, KV head) pairs stay on four waves per row
+    a = _attn(dsa, q=None, k_cache=None, v_cache=None, indices=None, kv_len=None, out=None,
+              S=512, L_cap=131072, max_kv_len=131072, kv_dtype=2)
+    assert F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))["schedule"] == "split"
     # invalid queries: 0, with the reason
     with pytest.raises(dsa.DsaError):
         d(7, 1, 1, 16)

@@ -40,13 +40,13 @@ SAMPLE_ROWS = {
 # form), as dsa_describe_plan reports them -- the same descriptions the bench
 # logs next to its timings.
 EXPECTED_PLANS = {
-    "tiny_decode_1k": ("indexer_score_kernel", "resident", "attention_decode"),
-    "spec_decode_32k": ("indexer_score_kernel", "resident", "attention_decode"),
-    "prefill_128k": ("indexer_stream_kernel", "stream", "attention_prefill"),
-    "int8_batched_decode_64k": (None, None, "attention_decode"),
-    "decode_256k": ("indexer_stream_kernel", "split", "attention_decode"),
-    "ragged_decode_256k": ("indexer_stream_kernel", "split", "attention_decode"),
-    "ragged_prefill_64k": ("indexer_stream_kernel", "stream", "attention_prefill"),
+    "tiny_decode_1k": ("indexer_score_kernel", "resident", "attention_decode/split"),
+    "spec_decode_32k": ("indexer_score_kernel", "resident", "attention_decode/split"),
+    "prefill_128k": ("indexer_stream_kernel", "stream", "attention_prefill/wave_rows"),
+    "int8_batched_decode_64k": (None, None, "attention_decode/split"),
+    "decode_256k": ("indexer_stream_kernel", "split", "attention_decode/split"),
+    "ragged_decode_256k": ("indexer_stream_kernel", "split", "attention_decode/split"),
+    "ragged_prefill_64k": ("indexer_stream_kernel", "stream", "attention_prefill/wave_rows"),
 }
 
 
@@ -61,7 +61,8 @@ def _plans(dsa, wl, g, idx, out):
     a = dsa.attention_args(g["q"], g["k_cache"], g["v_cache"], idx, g["kv_len"], out,
                            g["k_scale"], g["v_scale"], max_kv_len=mx)
     op = dsa.DSA_PLAN_ATTENTION_DECODE if wl.decode_form else dsa.DSA_PLAN_ATTENTION_PREFILL
-    got.append(dsa.plan_fields(dsa.dsa_describe_plan(op, attention=a))["op"])
+    f = dsa.plan_fields(dsa.dsa_describe_plan(op, attention=a))
+    got.append(f"{f['op']}/{f['schedule']}")
     return tuple(got)
 
 
