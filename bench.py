@@ -568,9 +568,10 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
             run = dict(fns)
 
     # The gather ceiling of a prefill attention: the same K and V row reads,
-    # in the same launch order and tiling, with nothing else to do (the
-    # probe kernel), on this layer's caches and indices.
+    # in the same launch order, schedule and tiling, with nothing else to do
+    # (the probe kernel), on this layer's caches and indices.
     if not decode and w.D * ELT[w.kv_dtype] == 256:
+        wave_rows = dsa.plan_fields(plans["attention"]).get("schedule") == "wave_rows"
         run["step"]()
         torch.cuda.synchronize()
         ind = idx if w.has_indexer else g0["indices"]
@@ -578,7 +579,7 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
         for _ in range(max(5, K)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            rl.kv_gather(g0["k_cache"], g0["v_cache"], ind, S, sink)
+            rl.kv_gather(g0["k_cache"], g0["v_cache"], ind, S, sink, wave_rows=wave_rows)
             e1.record()
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) * 1e-3

@@ -39,12 +39,16 @@ int dsa_roofline_gather(const void* buf, size_t buf_bytes, const int32_t* rows, 
 
 /* The K/V reads of a sparse-attention launch with 256-byte rows (D * element
  * size = 256) and nothing else: caches [B, L_cap, H_kv, 256 bytes], indices
- * [rows, k] (row r of sequence r / S; entries outside [0, L_cap) skipped);
- * one 4-wave workgroup per (row, KV head), each wave reading the K and V rows
- * of its 32-key tiles a 128-byte line per 8 lanes, two tiles in flight.
- * rows, H_kv <= 65535. */
+ * [rows, k] (row r of sequence r / S; entries outside [0, L_cap) skipped).
+ * Each wave reads the K and V rows of its 32-key tiles a 128-byte line per 8
+ * lanes, two tiles in flight, at two 4-wave workgroups per CU.  wave_rows = 0:
+ * one workgroup per (row, KV head), wave w reading tiles w, w + 4, ...;
+ * wave_rows = 1: workgroup j takes KV head j % H_kv and rows 4 (j / H_kv) +
+ * wave, each wave reading all tiles of its row in order (the two schedules
+ * of the attention kernel).  rows, H_kv <= 65535. */
 int dsa_roofline_kv_gather(const void* k_cache, const void* v_cache, const int32_t* indices,
-                           int rows, int k, int S, int H_kv, int L_cap, void* sink, void* stream);
+                           int rows, int k, int S, int H_kv, int L_cap, int wave_rows, void* sink,
+                           void* stream);
 
 /* `workgroups` x `threads` (<= 1024) threads; every workgroup reads word[0]
  * and stores nothing (sink is only written for word[0] == 0x1234567): the

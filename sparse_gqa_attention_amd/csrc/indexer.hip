@@ -86,6 +86,15 @@ __device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
   }
 }
 
+// An empty use of a register value.  Placed on a kernel's early-exit path
+// it keeps loads whose results the other path consumes above the branch
+// (the compiler would otherwise sink them past it, adding a memory round
+// trip after the branch); the exit path waits for every load anyway.
+template <typename V>
+__device__ __forceinline__ void keep_loaded(const V& v) {
+  asm volatile("" ::"v"(v));
+}
+
 typedef __attribute__((address_space(3))) char lds_char;
 
 // global_load_lds_dwordx4 written out, for copies whose completion the
@@ -423,30 +432,40 @@ __global__ __launch_bounds__(WAVES * kWave, WPE) void indexer_stream_kernel(
   int tx, ty, tz;
   xcd_tile(tx, ty, tz);
   const int b = tz;
-  int kvl = kv_len[b];
-  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
   const int j_begin = ty * keys_per_wg;
-  const int j_end = min(j_begin + keys_per_wg, kvl);
   const int s_first = tx * kTokPerWg;
-  // Keys beyond the last position of this block's tokens are never selected.
-  const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
-  if (j_begin >= j_end || j_begin > last_pos) return;
-
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const int half = l >> 5, col = l & 31;
   const T* ks_b = key_state + (size_t)b * L_cap * DI;
 
+  // The first run's copy and the query operands go out before kv_len is read
+  // (the copy covers cache rows that exist whatever the live length:
+  // [j_begin, L_cap)), so they share one memory round trip.  A workgroup
+  // that then finds no live key waits for its copies before it ends.
   const FullRunLane<T, DI, NT> ln(wave, l);
-  if (j_end - j_begin >= R) copy_full_run<T, DI, NT, R>(ks_b + (size_t)j_begin * DI, buf0, wave, ln);
-  else copy_key_rows<T, DI, NT, true>(ks_b, j_begin, j_end, buf0, wave, l);
-
+  const int j_cap = min(j_begin + R, L_cap);
+  if (j_cap - j_begin >= R) copy_full_run<T, DI, NT, R>(ks_b + (size_t)j_begin * DI, buf0, wave, ln);
+  else if (j_begin < j_cap) copy_key_rows<T, DI, NT, true>(ks_b, j_begin, j_cap, buf0, wave, l);
   V8 a[PAIRS][Tr::kSteps];
   float wv[PAIRS][16];
   const int s_w = s_first + wave * kTokPerWave;        // first token of this wave
 #pragma unroll
   for (int p = 0; p < PAIRS; ++p)
     load_pair<T, DI>(q_idx, w_idx, b, S, H, s_w + 2 * p, col, half, a[p], wv[p]);
+  int kvl = kv_len[b];
+  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
+  const int j_end = min(j_begin + keys_per_wg, kvl);
+  // Keys beyond the last position of this block's tokens are never selected.
+  const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
+  if (j_begin >= j_end || j_begin > last_pos) {
+    wait_vmem();            // no copy may land after the workgroup ends
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p)
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) keep_loaded(a[p][st]);
+    return;
+  }
 
   // Score stores: one buffer resource per wave based at its first token's
   // row; tokens past S fall outside its record count and are dropped.
@@ -482,27 +501,38 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void indexer_score_kernel(
   int tx, ty, tz;
   xcd_tile(tx, ty, tz);
   const int b = tz;
-  int kvl = kv_len[b];
-  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
   const int j_begin = ty * keys_per_wg;
-  const int j_end = min(j_begin + keys_per_wg, kvl);
   const int s_first = tx * kTokPerWg;
-  const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
-  if (j_begin >= j_end || j_begin > last_pos) return;
-
   const int wave = threadIdx.x / kWave;
   const int l = lane_id();
   const int half = l >> 5;     // 0: lanes 0..31, 1: lanes 32..63
   const int col = l & 31;
   const T* ks_b = key_state + (size_t)b * L_cap * DI;
-  copy_key_rows<T, DI, NT, false>(ks_b, j_begin, j_end, run, wave, l);
-
+  // The run's copy and the query operands go out before kv_len is read
+  // (cache rows [j_begin, L_cap) exist whatever the live length), so they
+  // share one memory round trip; rows past the live length are copied but
+  // never scored.  A workgroup that finds no live key waits for its copies
+  // before it ends.
+  const int j_cap = min(j_begin + keys_per_wg, L_cap);
+  if (j_begin < j_cap) copy_key_rows<T, DI, NT, false>(ks_b, j_begin, j_cap, run, wave, l);
   V8 a[PAIRS][Tr::kSteps];
   float wv[PAIRS][16];
 #pragma unroll
   for (int p = 0; p < PAIRS; ++p)
     load_pair<T, DI>(q_idx, w_idx, b, S, H, s_first + wave * 2 * PAIRS + 2 * p, col, half, a[p],
                      wv[p]);
+  int kvl = kv_len[b];
+  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
+  const int j_end = min(j_begin + keys_per_wg, kvl);
+  const int last_pos = kvl - S + min(s_first + kTokPerWg, S) - 1;
+  if (j_begin >= j_end || j_begin > last_pos) {
+    wait_vmem();
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p)
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) keep_loaded(a[p][st]);
+    return;
+  }
   // Score row of each pair's token for this lane (lanes 0..31: t0, 32..63: t1).
   float* srow[PAIRS];
   bool s_ok[PAIRS];

@@ -95,48 +95,67 @@ __global__ __launch_bounds__(kThreads) void roof_gather_kernel(const uint4* __re
   if (acc == 0x9E3779B9u) out[0] = acc;
 }
 
-// The reads of a sparse-attention launch with nothing else to do: one
-// 4-wave workgroup per (query row, KV head) in the attention's launch order;
-// each wave takes 32-key tiles of the row's index list (tile w, w + 4, ...),
-// and for a tile reads the 32 K rows and the 32 V rows of 256 bytes, a
-// 128-byte line per 8 lanes, two tiles in flight.  Entries outside
-// [0, L_cap) are skipped (-1 padding).
+// The K/V reads of a sparse-attention launch and nothing else, in either of
+// its schedules.  The workgroup holds 64 KB of LDS, so two fit on a CU: the
+// residency of the 16-bit D = 128 attention kernel.
+//   WAVE_ROWS = false: workgroup (row, KV head); wave w reads tiles w, w + 4,
+//     ... of the row (two in flight: the tile and the one four further);
+//   WAVE_ROWS = true: workgroup j takes KV head j % H_kv and rows
+//     4 (j / H_kv) + wave; each wave reads every tile of its row in order,
+//     two in flight.
+constexpr int kKvHoldBytes = 64 * 1024;
+
+template <bool WAVE_ROWS>
 __global__ __launch_bounds__(kThreads) void roof_kv_gather_kernel(
     const unsigned char* __restrict__ kc, const unsigned char* __restrict__ vc,
-    const int32_t* __restrict__ idx, int k, int S, int H_kv, int L_cap, uint32_t* out) {
-  const int g = blockIdx.y, row = blockIdx.z, b = row / S;
+    const int32_t* __restrict__ idx, int k, int S, int H_kv, int L_cap, int rows, uint32_t* out) {
+  __shared__ uint32_t hold[kKvHoldBytes / 4];
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const size_t tok_bytes = (size_t)H_kv * 256;
-  const unsigned char* kb = kc + (size_t)b * L_cap * tok_bytes + (size_t)g * 256;
-  const unsigned char* vb = vc + (size_t)b * L_cap * tok_bytes + (size_t)g * 256;
-  const int32_t* ir = idx + (size_t)row * k;
+  int g, row, first, step, ahead;
+  if (WAVE_ROWS) {
+    g = (int)(blockIdx.x % (unsigned)H_kv);
+    row = (int)(blockIdx.x / (unsigned)H_kv) * 4 + wave;
+    first = 0; step = 64; ahead = 32;
+  } else {
+    g = blockIdx.y; row = blockIdx.z;
+    first = 32 * wave; step = 256; ahead = 128;
+  }
   uint32_t acc = 0;
-  for (int t0 = 32 * wave; t0 < k; t0 += 2 * 128) {
-    uint4 x[2][16];
+  if (row < rows) {
+    const int b = row / S;
+    const size_t tok_bytes = (size_t)H_kv * 256;
+    const unsigned char* kb = kc + (size_t)b * L_cap * tok_bytes + (size_t)g * 256;
+    const unsigned char* vb = vc + (size_t)b * L_cap * tok_bytes + (size_t)g * 256;
+    const int32_t* ir = idx + (size_t)row * k;
+    for (int t0 = first; t0 < k; t0 += step) {
+      uint4 x[2][16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int base = t0 + h * 128;
+      for (int h = 0; h < 2; ++h) {
+        const int base = t0 + h * ahead;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = base + 8 * q + (l >> 3);
-        int j = e < k ? ir[e] : -1;
-        j = (j >= 0 && j < L_cap) ? j : -1;
-        const size_t off = (size_t)(j < 0 ? 0 : j) * tok_bytes + 16 * (l & 7);
+        for (int q = 0; q < 4; ++q) {
+          const int e = base + 8 * q + (l >> 3);
+          int j = e < k ? ir[e] : -1;
+          j = (j >= 0 && j < L_cap) ? j : -1;
+          const size_t off = (size_t)(j < 0 ? 0 : j) * tok_bytes + 16 * (l & 7);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          x[h][4 * q + 2 * half] = j < 0 ? make_uint4(0, 0, 0, 0)
-                                         : *reinterpret_cast<const uint4*>(kb + off + 128 * half);
-          x[h][4 * q + 2 * half + 1] = j < 0 ? make_uint4(0, 0, 0, 0)
-                                             : *reinterpret_cast<const uint4*>(vb + off + 128 * half);
+          for (int half = 0; half < 2; ++half) {
+            x[h][4 * q + 2 * half] = j < 0 ? make_uint4(0, 0, 0, 0)
+                                           : *reinterpret_cast<const uint4*>(kb + off + 128 * half);
+            x[h][4 * q + 2 * half + 1] = j < 0 ? make_uint4(0, 0, 0, 0)
+                                               : *reinterpret_cast<const uint4*>(vb + off + 128 * half);
+          }
         }
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc ^= x[h][i].x ^ x[h][i].y ^ x[h][i].z ^ x[h][i].w;
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc ^= x[h][i].x ^ x[h][i].y ^ x[h][i].z ^ x[h][i].w;
   }
-  if (acc == 0x9E3779B9u) out[0] = acc;
+  hold[threadIdx.x] = acc;
+  __syncthreads();
+  if (hold[(threadIdx.x + 1) % kThreads] == 0x9E3779B9u) out[0] = acc;
 }
 
 // The least a hot-path kernel does: every workgroup reads one word of its
@@ -203,15 +222,23 @@ int dsa_roofline_gather(const void* buf, size_t buf_bytes, const int32_t* rows, 
 }
 
 int dsa_roofline_kv_gather(const void* k_cache, const void* v_cache, const int32_t* indices,
-                           int rows, int k, int S, int H_kv, int L_cap, void* sink, void* stream) {
+                           int rows, int k, int S, int H_kv, int L_cap, int wave_rows, void* sink,
+                           void* stream) {
   if (!k_cache || !v_cache || !indices || !sink || rows < 1 || k < 1 || S < 1 || H_kv < 1 ||
       L_cap < 1 || rows > 65535 || H_kv > 65535 || ((uintptr_t)k_cache & 15u) ||
       ((uintptr_t)v_cache & 15u))
     return 2;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(roof_kv_gather_kernel, dim3(1, H_kv, rows), dim3(kThreads), 0,
-                     (hipStream_t)stream, (const unsigned char*)k_cache,
-                     (const unsigned char*)v_cache, indices, k, S, H_kv, L_cap, (uint32_t*)sink);
+  if (wave_rows)
+    hipLaunchKernelGGL(roof_kv_gather_kernel<true>, dim3(H_kv * ((rows + 3) / 4)), dim3(kThreads),
+                       0, (hipStream_t)stream, (const unsigned char*)k_cache,
+                       (const unsigned char*)v_cache, indices, k, S, H_kv, L_cap, rows,
+                       (uint32_t*)sink);
+  else
+    hipLaunchKernelGGL(roof_kv_gather_kernel<false>, dim3(1, H_kv, rows), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const unsigned char*)k_cache,
+                       (const unsigned char*)v_cache, indices, k, S, H_kv, L_cap, rows,
+                       (uint32_t*)sink);
   return status("kv_gather");
 }
 

@@ -30,7 +30,7 @@ def _load():
     lib.dsa_roofline_gather.restype = i32
     lib.dsa_roofline_gather.argtypes = [vp, sz, vp, i32, vp, vp]
     lib.dsa_roofline_kv_gather.restype = i32
-    lib.dsa_roofline_kv_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.dsa_roofline_kv_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.dsa_roofline_floor.restype = i32
     lib.dsa_roofline_floor.argtypes = [vp, vp, i32, i32, vp]
     return lib
@@ -73,9 +73,10 @@ def floor(word, sink, workgroups, threads):
         "dsa_roofline_floor")
 
 
-def kv_gather(k_cache, v_cache, indices, S, sink):
+def kv_gather(k_cache, v_cache, indices, S, sink, wave_rows=False):
     B, L, H_kv, D = k_cache.shape
     rows, k = indices.shape[0] * indices.shape[1], indices.shape[-1]
     _ok(LIB.dsa_roofline_kv_gather(k_cache.data_ptr(), v_cache.data_ptr(), indices.data_ptr(), rows,
-                                   k, S, H_kv, L, sink.data_ptr(), _stream()),
+                                   k, S, H_kv, L, int(bool(wave_rows)), sink.data_ptr(),
+                                   _stream()),
         "dsa_roofline_kv_gather")
