@@ -44,29 +44,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "5b5c00305124b604",
+    "sources": "1d722cacd4afb100",
     "tiny_decode_1k": {
-        "indexer": 128055,
+        "indexer": 129080,
         "topk": 28287,
-        "attention": 83064
+        "attention": 81913
     },
     "spec_decode_32k": {
-        "indexer": 5434644,
-        "topk": 1302367,
-        "attention": 18136701
+        "indexer": 5435188,
+        "topk": 1302446,
+        "attention": 18117183
     },
     "prefill_128k": {
-        "indexer": 1125405584,
-        "topk": 1090159025,
-        "attention": 3429227926
+        "indexer": 1125406878,
+        "topk": 1089566959,
+        "attention": 1962470131
     },
     "int8_batched_decode_64k": {
-        "attention": 1154177024
+        "attention": 1154476018
     },
     "decode_256k": {
-        "indexer": 42209395,
-        "topk": 10667941,
-        "attention": 20357731
+        "indexer": 42209552,
+        "topk": 10672710,
+        "attention": 20334021
     }
 }
 
