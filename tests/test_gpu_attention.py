@@ -47,13 +47,24 @@ COMBOS = [
 ]
 
 
-def _run_case(dsa, combo, B, S, L, k, kv_len, decode, seed):
+def _schedule(dsa, g, idx, od, decode):
+    q = g["q"]
+    out = torch.empty(q.shape, dtype=torch_dtype(od), device=DEV)
+    a = dsa.attention_args(q, g["k_cache"], g["v_cache"], idx, g["kv_len"], out, g.get("k_scale"),
+                           g.get("v_scale"))
+    op = dsa.DSA_PLAN_ATTENTION_DECODE if decode else dsa.DSA_PLAN_ATTENTION_PREFILL
+    return dsa.plan_fields(dsa.dsa_describe_plan(op, attention=a))["schedule"]
+
+
+def _run_case(dsa, combo, B, S, L, k, kv_len, decode, seed, schedule=None):
     qd, kd, od, D, H_q, H_kv = combo
     w = scaled(SPEC_DECODE_32K, B=B, S=S, L=L, H_q=H_q, H_kv=H_kv, D=D, q_dtype=qd,
                kv_dtype=kd, out_dtype=od, k=k, H_idx=None, D_idx=None, seed=seed)
     x = make_inputs(w, kv_len=kv_len)
     idx = random_selection(np.random.default_rng(seed), x["kv_len"].tolist(), S, k, L)
     g = upload(x)
+    if schedule is not None:
+        assert _schedule(dsa, g, idx.to(DEV), od, decode) == schedule
     out = run_attention(dsa, g, idx.to(DEV), torch_dtype(od), decode=decode)
     torch.cuda.synchronize()
     ref = oracle.sparse_attention(x["q"], x["k_cache"], x["v_cache"], idx, x["kv_len"].tolist(),
@@ -69,6 +80,19 @@ def _run_case(dsa, combo, B, S, L, k, kv_len, decode, seed):
 @pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(map(str, c)))
 def test_attention_dtype_combos(dsa, combo, decode):
     _run_case(dsa, combo, B=2, S=3, L=600, k=150, kv_len=[600, 421], decode=decode, seed=31)
+
+
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(map(str, c)))
+def test_attention_prefill_whole_row_waves(dsa, combo):
+    """Prefill with at least 2048 (row, KV head) pairs runs whole-row waves (each
+    wave walks every tile of one row; 4 rows per workgroup, ragged last
+    workgroup).  Two sequences: the second one's first rows hold fewer keys
+    than k (-1 padding, partial tiles)."""
+    H_kv = combo[5]
+    S = -(-1024 // H_kv) + 1                   # 2 S H_kv >= 2048 pairs, S not a multiple of 4
+    L = S + 300
+    _run_case(dsa, combo, B=2, S=S, L=L, k=100, kv_len=[L, S + 37], decode=False, seed=36,
+              schedule="wave_rows")
 
 
 @pytest.mark.parametrize("decode", [True, False], ids=["decode", "prefill"])

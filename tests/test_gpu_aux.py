@@ -87,3 +87,15 @@ def test_aux_with_the_maximum_number_of_splits(dsa):
     # a long selection reaches the split cap; the aux keys take the last merge slot
     _run(dsa, ("f16", "f16", "f16", "f16", 64, 4, 1), B=1, S=1, S_aux=1, L=20000, k=9000,
          kv_len=[20000], decode=True, seed=45)
+
+
+@pytest.mark.parametrize("combo", [COMBOS[0], COMBOS[3], COMBOS[4]],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_aux_prefill_whole_row_waves(dsa, combo):
+    # >= 2048 (row, KV head) pairs: the main launch runs whole-row waves, each
+    # writing its row's partial next to the auxiliary split's (32 fresh tokens;
+    # the second sequence holds 40 tokens, so its early rows see few cache keys)
+    H_kv = combo[6]
+    S = -(-1024 // H_kv) + 1
+    _run(dsa, combo, B=2, S=S, S_aux=32, L=S + 300, k=100, kv_len=[S + 300, S], decode=False,
+         seed=44)
