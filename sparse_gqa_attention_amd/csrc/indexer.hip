@@ -685,9 +685,11 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
     // Decode (S <= 8): 4 waves x 1 token pair.  Up to two runs per CU: one
     // key run per workgroup, ~512 workgroups (at 8 x 32K keys, 64 keys each
     // measured 4.1 us against 4.9 us for 32 and 5.5 us for a full run of
-    // 256), runs of whole 32-key chunks.  More runs: stream up to four runs
-    // per workgroup (at 8 x 256K keys: 10.5 us for four runs, 11.1 us for
-    // two, 12.6-13.1 us for one-run workgroups).
+    // 256), runs of whole 32-key chunks.  More runs: stream them, enough
+    // runs per workgroup (at most four) that one dispatch round of two
+    // workgroups per CU covers the keys, so each CU has two runs' copies in
+    // flight (at 8 x 256K keys, two runs per workgroup, 512 workgroups:
+    // stage 12.35 us against 12.53 us for four runs on 256 workgroups).
     a.pairs = 1;
     a.waves = 4;
     a.tile = 32768 / (2 * D_idx);
@@ -695,7 +697,7 @@ IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
     const long long runs = ((long long)max_kv_len + a.tile - 1) / a.tile * B * a.tok_blocks;
     if (runs > 2LL * kNumCUs) {
       a.stream_decode = true;
-      long long rpw = (runs + kNumCUs - 1) / kNumCUs;
+      long long rpw = (runs + 2 * kNumCUs - 1) / (2 * kNumCUs);
       if (rpw > 4) rpw = 4;
       a.keys_per_wg = (int)(rpw * a.tile);
     } else {
