@@ -222,6 +222,34 @@ __device__ uint32_t select_bin_rel(const uint32_t* hist, uint32_t need, uint32_t
   return total;
 }
 
+// Exact selection inside one radix bin that holds at most a wave's worth of
+// keys: the bin's keys, appended to `list` (LDS, list[kWave] a zeroed append
+// counter), are ranked by wave 0, each lane comparing its key with all the
+// others (ties counted), instead of one or two more radix levels with their
+// histogram, scan and barriers.  res[0] = T, the need-th largest of the bin's
+// nb keys; res[1] = how many keys equal to T belong to the top `need`.
+// Block-wide: call after the appends, with every thread; 1 <= need <= nb.
+template <int NT>
+__device__ __forceinline__ void rank_small_bin(const uint32_t* list, uint32_t nb, uint32_t need,
+                                               uint32_t* res) {
+  __syncthreads();                             // the appends have landed
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    const uint32_t v = l < (int)nb ? list[l] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (int j = 0; j < (int)nb; ++j) {
+      const uint32_t x = list[j];
+      gt += x > v ? 1u : 0u;
+      ge += x >= v ? 1u : 0u;
+    }
+    if (l < (int)nb && gt < need && need <= ge) {   // the lanes holding T agree
+      res[0] = v;
+      res[1] = need - gt;
+    }
+  }
+  __syncthreads();
+}
+
 template <int NT, typename KeyOf>
 __device__ void radix_select_rel(KeyOf key_of, int count, uint32_t need, uint32_t base,
                                  uint32_t range, uint32_t* hist, uint32_t* scratch,
@@ -490,6 +518,20 @@ __device__ void radix_select_rel_pre(KeyOf key_of, int count, uint32_t need, uin
     need -= misc[2 * lvl + 1];
     prefix |= misc[2 * lvl] << lo;
     if (lo == 0) break;
+    const uint32_t nb = hist[misc[2 * lvl]];    // keys in the chosen bin (block-uniform)
+    if (nb <= (uint32_t)kWave) {
+      // few keys left: rank them in one wave (the next level's histogram,
+      // zeroed and unused, holds the list and its counter)
+      uint32_t* list = hists + (lvl + 1) * kRelBins;
+      for (int i = threadIdx.x; i < count; i += NT) {
+        const uint32_t k = key_of(i);
+        if (((k - base) >> lo) == (prefix >> lo)) list[atomicAdd(&list[kWave], 1u)] = k;
+      }
+      rank_small_bin<NT>(list, nb, need, misc + 2 * lvl + 2);
+      T = misc[2 * lvl + 2];
+      take = misc[2 * lvl + 3];
+      return;
+    }
     hi = lo;
   }
   T = base + prefix;
@@ -1052,6 +1094,18 @@ __device__ bool select_regs(const uint32_t (&key)[E], uint32_t vm, uint32_t base
   need -= misc[1];
   uint32_t prefix = base + (bA << shA);
   if (shA > 0) {
+    const uint32_t nb = hA[bA];                 // keys in the chosen bin (block-uniform)
+    if (nb <= (uint32_t)kWave) {
+      // few keys left: rank them in one wave; hB (zeroed, unused) holds the
+      // list and, at hB[kWave], its counter
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (((vm >> j) & 1u) && ((key[j] - base) >> shA) == bA) hB[atomicAdd(&hB[kWave], 1u)] = key[j];
+      rank_small_bin<NT>(hB, nb, need, misc + 2);
+      T = misc[2];
+      take = misc[3];
+      return true;
+    }
     const int shB = shA > kRelBits ? shA - kRelBits : 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
