@@ -211,7 +211,7 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* 
   CHECK(check_ptr(key_state, "key_state"));
   CHECK(check_ptr(kv_len, "kv_len"));
   CHECK(check_ptr(scores, "scores"));
-  dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, max_kv_len);
+  dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, L_cap, max_kv_len);
   l.q_idx = q_idx; l.w_idx = w_idx; l.key_state = key_state; l.kv_len = kv_len;
   l.scores = scores; l.H = H_idx; l.L_cap = L_cap; l.bf16 = idx_dtype == DSA_BF16;
   (void)hipGetLastError();
@@ -269,12 +269,17 @@ size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k,
     if ((long long)B * S == 0 || max_kv_len == 0) {
       d = "op=indexer kernels=none";
     } else {
-      const dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, max_kv_len);
+      const dsa::IndexerLaunch l = dsa::plan_indexer(B, S, D_idx, L_cap, max_kv_len);
       const bool stream = l.prefill || l.stream_decode;
-      appendf(d, "op=indexer kernel=%s grid=%dx%dx%d threads=%d waves=%d token_pairs_per_wave=%d "
-                 "keys_per_buffer=%d keys_per_workgroup=%d",
-              stream ? "indexer_stream_kernel" : "indexer_score_kernel", l.tok_blocks, l.key_blocks,
-              B, 64 * l.waves, l.waves, l.pairs, l.tile, l.keys_per_wg);
+      if (l.fold)
+        appendf(d, "op=indexer kernel=indexer_fold_kernel grid=%dx%dx%d threads=%d waves=%d "
+                   "tokens_per_workgroup=32 keys_per_workgroup=%d",
+                l.tok_blocks, l.key_blocks, B, 64 * l.waves, l.waves, l.keys_per_wg);
+      else
+        appendf(d, "op=indexer kernel=%s grid=%dx%dx%d threads=%d waves=%d token_pairs_per_wave=%d "
+                   "keys_per_buffer=%d keys_per_workgroup=%d",
+                stream ? "indexer_stream_kernel" : "indexer_score_kernel", l.tok_blocks,
+                l.key_blocks, B, 64 * l.waves, l.waves, l.pairs, l.tile, l.keys_per_wg);
     }
   } else if (op == DSA_PLAN_TOPK) {
     if (validate_topk_shape(B, S, L_cap, max_kv_len, k) != DSA_OK) return 0;

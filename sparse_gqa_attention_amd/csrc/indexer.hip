@@ -40,6 +40,8 @@
 // so key-state runs are read through L2 (about 33 MB of HBM-side fetch for
 // a 2048-token prefill at 128K, against 1 GiB of LDS copies) and every XCD
 // gets an equal share of every sequence.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -485,6 +487,195 @@ __global__ __launch_bounds__(WAVES * kWave, WPE) void indexer_stream_kernel(
                                                    wv, rs, row_off);
 }
 
+// ------------------------------------------------------------------ folded prefill
+// The score has no per-head nonlinearity, so
+//   sum_h w_h (q_h . k) = (sum_h w_h q_h) . k:
+// the prefill kernel folds the head weights into the query once per token
+// (q' in FP32; exact for integer inputs while its partial sums stay below
+// 2^24) and contracts q' with the keys: one 32-token x 32-key MFMA tile
+// instead of sixteen per-head tiles, so the stage is bound by its score
+// stores.  q' enters the MFMA in parts of the key's 16-bit type, each
+// multiplied by the exact key and accumulated in FP32:
+//   BF16: hi + mid + lo hold q's 24-bit significand (BF16 has FP32's range);
+//   FP16: hi + lo hold 22 bits; a token whose largest |q'| is 2^14 or more,
+//         or below 1, is scaled by a power of two first (into [2^13, 2^14))
+//         and its scores scaled back (both exact), so no part overflows or
+//         falls into FP16 subnormals.
+// A workgroup of 4 waves holds 32 tokens; wave w walks the 32-key chunks w,
+// w + 4, ... of the workgroup's key range, its B operands (the key rows)
+// loaded from global memory one chunk ahead; the key ranges of the token
+// blocks that share them run consecutively on one XCD (xcd_tile), so the
+// key rows come from that XCD's L2.
+constexpr int kFoldWaves = 4;
+constexpr int kFoldTokens = 32;
+
+template <typename T, int DI, int SPOL>
+__global__ __launch_bounds__(kFoldWaves * kWave) void indexer_fold_kernel(
+    const T* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const T* __restrict__ key_state, const int32_t* __restrict__ kv_len,
+    int S, int H, int L_cap, int keys_per_wg, float* __restrict__ scores) {
+  using V8 = typename vec8<T>::type;
+  constexpr bool kBF16 = std::is_same<T, __bf16>::value;
+  constexpr int kParts = kBF16 ? 3 : 2;
+  constexpr int NT = kFoldWaves * kWave;
+  constexpr int kSteps = DI / 16;
+  constexpr int kGroup = DI / 8;                 // threads per token in the fold
+  __shared__ float qf[kFoldTokens][DI + 4];      // folded queries, FP32
+  __shared__ float qexp[kFoldTokens];            // FP16: 2^-e of the token's scale
+
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
+  const int b = tz;
+  const int j_begin = ty * keys_per_wg;
+  const int s0 = tx * kFoldTokens;
+  const int wave = threadIdx.x / kWave;
+  const int l = lane_id();
+  int kvl = kv_len[b];
+  kvl = kvl < 0 ? 0 : (kvl > L_cap ? L_cap : kvl);
+  const int j_end = min(j_begin + keys_per_wg, kvl);
+  // keys beyond the last position of this block's tokens are never selected
+  const int last_pos = kvl - S + min(s0 + kFoldTokens, S) - 1;
+  if (j_begin >= j_end || j_begin > last_pos) return;   // block-uniform
+
+  // ---- q'[token][d] = sum_h w[token][h] q[token][h][d]: a thread per
+  // (token, 8 dims), 16-byte query loads; FP16 scales q' by 2^e (e <= 0)
+  static_assert(NT % kGroup == 0 && kGroup <= kWave, "a token's threads share a wave");
+  for (int e = threadIdx.x; e < kFoldTokens * kGroup; e += NT) {
+    const int tok = e / kGroup, d8 = e % kGroup;
+    const int s = s0 + tok;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (s < S) {
+      const size_t row = (size_t)b * S + s;
+      const T* qrow = q_idx + row * H * DI + 8 * d8;
+      const float* wrow = w_idx + row * H;
+      for (int h = 0; h < H; ++h) {
+        const float wh = wrow[h];
+        const uint4 raw = ld_vec<uint4>(qrow + (size_t)h * DI);
+        T v[8];
+        __builtin_memcpy(v, &raw, 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wh, to_f32(v[i]), acc[i]);
+      }
+    }
+    if constexpr (!kBF16) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(acc[i]));
+#pragma unroll
+      for (int o = kGroup / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+      // a largest |q'| of 2^14 or more is scaled below 2^14 (hi + lo stay
+      // finite), one below 1 up to [2^13, 2^14) (clear of FP16 subnormals);
+      // integer-valued q' (|q'| >= 1, or 0) is never scaled, so the
+      // integer-exact case is unchanged; 0 and non-finite keep e = 0
+      int ex = 0;
+      if (mx > 0.0f && mx <= 3.0e38f && (mx >= 16384.0f || mx < 1.0f)) {
+        int m;
+        (void)frexpf(mx, &m);                   // mx in [2^(m-1), 2^m)
+        ex = 14 - m;                            // mx * 2^ex in [2^13, 2^14)
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = ldexpf(acc[i], ex);
+      if (d8 == 0) qexp[tok] = ldexpf(1.0f, -ex);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[tok][8 * d8 + i] = acc[i];
+  }
+  __syncthreads();
+
+  // ---- A operands: lane l supplies token l % 32, dims 16 st + 8 (l / 32)
+  // + [0, 8) of each K-step, as kParts parts of the 16-bit type
+  V8 a[kParts][kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float r = qf[l & 31][16 * st + 8 * (l >> 5) + i];
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) {
+        const T part = from_f32<T>(r);
+        a[p][st][i] = part;
+        r -= to_f32(part);
+      }
+    }
+  }
+  // element v of lane l is token 8 (v / 4) + 4 (l / 32) + v % 4 of the tile
+  float post[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) post[v] = kBF16 ? 1.0f : qexp[8 * (v >> 2) + 4 * (l >> 5) + (v & 3)];
+
+  // ---- scores, key l % 32 of each chunk.  One buffer resource over the
+  // block's token rows: tokens past S fall outside it and are dropped, keys
+  // past the live range get an out-of-range offset.
+  const int n_tok = max(0, min(S - s0, kFoldTokens));
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(
+      scores + ((size_t)b * S + min(s0, S - 1)) * L_cap, (uint32_t)n_tok * (uint32_t)L_cap * 4u);
+  const uint32_t row_bytes = (uint32_t)__builtin_amdgcn_readfirstlane(L_cap * 4);
+  const T* ks_b = key_state + (size_t)b * L_cap * DI + 8 * (l >> 5);
+  // B operands of a chunk: lane l supplies key l % 32, dims 16 st + 8 (l / 32)
+  // + [0, 8); addresses clamped into the cache, so the loads are
+  // unconditional
+  auto load_b = [&](int jc, V8 (&bop)[kSteps]) {
+    const int key = min(jc + (l & 31), L_cap - 1);
+    const T* src = ks_b + (size_t)key * DI;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) bop[st] = __builtin_bit_cast(V8, ld_vec<uint4>(src + 16 * st));
+  };
+  constexpr int kStride = 32 * kFoldWaves;
+  // One chunk: the MFMAs on its B operands, then its 16 score stores.
+  auto chunk = [&](int jc, const V8 (&bop)[kSteps]) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) acc = mfma32x32x16(a[p][st], bop[st], acc);
+    }
+    // Lane part of the offset (token 4 (l / 32), key l % 32) with bit 31
+    // set for keys past the live range (beyond the resource: dropped), and
+    // the scalar part per element (token 8 (v / 4) + v % 4); no branch, so
+    // every chunk issues exactly 16 stores.
+    const int key = jc + (l & 31);
+    const uint32_t drop = ((uint32_t)(j_end - 1 - key) >> 31) << 31;
+    const uint32_t voff = (((uint32_t)(4 * (l >> 5)) * (uint32_t)L_cap + (uint32_t)key) * 4u) | drop;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const uint32_t soff = (uint32_t)(8 * (v >> 2) + (v & 3)) * row_bytes;
+      const float sc = kBF16 ? acc[v] : acc[v] * post[v];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs, voff, (int)soff, SPOL);
+    }
+  };
+  // Two chunks per trip, the operand sets swapping roles; each set is
+  // reloaded (one chunk ahead, clamped past the end) right after its chunk.
+  // The trip has no exit between its chunks (the compiler would sink the
+  // loads past it); a second chunk past the range stores nothing.  The
+  // scheduling barriers keep each load ahead of the chunk it overlaps.  The
+  // compiler's wait before a chunk counts the memory operations issued after
+  // that chunk's loads and takes the smaller count of the loop's entry and
+  // back edge; 16 dropped stores (distinct addresses, so none is merged away)
+  // in the prologue give the entry the same 20
+  // (16 stores, 4 loads) as every later trip, so no wait covers a store.
+  int jc = j_begin + 32 * wave;
+  if (jc >= j_end) return;                      // this wave has no chunk
+  // (the prologue sits in one block with the loop, so the compiler keeps
+  // its order)
+  V8 b0[kSteps], b1[kSteps];
+  load_b(jc, b0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    __builtin_amdgcn_raw_buffer_store_b32(0u, rs, kDropOffset + 4u * v, 0, SPOL);
+  load_b(jc + kStride, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  do {
+    chunk(jc, b0);
+    load_b(jc + 2 * kStride, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(jc + kStride, b1);
+    load_b(jc + 3 * kStride, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    jc += 2 * kStride;
+  } while (jc < j_end);
+}
+
 // ------------------------------------------------------------------ decode
 
 template <typename T, int DI, int PAIRS, int WAVES, int KR>
@@ -611,8 +802,22 @@ void launch_resident(const IndexerLaunch& a, hipStream_t st) {
 // Decode keeps one 32 KB run per workgroup (4 waves x 1 token pair).
 template <int DI> constexpr int kDecodeRun = 32768 / (2 * DI);
 
+template <typename T, int DI>
+void launch_fold(const IndexerLaunch& a, hipStream_t st) {
+  dim3 grid(a.tok_blocks, a.key_blocks, a.B);
+  hipLaunchKernelGGL((indexer_fold_kernel<T, DI, kStoreStreaming>), grid, dim3(kFoldWaves * kWave),
+                     0, st, (const T*)a.q_idx, a.w_idx, (const T*)a.key_state, a.kv_len, a.S, a.H,
+                     a.L_cap, a.keys_per_wg, a.scores);
+}
+
 template <typename T>
 void launch_idx_d(const IndexerLaunch& a, hipStream_t st) {
+  if (a.fold) {
+    if (a.D_idx == 32) launch_fold<T, 32>(a, st);
+    else if (a.D_idx == 64) launch_fold<T, 64>(a, st);
+    else launch_fold<T, 128>(a, st);
+    return;
+  }
   switch (a.D_idx) {
     case 32:
       if (a.prefill) launch_stream<T, 32>(a, st);
@@ -645,11 +850,30 @@ constexpr int kNumCUs = 256;
 
 }  // namespace
 
-IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len) {
+IndexerLaunch plan_indexer(int B, int S, int D_idx, int L_cap, int max_kv_len) {
   IndexerLaunch a{};
   a.B = B;
   a.S = S;
   a.D_idx = D_idx;
+  // Prefill (S > 8) folds the head weights into the query.  Its score
+  // stores address a 32-token block with 32-bit byte offsets: L_cap < 2^24.
+  if (S > 8 && L_cap < (1 << 24)) {
+    a.prefill = true;
+    a.fold = true;
+    a.waves = kFoldWaves;
+    a.pairs = 0;
+    a.tile = 0;
+    a.tok_blocks = (S + kFoldTokens - 1) / kFoldTokens;
+    // about 2048 workgroups (8 per CU), whole 128-key strides of the 4 waves
+    const long long tiles = (long long)B * a.tok_blocks;
+    long long kpw = ((long long)max_kv_len * tiles + 2047) / 2048;
+    kpw = ((kpw + 127) / 128) * 128;
+    if (kpw < 128) kpw = 128;
+    while ((((long long)max_kv_len + kpw - 1) / kpw + 7) / 8 * 8 > 65535) kpw *= 2;
+    a.keys_per_wg = (int)kpw;
+    a.key_blocks = (int)((((long long)max_kv_len + kpw - 1) / kpw + 7) & ~7LL);
+    return a;
+  }
   // Decode (S <= 8) keeps one run per workgroup; a context so long that its
   // key blocks would exceed the grid's y limit streams as prefill does.
   const bool prefill = S > 8 || (long long)max_kv_len > 60000LL * (32768 / (2 * D_idx));

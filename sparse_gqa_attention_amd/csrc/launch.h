@@ -20,6 +20,7 @@ struct IndexerLaunch {
   bool bf16;
   bool prefill;     // S > 8: 8-wave workgroups streaming key runs
   bool stream_decode;  // long decode context: 4-wave workgroups streaming key runs
+  bool fold;        // prefill: head weights folded into the query (indexer_fold_kernel)
   int pairs;        // token pairs per wave (1 or 2)
   int waves;        // waves per workgroup
   int tile;         // keys per LDS buffer
@@ -29,7 +30,7 @@ struct IndexerLaunch {
 };
 // Largest L_cap the indexer supports (32-bit byte offsets of score stores).
 constexpr int kIndexerMaxLcap = 1 << 27;
-IndexerLaunch plan_indexer(int B, int S, int D_idx, int max_kv_len);
+IndexerLaunch plan_indexer(int B, int S, int D_idx, int L_cap, int max_kv_len);
 void launch_indexer(const IndexerLaunch& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k

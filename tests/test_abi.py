@@ -297,9 +297,10 @@ def test_describe_plan_names_the_launches(dsa):
     assert f["chunk_grid"] == "25x32"
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 4, 262144, k=9000))
     assert f["mode"] == "exact" and f["chunk_grid"] == "0x4"
-    # 128K prefill: streaming indexer, one top-k workgroup per row
+    # 128K prefill: head-folded indexer, one top-k workgroup per row
     f = F(d(dsa.DSA_PLAN_INDEXER, 1, 2048, 131072, D_idx=64))
-    assert f["kernel"] == "indexer_stream_kernel" and f["waves"] == "8"
+    assert f["kernel"] == "indexer_fold_kernel" and f["grid"] == "64x32x1"
+    assert f["keys_per_workgroup"] == "4096"
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 2048, 131072, k=2048))
     assert f["plan"] == "stream" and f["grid"] == "2048"
     # ... and whole-row attention waves (4 rows per workgroup, KV head j % 2)

@@ -42,11 +42,11 @@ SAMPLE_ROWS = {
 EXPECTED_PLANS = {
     "tiny_decode_1k": ("indexer_score_kernel", "resident", "attention_decode/split"),
     "spec_decode_32k": ("indexer_score_kernel", "resident", "attention_decode/split"),
-    "prefill_128k": ("indexer_stream_kernel", "stream", "attention_prefill/wave_rows"),
+    "prefill_128k": ("indexer_fold_kernel", "stream", "attention_prefill/wave_rows"),
     "int8_batched_decode_64k": (None, None, "attention_decode/split"),
     "decode_256k": ("indexer_stream_kernel", "split", "attention_decode/split"),
     "ragged_decode_256k": ("indexer_stream_kernel", "split", "attention_decode/split"),
-    "ragged_prefill_64k": ("indexer_stream_kernel", "stream", "attention_prefill/wave_rows"),
+    "ragged_prefill_64k": ("indexer_fold_kernel", "stream", "attention_prefill/wave_rows"),
 }
 
 
