@@ -23,6 +23,11 @@ extern "C" {
 /* Reads `bytes` (a multiple of 16) from src with 16-byte loads. */
 int dsa_roofline_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/* Writes every byte of dst[0..bytes) (16-byte aligned, bytes % 16 == 0) with
+ * 16-byte non-temporal stores, one per thread, in address order: the
+ * streaming-write ceiling.  bytes / 4096 < 2^31. */
+int dsa_roofline_write(void* dst, size_t bytes, void* stream);
+
 /* Copies `bytes` (a multiple of 16) from src to dst with 16-byte loads and stores. */
 int dsa_roofline_copy(const void* src, void* dst, size_t bytes, void* stream);
 

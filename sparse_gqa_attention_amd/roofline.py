@@ -8,7 +8,7 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_roofline.so")
-EXPORTS = ("dsa_roofline_read", "dsa_roofline_copy", "dsa_roofline_mfma",
+EXPORTS = ("dsa_roofline_read", "dsa_roofline_write", "dsa_roofline_copy", "dsa_roofline_mfma",
            "dsa_roofline_mfma_flops", "dsa_roofline_gather", "dsa_roofline_kv_gather",
            "dsa_roofline_floor")
 
@@ -21,6 +21,8 @@ def _load():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.dsa_roofline_read.restype = i32
     lib.dsa_roofline_read.argtypes = [vp, sz, vp, vp]
+    lib.dsa_roofline_write.restype = i32
+    lib.dsa_roofline_write.argtypes = [vp, sz, vp]
     lib.dsa_roofline_copy.restype = i32
     lib.dsa_roofline_copy.argtypes = [vp, vp, sz, vp]
     lib.dsa_roofline_mfma.restype = i32
@@ -51,6 +53,11 @@ def _ok(rc, what):
 def read(src, sink):
     _ok(LIB.dsa_roofline_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
                               _stream()), "dsa_roofline_read")
+
+
+def write(dst):
+    _ok(LIB.dsa_roofline_write(dst.data_ptr(), dst.numel() * dst.element_size(), _stream()),
+        "dsa_roofline_write")
 
 
 def copy(src, dst):

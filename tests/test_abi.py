@@ -263,7 +263,7 @@ def test_roofline_probe_library_exports_its_header():
     header = os.path.join(ROOT, "include", "dsa_roofline.h")
     lib = C.CDLL(os.path.join(ROOT, "sparse_gqa_attention_amd", "libdsa_roofline.so"))
     names = declared_functions(header)
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa_roofline.h but not exported"
     from sparse_gqa_attention_amd import roofline
