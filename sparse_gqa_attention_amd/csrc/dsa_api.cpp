@@ -295,7 +295,7 @@ size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k,
     } else {
       const int nch = (max_kv_len + p.chunk - 1) / p.chunk;
       appendf(d, "op=topk plan=split kernels=topk_chunk_kernel,topk_select_kernel "
-                 "chunk_grid=%dx%d chunk_threads=256 select_grid=%d select_threads=512 "
+                 "chunk_grid=%dx%d chunk_threads=512 select_grid=%d select_threads=512 "
                  "chunk=%d chunks=%d sample=%d slots=%d spec=%d entries=%d mode=%s workspace=%zu",
               p.exact_only ? 0 : nch, p.rows, p.rows, p.chunk, p.chunks, p.sample, p.cap, p.spec,
               p.entries, p.exact_only ? "exact" : (p.spec > 0 ? "fast" : "general"), p.ws_bytes);

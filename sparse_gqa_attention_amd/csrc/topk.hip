@@ -871,7 +871,7 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // ====================================================================== split plan
 // Few rows (B*S < 128) of any length.  Each row is cut into chunks of CH keys.
 //
-// K1, topk_chunk_kernel: one 256-thread workgroup per (chunk, row).  Every
+// K1, topk_chunk_kernel: one 512-thread workgroup per (chunk, row).  Every
 // workgroup of a row draws the same sample of the row and computes the same
 // sample threshold T_lo (a kernel of its own, or a hand-off between
 // workgroups, costs more than recomputing it).  The sample is spread over the
@@ -897,8 +897,8 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // equals the selection on the row.  Otherwise (a threshold above the k-th
 // key, a chunk with more candidates than slots, a list longer than LDS holds)
 // K2 selects exactly from the whole row.
-constexpr int kChunkThreads = 256;
-static_assert(kChunkThreads == kSampleBlock, "lane t takes element t of every sample block");
+constexpr int kChunkThreads = 512;
+static_assert(kChunkThreads % kSampleBlock == 0, "whole sample blocks per pass of the lanes");
 constexpr int kSelThreads = 512;
 constexpr int kListCap = 8192;          // candidates the general path holds in LDS
 static_assert(kListCap < 65536, "ordered emission packs counts in 16 bits");
@@ -956,7 +956,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     int span, int k, int nch_ws, int cap, int spec, int e_log2, int tpc_log2, SplitWs w) {
   constexpr int NT = kChunkThreads;
   constexpr int CH = U * NT;
-  constexpr int NB = NS / kSampleBlock;        // sample keys per lane
+  constexpr int SPL = NS / NT;                 // sample keys per lane
+  constexpr int BPP = NT / kSampleBlock;       // sample blocks per pass of the lanes
   __shared__ __attribute__((aligned(16))) uint32_t h0[kBins];
   __shared__ __attribute__((aligned(16))) uint32_t h1[kBins];
   __shared__ uint32_t scratch[32];
@@ -969,19 +970,29 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   // ---- chunk keys and the sample: every load in flight before kv_len is known
   float v[U];
   if (VEC && jl + U <= L_cap) {                // rows 16-byte aligned (L_cap % 4 == 0)
+    if constexpr (U % 4 == 0) {
 #pragma unroll
-    for (int q = 0; q < U / 4; ++q) {
-      const float4 x = reinterpret_cast<const float4*>(src + jl)[q];
-      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+      for (int q = 0; q < U / 4; ++q) {
+        const float4 x = reinterpret_cast<const float4*>(src + jl)[q];
+        v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < U / 2; ++q) {
+        const float2 x = reinterpret_cast<const float2*>(src + jl)[q];
+        v[2 * q] = x.x; v[2 * q + 1] = x.y;
+      }
     }
   } else {
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = jl + u < L_cap ? src[jl + u] : 0.0f;
   }
-  float sv[NB];
+  // lane t takes element t % 256 of sample blocks BPP u + t / 256
+  const int se = t % kSampleBlock, sb = t / kSampleBlock;
+  float sv[SPL];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int p = sample_block_base<NS>(u, span) + t;
+  for (int u = 0; u < SPL; ++u) {
+    const int p = sample_block_base<NS>(BPP * u + sb, span) + se;
     sv[u] = src[p < span ? p : 0];             // span <= L_cap
   }
   for (int i = t; i < kBins; i += NT) { h0[i] = 0u; h1[i] = 0u; }
@@ -997,8 +1008,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     sspan = n;
     nsv = sample_valid<NS>(n, n);
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int p = sample_block_base<NS>(u, n) + t;
+    for (int u = 0; u < SPL; ++u) {
+      const int p = sample_block_base<NS>(BPP * u + sb, n) + se;
       sv[u] = src[p < n ? p : 0];
     }
   }
@@ -1006,12 +1017,12 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
 
   // ---- sample threshold: two radix levels (key bits [31:21], [20:10]); the
   // largest sampled key sizes the select kernel's digits
-  uint32_t sk[NB];
+  uint32_t sk[SPL];
   uint32_t smax = 0u, sok = 0u;
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
+  for (int u = 0; u < SPL; ++u) {
     sk[u] = score_key(sv[u]);
-    if (sample_block_base<NS>(u, sspan) + t < slim) {
+    if (sample_block_base<NS>(BPP * u + sb, sspan) + se < slim) {
       sok |= 1u << u;
       smax = max(smax, sk[u]);
     }
@@ -1019,7 +1030,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   smax = wave_inclusive_max_u32(smax);
   __syncthreads();                             // histograms zeroed
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
+  for (int u = 0; u < SPL; ++u)
     if ((sok >> u) & 1u) atomicAdd(&h0[sk[u] >> 21], 1u);
   if (lane_id() == kWave - 1) atomicMax(&misc[4], smax);
   __syncthreads();
@@ -1028,7 +1039,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   const uint32_t b0 = misc[0];
   need -= misc[1];
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
+  for (int u = 0; u < SPL; ++u)
     if (((sok >> u) & 1u) && (sk[u] >> 21) == b0) atomicAdd(&h1[(sk[u] >> 10) & 0x7FFu], 1u);
   __syncthreads();
   select_bin<NT>(h1, need, scratch, misc + 2);
@@ -1045,9 +1056,15 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   // The lane's keys go to LDS so that the write loop visits its hits only
   // (a key picked by a per-lane bit index cannot be read from registers).
   // Each lane reads back only what it wrote itself: no barrier.
+  if constexpr (U % 4 == 0) {
 #pragma unroll
-  for (int q = 0; q < U / 4; ++q)
-    reinterpret_cast<float4*>(chunk + U * t)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    for (int q = 0; q < U / 4; ++q)
+      reinterpret_cast<float4*>(chunk + U * t)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < U / 2; ++q)
+      reinterpret_cast<float2*>(chunk + U * t)[q] = make_float2(v[2 * q], v[2 * q + 1]);
+  }
   uint32_t total;
   uint32_t pos = block_exclusive_scan<NT>((uint32_t)__popc(hits), scratch, &total);
   if (total <= (uint32_t)cap) {
@@ -1377,10 +1394,10 @@ void launch_chunk_ns(int U, bool vec, dim3 grid, hipStream_t st, const float* sc
                      const int32_t* kv_len, int S, int L_cap, int span, int k, int nch_ws, int cap,
                      int spec, int el, int tl, SplitWs w) {
   switch (U) {
+    case 2: launch_chunk<2, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
     case 4: launch_chunk<4, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
     case 8: launch_chunk<8, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
-    case 16: launch_chunk<16, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
-    default: launch_chunk<32, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
+    default: launch_chunk<16, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
   }
 }
 }  // namespace

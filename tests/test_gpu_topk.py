@@ -238,3 +238,79 @@ def test_topk_very_long_rows(dsa):
     r = rng(19)
     sc = torch.from_numpy(r.standard_normal((1, 2, 4_500_000)).astype(np.float32))
     _check(dsa, sc, [4_500_000], 2048, what="4.5M keys")
+
+
+
+@pytest.mark.parametrize("B,S,L,k,kv", [
+    (8, 8, 65536, 2048, [65536, 60000, 4000, 2049, 2048, 9, 65536, 31000]),   # 64 rows, ragged
+    (1, 3, 100003, 1500, [100003]),                # 3 rows, L % 4 = 3
+    (1, 1, 262144, 4096, [262144])])               # one long row, k = 4096
+def test_topk_few_rows_indexer_like_and_normal(dsa, B, S, L, k, kv):
+    r = rng(30 + B * S)
+    _check(dsa, indexer_like_scores(r, (B, S, L)), kv, k, what="indexer-like")
+    _check(dsa, torch.from_numpy(r.standard_normal((B, S, L)).astype(np.float32)), kv, k,
+           what="normal")
+
+
+@pytest.mark.parametrize("L", [32768, 262144])
+def test_topk_repeated_calls_and_graph_replays(dsa, L):
+    # No state carries from one call to the next: 40 calls in a row and 5
+    # replays of a captured graph of 20 calls (one shared workspace for the
+    # two-kernel plan at 256K), each result checked.
+    B, S, k = 1, 8, 2048
+    r = rng(40)
+    sc_cpu = indexer_like_scores(r, (B, S, L))
+    want = np.stack([oracle.topk_row(sc_cpu[0, s], L - S + s, k) for s in range(S)])
+    sc = sc_cpu.to(DEV)
+    kv = torch.tensor([L], dtype=torch.int32, device=DEV)
+    outs = [torch.full((B, S, k), -7, dtype=torch.int32, device=DEV) for _ in range(40)]
+    for o in outs:
+        dsa.dsa_topk(sc, kv, k, o)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert np.array_equal(o.cpu().numpy()[0], want), f"call {i}"
+    need = dsa.dsa_topk_workspace_bytes(B, S, L, k)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV) if need > 0 else None
+    gouts = [torch.full((B, S, k), -7, dtype=torch.int32, device=DEV) for _ in range(20)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for o in gouts:
+                dsa.dsa_topk(sc, kv, k, o, workspace=ws)
+    for rep in range(5):
+        for o in gouts:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(gouts):
+            assert np.array_equal(o.cpu().numpy()[0], want), f"replay {rep} call {i}"
+
+
+def test_topk_two_streams_at_once(dsa):
+    # Calls in flight together on two streams, each with its own workspace.
+    B, S, L, k = 1, 8, 65536, 2048
+    r = rng(41)
+    a_cpu = indexer_like_scores(r, (B, S, L))
+    b_cpu = torch.from_numpy(r.standard_normal((B, S, L)).astype(np.float32))
+    kv = torch.tensor([L], dtype=torch.int32, device=DEV)
+    a, b = a_cpu.to(DEV), b_cpu.to(DEV)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(6):
+        oa = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
+        ob = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
+        with torch.cuda.stream(s1):
+            dsa.dsa_topk(a, kv, k, oa)
+        with torch.cuda.stream(s2):
+            dsa.dsa_topk(b, kv, k, ob)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    want_a = np.stack([oracle.topk_row(a_cpu[0, s], L - S + s, k) for s in range(S)])
+    want_b = np.stack([oracle.topk_row(b_cpu[0, s], L - S + s, k) for s in range(S)])
+    for rep, (oa, ob) in enumerate(outs):
+        assert np.array_equal(oa.cpu().numpy()[0], want_a), f"stream 1, call {rep}"
+        assert np.array_equal(ob.cpu().numpy()[0], want_b), f"stream 2, call {rep}"
