@@ -44,29 +44,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "1d722cacd4afb100",
+    "sources": "347e45cfa4fcd804",
     "tiny_decode_1k": {
-        "indexer": 129080,
-        "topk": 28287,
-        "attention": 81913
+        "indexer": 129083,
+        "topk": 31102,
+        "attention": 81912
     },
     "spec_decode_32k": {
-        "indexer": 5435188,
-        "topk": 1302446,
-        "attention": 18117183
+        "indexer": 5436811,
+        "topk": 1324902,
+        "attention": 18116652
     },
     "prefill_128k": {
-        "indexer": 1125406878,
-        "topk": 1089566959,
-        "attention": 1962470131
+        "indexer": 1186375683,
+        "topk": 1090370366,
+        "attention": 1944912995
     },
     "int8_batched_decode_64k": {
-        "attention": 1154476018
+        "attention": 1156052047
     },
     "decode_256k": {
-        "indexer": 42209552,
-        "topk": 10672710,
-        "attention": 20334021
+        "indexer": 42209248,
+        "topk": 10642357,
+        "attention": 20333932
     }
 }
 
@@ -186,8 +186,7 @@ def roofline_entry(w, stage, work, us, ceilings):
         c = ceilings.get("attention_gather_gbps")
         gb = work["gathered"] / sec / 1e9
         e.update(achieved=round(gb, 1), bytes_per_call=work["gathered"], peak=c,
-                 frac=round(gb / c, 4) if c else None, ceiling_name="attention_gather_gbps",
-                 hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+                 frac=round(gb / c, 4) if c else None, ceiling_name="attention_gather_gbps")
     else:
         e.update(peak=HBM_PEAK_GBPS, frac=round(gbps / HBM_PEAK_GBPS, 4))
         # the indexer's bytes are mostly its score stores, the others' loads
@@ -202,9 +201,11 @@ def roofline_entry(w, stage, work, us, ceilings):
         e["mfma_tflops"] = round(tf, 2)
         e["mfma_frac"] = round(tf / MFMA_PEAK_TFLOPS, 4)
     if stage == "indexer" and work.get("flops"):
-        # the method's per-head FLOP count over the stage time; the prefill
-        # kernel folds the head weights into the query and issues fewer
+        # the method's per-head FLOP count over the stage time
         e["mfma_frac_algorithmic"] = round(work["flops"] / sec / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        if not w.decode_form:
+            e["mfma_note"] = ("per-head FLOP count; the prefill kernel folds the head weights into "
+                              "the query and issues 3/16 (BF16) or 2/16 (FP16) of it")
     return e
 
 
@@ -599,6 +600,11 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
         # HBM-side bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE
         # (null once the kernel sources differ from the measured ones)
         roof[st]["traffic"] = measured.get(st)
+        if roof[st]["bound"] == "gather" and measured.get(st):
+            # the gathered rows' HBM-side share: measured traffic per call
+            # over the stage time, against the HBM peak
+            roof[st]["hbm_traffic_frac"] = round(
+                measured[st] / (stage_d[st]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
     path_gbps = work["path"]["bytes"] / (step_d["mean"] * 1e-6) / 1e9
     res = {
         "us_per_layer": step_d,
