@@ -1,11 +1,12 @@
 """Benchmark of the dynamic sparse GQA attention hot path on one MI355X.
 
 One step = the whole hot path (indexer score -> top-k -> sparse attention)
-run once per "layer" over N distinct layer buffer sets whose total footprint
-exceeds 1 GiB, so that no layer's key-state or KV cache is still resident in
-the 256 MB Infinity Cache when it is read again.  The reported value is the
-time per layer (microseconds): step time / N, on the speculative-decode
-workload at 32K context (B1 S8, FP16 KV).  The other four workloads (1K tiny
+run once per "layer", cycling through N distinct layer buffer sets whose
+total footprint exceeds 1 GiB (so that no layer's key-state or KV cache is
+still resident in the 256 MB Infinity Cache when it is read again), for at
+least 32 layers.  The reported value is the time per layer (microseconds):
+step time / layers, on the speculative-decode workload at 32K context (B1
+S8, FP16 KV).  The other four workloads (1K tiny
 decode, 128K prefill chunk, INT8 batched decode at 64K, 256K decode) are
 timed the same way and reported under `by_workload`.
 
@@ -16,8 +17,9 @@ torch.cuda.CUDAGraph) and replayed, as a decode step is in a serving loop
 replays after K untimed ones, each replay with its own event pair (mean,
 p10, p90), then K replays of a graph of each stage alone.  Each stage gets a
 roofline against the bound that fits it: HBM bytes for the decode stages and
-the top-k, MFMA flops for the prefill indexer, and for the prefill
-attention the random-row gather rate measured in the same run.  Ceilings
+the top-k, the score write for the prefill indexer (with its per-head
+FLOP rate beside it), and for the prefill attention the rate at which the
+same rows are gathered with no compute, measured in the same run.  Ceilings
 (streaming read and copy, a BF16 MFMA loop, 256-byte row gathers, and a
 graph of do-nothing kernels with the step's grids) are measured first.
 The CPU baseline times the FP64 oracle on the host on a bounded sample.
@@ -70,6 +72,9 @@ MEASURED_TRAFFIC = {
     }
 }
 
+MIN_LAYER_STEPS = 32            # layers per timed step (a deep model's step)
+MIN_TOUCHED = 512 << 20         # bytes read per pass over the layer sets (2x the Infinity Cache)
+MAX_SET_BYTES = 48 << 30        # device memory the layer sets may take
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense BF16/FP16 MFMA
 ELT = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
@@ -172,7 +177,7 @@ def stage_bound(w, stage):
     return "hbm"
 
 
-def roofline_entry(w, stage, work, us, ceilings):
+def roofline_entry(w, stage, work, us, ceilings, fold_parts=0):
     bound = stage_bound(w, stage)
     sec = us * 1e-6
     e = {"bound": bound, "us_per_call": round(us, 3)}
@@ -201,11 +206,17 @@ def roofline_entry(w, stage, work, us, ceilings):
         e["mfma_tflops"] = round(tf, 2)
         e["mfma_frac"] = round(tf / MFMA_PEAK_TFLOPS, 4)
     if stage == "indexer" and work.get("flops"):
-        # the method's per-head FLOP count over the stage time
-        e["mfma_frac_algorithmic"] = round(work["flops"] / sec / 1e12 / MFMA_PEAK_TFLOPS, 4)
-        if not w.decode_form:
-            e["mfma_note"] = ("per-head FLOP count; the prefill kernel folds the head weights into "
-                              "the query and issues 3/16 (BF16) or 2/16 (FP16) of it")
+        # the method's per-head FLOP count over the stage time, and the MFMA
+        # work the kernel issues: the same for the per-head kernels; the
+        # folded prefill kernel contracts one folded query, taken in
+        # fold_parts 16-bit parts, instead of H_idx heads
+        e["per_head_tflops"] = round(work["flops"] / sec / 1e12, 1)
+        issued = work["flops"] * (fold_parts / w.H_idx if fold_parts else 1.0)
+        e["mfma_tflops"] = round(issued / sec / 1e12, 1)
+        e["mfma_frac"] = round(issued / sec / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        if fold_parts:
+            e["mfma_note"] = (f"head weights folded into the query: {fold_parts} MFMA parts per "
+                              f"(token, key) tile against {w.H_idx} heads in the per-head form")
     return e
 
 
@@ -387,9 +398,23 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
     kv_len = x["kv_len"].tolist()
     layer_bytes = sum(v.numel() * v.element_size() for v in x.values()
                       if isinstance(v, torch.Tensor))
-    n_layers = args.layers or min(512, max(2, -(-(1 << 30) // layer_bytes)))
+    # Distinct sets: at least 1 GiB of buffers, and at least MIN_TOUCHED bytes
+    # read per pass over them (key-state rows, gathered K/V rows, queries):
+    # a layer reads only a fraction of its KV cache, and each set must leave
+    # the Infinity Cache before it is read again.
+    touched = stage_work(w, kv_len)["path"]["bytes"]
+    n_layers = args.layers or min(512, max(2, -(-(1 << 30) // layer_bytes),
+                                          -(-MIN_TOUCHED // max(1, touched))))
+    while not args.layers and n_layers > 2 and n_layers * layer_bytes > MAX_SET_BYTES:
+        n_layers -= 1
     layers = [{kk: (v.to(dev) if isinstance(v, torch.Tensor) else v) for kk, v in x.items()}
               for _ in range(n_layers)]
+    # A step runs at least MIN_LAYER_STEPS layers, cycling through the
+    # distinct sets (each set recurs only after every other set has passed
+    # through the Infinity Cache), so that one replay's launch overhead is
+    # spread over as many layers as a deep model's step has, whatever the
+    # set count.
+    seq = layers * max(1, -(-MIN_LAYER_STEPS // n_layers))
     B, S, L = w.B, w.S, w.L
     scores = torch.empty((B, S, L), dtype=torch.float32, device=dev) if w.has_indexer else None
     idx = torch.empty((B, S, w.k), dtype=torch.int32, device=dev)
@@ -426,12 +451,12 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
     stages = (["indexer", "topk"] if w.has_indexer else []) + ["attention"]
 
     def step():
-        for g in layers:
+        for g in seq:
             for st in stages:
                 stage(st, g)
 
     fns = {"step": step}
-    fns.update({st: (lambda st=st: [stage(st, g) for g in layers]) for st in stages})
+    fns.update({st: (lambda st=st: [stage(st, g) for g in seq]) for st in stages})
 
     # The launch floor: the step's kernels as do-nothing kernels (each
     # workgroup reads one word) with the same grids, replayed the same way.
@@ -448,7 +473,7 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
     floor_launches = [(min(g, 65535), t) for g, t in floor_launches]
 
     def floor_step():
-        for _ in layers:
+        for _ in seq:
             for g, t in floor_launches:
                 rl.floor(word, sink, g, t)
     fns["floor"] = floor_step
@@ -493,9 +518,9 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
             attn(g["q"], g["k_cache"], g["v_cache"], ind, g["kv_len"], out,
                  k_scale=g["k_scale"], v_scale=g["v_scale"], workspace=aux_ws, max_kv_len=mx,
                  aux_k=aux["aux_k"], aux_v=aux["aux_v"])
-        fns["cache_append"] = lambda: [append_stage(g) for g in layers]
-        fns["rmsnorm_rope"] = lambda: [rope_stage() for _ in layers]
-        fns["attention_aux"] = lambda: [attention_aux_stage(g) for g in layers]
+        fns["cache_append"] = lambda: [append_stage(g) for g in seq]
+        fns["rmsnorm_rope"] = lambda: [rope_stage() for _ in seq]
+        fns["attention_aux"] = lambda: [attention_aux_stage(g) for g in seq]
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -586,7 +611,7 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
         gathered = stage_work(w, kv_len)["attention"]["gathered"]
         ceilings = dict(ceilings, attention_gather_gbps=round(gathered / best / 1e9, 1))
 
-    per_layer = lambda d: {kk: round(v * 1e3 / n_layers, 3) for kk, v in d.items()}
+    per_layer = lambda d: {kk: round(v * 1e3 / len(seq), 3) for kk, v in d.items()}
     step_d = per_layer(dist(run["step"], K))
     stage_d = {st: per_layer(dist(run[st], K)) for st in stages}
     floor_d = per_layer(dist(run["floor"], K))
@@ -594,7 +619,11 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
                                                           "attention_aux") if st in run}
     eager_d = per_layer(dist(step, max(3, K // 5))) if mode != "eager" else step_d
     work = stage_work(w, kv_len)
-    roof = {st: roofline_entry(w, st, work[st], stage_d[st]["mean"], ceilings) for st in stages}
+    fold_parts = 0
+    if w.has_indexer and "indexer_fold_kernel" in plans.get("indexer", ""):
+        fold_parts = 3 if w.idx_dtype == "bf16" else 2
+    roof = {st: roofline_entry(w, st, work[st], stage_d[st]["mean"], ceilings, fold_parts)
+            for st in stages}
     measured = MEASURED_TRAFFIC.get(w.name, {}) if sources_digest() == MEASURED_TRAFFIC["sources"] else {}
     for st in stages:
         # HBM-side bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE
@@ -610,7 +639,8 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
         "us_per_layer": step_d,
         "tokens_per_s": round(B * S / (step_d["mean"] * 1e-6), 1),
         "launch_mode": mode,
-        "layers_per_step": n_layers,
+        "layers_per_step": len(seq),
+        "layer_sets": n_layers,
         "eager_us_per_layer": eager_d["mean"],
         "stage_us": stage_d,
         "stage_roofline": roof,
@@ -642,7 +672,7 @@ def run_workload(w, args, torch, dev, ceilings, x, extras):
                           "attention_aux": "attention with the step's S newest tokens as "
                                            "auxiliary K/V"}[st] + "; measured on its own, not in value"}
             for st, v in extra_d.items()}
-    del layers, scores, idx, out, topk_ws, attn_ws
+    del seq, layers, scores, idx, out, topk_ws, attn_ws
     torch.cuda.empty_cache()
     return res
 
@@ -711,6 +741,8 @@ def main():
         "us_per_layer": main_res["us_per_layer"],
         "tokens_per_s": main_res["tokens_per_s"],
         "launch_mode": main_res["launch_mode"],
+        "layers_per_step": main_res["layers_per_step"],
+        "layer_sets": main_res["layer_sets"],
         "eager_us_per_layer": main_res["eager_us_per_layer"],
         "launch_floor_us_per_layer": main_res["launch_floor_us_per_layer"],
         "path": main_res["path"],
