@@ -221,7 +221,8 @@ dsa_status dsa_indexer_score(const void* q_idx, const float* w_idx, const void* 
 
 size_t dsa_topk_workspace_bytes(int B, int S, int L_cap, int k) {
   if (B <= 0 || S <= 0 || L_cap < 1 || k < 1 || L_cap > (1 << 24)) return 0;
-  return dsa::plan_topk(B, S, L_cap, k).ws_bytes;
+  // the plan of the largest runtime bound, max_kv_len = L_cap (no shorter bound needs more)
+  return dsa::plan_topk(B, S, L_cap, L_cap, k).ws_bytes;
 }
 
 dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, int L_cap,
@@ -232,7 +233,7 @@ dsa_status dsa_topk(const float* scores, const int32_t* kv_len, int B, int S, in
   CHECK(check_ptr(scores, "scores"));
   CHECK(check_ptr(kv_len, "kv_len"));
   CHECK(check_ptr(indices, "indices"));
-  dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, k);
+  dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, max_kv_len, k);
   if (p.ws_bytes > 0) {
     if (workspace_bytes < p.ws_bytes)
       return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
@@ -283,9 +284,12 @@ size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k,
     }
   } else if (op == DSA_PLAN_TOPK) {
     if (validate_topk_shape(B, S, L_cap, max_kv_len, k) != DSA_OK) return 0;
-    const dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, k);
+    const dsa::TopkPlan p = dsa::plan_topk(B, S, L_cap, max_kv_len, k);
     if (p.rows == 0) {
       d = "op=topk kernels=none";
+    } else if (p.kind == 3) {
+      appendf(d, "op=topk plan=wave kernel=topk_wave_kernel grid=%d threads=256 rows_per_workgroup=4 "
+                 "keys_per_lane=%d workspace=0", (p.rows + 3) / 4, p.lane_keys);
     } else if (p.kind == 0) {
       appendf(d, "op=topk plan=stream kernel=topk_stream_kernel grid=%d threads=1024 workspace=0",
               p.rows);

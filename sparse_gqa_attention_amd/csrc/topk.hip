@@ -7,14 +7,15 @@
 //
 // 1. Threshold estimate.  A sample of the row (all of it when the row is
 //    short, else blocks of 256 consecutive keys spread evenly over the row:
-//    2048 keys for an LDS-resident row, 8192 when streaming, 4096 in the
-//    multi plan) goes through two radix levels (the top 11 + 11 key bits) to the
+//    2048 keys for an LDS-resident row, 8192 when streaming, 2048 or 4096 in
+//    the split plan) goes through two radix levels (the top 11 + 11 key bits) to the
 //    bin of the key of rank r = ceil(1.2e + 4 sqrt(e)) + 8, where e = k *
 //    sample / n is the expected sample rank of the k-th largest key.  The
 //    bin's lower edge T_lo is at or below that key; every key >= T_lo is a
 //    candidate (about 1.2k + 4 sqrt(e) n/sample keys).
 // 2. Collection.  One pass over the row lists the candidates; the resident
-//    and multi plans keep the list in index order.
+//    and split plans keep the list in index order.
+// (The wave plan for short rows skips steps 1-2: it selects on the whole row.)
 // 3. Exact selection on the list, in LDS: radix select of the k-th largest
 //    key T (index-ordered lists: 12-bit digits of key - T_lo, two levels
 //    for key spans below 2^24).  When only some of the keys equal to T fit,
@@ -30,7 +31,11 @@
 // passes) and emits from selection/tie bitmaps, carrying the tie count
 // across segments.  Every path computes the same, exact result.
 //
-// Plans (host-chosen from B*S and L_cap):
+// Plans (host-chosen from B*S, L_cap and the runtime bound max_kv_len):
+//  * wave      -- rows of at most 4096 keys (max_kv_len), any number of
+//    rows: one wave per row holds the row in registers and selects exactly
+//    on 8-bit digits of key - (the row's smallest key), with no threshold
+//    estimate and no workgroup barrier.
 //  * resident  -- few rows of <= 32768 keys (speculative decode at 32K): one
 //    1024-thread workgroup per row loads the row once into LDS (128 KB of
 //    keys) and does everything there.
@@ -38,12 +43,11 @@
 //    1024-thread workgroup per row reading the row ~1.06 times (two
 //    workgroups per CU: at most 64 VGPRs, four 16-byte loads per lane in
 //    flight).
-//  * multi     -- few rows longer than 32768 keys (decode at 256K): KA (one
-//    workgroup per row) computes T_lo and resets the row's pool counter, KB
-//    (many workgroups per row) lists each chunk's candidates in index order
-//    in the chunk's own slots (or a block of the row's pool), KC (one
-//    workgroup per row) gathers the chunks in order, selects and emits.
-//    Kernel boundaries order the three.
+//  * split     -- few rows longer than 32768 keys (decode at 256K): K1 (one
+//    workgroup per chunk of a row) recomputes the row's sample threshold and
+//    lists the chunk's candidates in index order in the chunk's own slots;
+//    K2 (one workgroup per row) selects exactly on the chunks' lists and
+//    emits.  The kernel boundary orders the two.
 #include <cmath>
 
 #include "dsa_device.h"
@@ -67,7 +71,7 @@ static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits t
 constexpr int kStreamLoads = 4;        // 16-byte loads per lane in flight (streaming plan)
 static_assert(4 * kStreamLoads <= 32, "one hit bit per key of a lane's step");
 
-enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanSplit = 2 };
+enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanSplit = 2, kPlanWave = 3 };
 
 // Radix levels: key bits [31:21], [20:10], [9:0].
 __device__ __forceinline__ int lvl_shift(int lvl) { return lvl == 0 ? 21 : (lvl == 1 ? 10 : 0); }
@@ -868,6 +872,166 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
                        regionA + kSegWords, out, s);
 }
 
+// ====================================================================== wave plan
+// Short rows: every row at most kWaveKeys keys long (by the runtime bound
+// max_kv_len), any number of rows.  One wave per row, kWaveRows rows per
+// workgroup, no workgroup barrier (each wave touches only its own LDS).  Lane
+// l holds keys [KPL l, KPL l + KPL) of its row in registers, so the lanes hold
+// the row in index order.  Exact selection on 8-bit radix digits of
+// key - kmin (kmin, kmax: the row's smallest and largest live keys; the first
+// level takes the top 8 bits of kmax - kmin): each level is a 256-bin LDS
+// histogram of the keys that share the digits chosen so far and one wave scan
+// over its bins.  Once the chosen bin holds at most 64 keys, the wave ranks
+// them directly (each lane compares its key with all of them, ties counted).
+// Ordered emission: one wave scan of the lanes' (above, tie) counts.
+constexpr int kWaveKeys = 4096;
+constexpr int kWaveRows = 4;
+constexpr int kWaveBins = 256;
+static_assert(kWaveBins == 4 * kWave, "a lane zeroes and reads four bins");
+static_assert(kWaveKeys < 65536, "emission packs counts in 16 bits");
+
+// Orders this wave's LDS accesses around cross-lane exchanges (lanes of one
+// wave execute each LDS instruction together, in program order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_max_u32(v), kWave - 1);
+}
+
+template <int KPL, bool VEC>
+__global__ __launch_bounds__(kWaveRows * kWave) void topk_wave_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
+    int rows, int k, int32_t* __restrict__ indices) {
+  static_assert(KPL % 4 == 0 && KPL * kWave <= kWaveKeys, "whole 16-byte loads per lane");
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[kWaveRows][kWaveBins];
+  __shared__ __attribute__((aligned(16))) uint32_t list_all[kWaveRows][kWave + 4];
+  const int wave = threadIdx.x / kWave, l = lane_id();
+  const int row = blockIdx.x * kWaveRows + wave;
+  if (row >= rows) return;
+  uint32_t* hist = hist_all[wave];
+  uint32_t* list = list_all[wave];
+  const float* src = scores + (size_t)row * L_cap;
+  int32_t* out = indices + (size_t)row * k;
+  const int j0 = KPL * l;
+
+  // ---- the lane's keys; the loads go out before kv_len is known (they stay
+  // inside the L_cap-long row)
+  uint32_t key[KPL];
+  if (VEC && j0 + KPL <= L_cap) {              // rows 16-byte aligned (L_cap % 4 == 0)
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+      const float4 x = reinterpret_cast<const float4*>(src + j0)[q];
+      key[4 * q] = __float_as_uint(x.x); key[4 * q + 1] = __float_as_uint(x.y);
+      key[4 * q + 2] = __float_as_uint(x.z); key[4 * q + 3] = __float_as_uint(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) key[u] = j0 + u < L_cap ? __float_as_uint(src[j0 + u]) : 0u;
+  }
+  // rows are at most max_kv_len <= KPL * 64 keys long
+  const int n = min(row_count(kv_len, row, S, L_cap), KPL * kWave);
+  if (n <= k) {
+    for (int i = l; i < k; i += kWave) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int nv = n - j0;                       // keys of this lane inside the row (may be <= 0)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    key[u] = score_key(__uint_as_float(key[u]));
+    if (u < nv) { kmin = min(kmin, key[u]); kmax = max(kmax, key[u]); }
+  }
+  kmax = wave_max_uniform(kmax);
+  kmin = ~wave_max_uniform(~kmin);
+
+  // ---- exact selection: T = the k-th largest key, take = how many keys
+  // equal to T are kept
+  const uint32_t range = kmax - kmin;
+  int hi = range ? 32 - __clz(range) : 0;      // bits [sh, hi) of key - kmin are this level's
+  uint32_t need = (uint32_t)k, prefix = 0u;    // digits fixed so far (bits >= hi)
+  uint32_t T, take;
+  while (true) {
+    const int sh = hi > 8 ? hi - 8 : 0;
+    reinterpret_cast<uint4*>(hist)[l] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const uint32_t d = key[u] - kmin;
+      if (u < nv && (hi >= 32 || (d >> hi) == (prefix >> hi))) atomicAdd(&hist[(d >> sh) & 0xFFu], 1u);
+    }
+    wave_lds_sync();
+    // lane l holds bins 255 - 4 l - i, i = 0..3 (highest first)
+    const uint4 q = reinterpret_cast<const uint4*>(hist)[kWave - 1 - l];
+    const uint32_t h[4] = {q.w, q.z, q.y, q.x};
+    const uint32_t local = h[0] + h[1] + h[2] + h[3];
+    uint32_t before = wave_inclusive_scan(local) - local;
+    int bin = -1;
+    uint32_t above = 0u, cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (before < need && need <= before + h[i]) { bin = kWaveBins - 1 - (4 * l + i); above = before; cnt = h[i]; }
+      before += h[i];
+    }
+    const int fl = (int)__builtin_ctzll(__ballot(bin >= 0)) & (kWave - 1);   // the one finder
+    bin = __builtin_amdgcn_readlane(bin, fl);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)above, fl);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, fl);
+    need -= above;
+    prefix |= (uint32_t)bin << sh;
+    if (sh == 0) { T = kmin + prefix; take = need; break; }
+    if (cnt <= (uint32_t)kWave) {
+      // the bin's keys into the list (zero-padded to whole 16-byte reads:
+      // every key is above 0, the key of no FP32 value but a negative NaN)
+      uint32_t c = 0u;
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        const bool in = u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh);
+        const uint64_t m = __ballot(in);
+        if (in) list[c + wave_prefix_count(m)] = key[u];
+        c += (uint32_t)__popcll(m);
+      }
+      if (l < 4) list[cnt + l] = 0u;
+      wave_lds_sync();
+      const uint32_t x = l < (int)cnt ? list[l] : 0u;
+      uint32_t gt = 0u, ge = 0u;
+      for (uint32_t j = 0; j < cnt; j += 4) {
+        const uint4 y = *reinterpret_cast<const uint4*>(list + j);
+        gt += (y.x > x) + (y.y > x) + (y.z > x) + (y.w > x);
+        ge += (y.x >= x) + (y.y >= x) + (y.z >= x) + (y.w >= x);
+      }
+      const bool hit = l < (int)cnt && gt < need && need <= ge;   // the lanes holding T agree
+      const int hl = (int)__builtin_ctzll(__ballot(hit)) & (kWave - 1);
+      T = (uint32_t)__builtin_amdgcn_readlane((int)x, hl);
+      take = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, hl);
+      break;
+    }
+    hi = sh;
+    wave_lds_sync();                           // bins read before the next level zeroes them
+  }
+
+  // ---- ordered emission: the lanes hold the row in index order
+  uint32_t gtc = 0u, eqc = 0u;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    gtc += (u < nv && key[u] > T) ? 1u : 0u;
+    eqc += (u < nv && key[u] == T) ? 1u : 0u;
+  }
+  const uint32_t packed = gtc | (eqc << 16);
+  const uint32_t ex = wave_inclusive_scan(packed) - packed;
+  uint32_t g = ex & 0xFFFFu, e = ex >> 16;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const bool above = u < nv && key[u] > T, tie = u < nv && key[u] == T;
+    if (above || (tie && e < take)) out[g + min(e, take)] = j0 + u;
+    g += above ? 1u : 0u;
+    e += tie ? 1u : 0u;
+  }
+}
+
 // ====================================================================== split plan
 // Few rows (B*S < 128) of any length.  Each row is cut into chunks of CH keys.
 //
@@ -1316,10 +1480,17 @@ using StreamPlan = StreamCfg<kStreamThreads, kRowCap>;
 
 }  // namespace
 
-TopkPlan plan_topk(int B, int S, int L_cap, int k) {
+TopkPlan plan_topk(int B, int S, int L_cap, int max_kv_len, int k) {
   TopkPlan p{};
   p.rows = B * S;
   const long long rows = p.rows;
+  if (max_kv_len <= kWaveKeys) {
+    p.kind = kPlanWave;
+    int kpl = 8;
+    while (kpl * kWave < max_kv_len) kpl *= 2;
+    p.lane_keys = kpl;
+    return p;
+  }
   if (rows >= 128) {
     p.kind = kPlanStream;
     return p;
@@ -1400,6 +1571,16 @@ void launch_chunk_ns(int U, bool vec, dim3 grid, hipStream_t st, const float* sc
     default: launch_chunk<16, NS>(vec, grid, st, scores, kv_len, S, L_cap, span, k, nch_ws, cap, spec, el, tl, w); break;
   }
 }
+template <int KPL>
+void launch_wave(bool vec, dim3 grid, hipStream_t st, const float* scores, const int32_t* kv_len,
+                 int S, int L_cap, int rows, int k, int32_t* indices) {
+  if (vec)
+    hipLaunchKernelGGL((topk_wave_kernel<KPL, true>), grid, dim3(kWaveRows * kWave), 0, st, scores,
+                       kv_len, S, L_cap, rows, k, indices);
+  else
+    hipLaunchKernelGGL((topk_wave_kernel<KPL, false>), grid, dim3(kWaveRows * kWave), 0, st, scores,
+                       kv_len, S, L_cap, rows, k, indices);
+}
 }  // namespace
 
 void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, int S,
@@ -1417,6 +1598,16 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
   switch (p.kind) {
+    case kPlanWave: {
+      const dim3 grid((p.rows + kWaveRows - 1) / kWaveRows);
+      switch (p.lane_keys) {
+        case 8: launch_wave<8>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
+        case 16: launch_wave<16>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
+        case 32: launch_wave<32>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
+        default: launch_wave<64>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
+      }
+      return;
+    }
     case kPlanStream:
       if (vec4)
         hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap, true>), dim3(p.rows),

@@ -288,6 +288,13 @@ def test_describe_plan_names_the_launches(dsa):
     f = F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))
     assert f["schedule"] == "split" and f["grid"] == "1x2x8" and "merge_grid" not in f
     assert f["workspace"] == "0"
+    # rows of at most 4096 keys (by the runtime bound): one wave per row
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 1, 1024, k=128))
+    assert f["plan"] == "wave" and f["grid"] == "1" and f["keys_per_lane"] == "16"
+    f = F(d(dsa.DSA_PLAN_TOPK, 3, 50, 262144, max_kv_len=4096, k=300))
+    assert f["plan"] == "wave" and f["grid"] == "38" and f["keys_per_lane"] == "64"
+    assert dsa.dsa_topk_workspace_bytes(1, 8, 4096, 2048) == 0
+    assert F(d(dsa.DSA_PLAN_TOPK, 1, 8, 4097, k=2048))["plan"] == "resident"
     # 256K decode: the two-kernel split top-k on its fast path
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 262144, k=2048))
     assert f["plan"] == "split" and f["chunk_grid"] == "32x8" and f["mode"] == "fast"

@@ -241,6 +241,54 @@ def test_topk_very_long_rows(dsa):
 
 
 
+@pytest.mark.parametrize("B,S,L,k,kv,bound", [
+    (1, 1, 1024, 128, [1024], 1024),                  # one decode row, 16 keys per lane
+    (1, 8, 4096, 2048, [4096], 4096),                 # 64 keys per lane, k = half the row
+    (1, 2, 500, 7, [500], 500),                       # 8 keys per lane, lanes past the row
+    (3, 50, 4000, 300, [4000, 2500, 60], 4000),       # 150 rows, ragged, partial last workgroup
+    (2, 7, 3001, 1, [3001, 17], 3001),                # L % 4 = 1 (element loads), k = 1
+    (1, 9, 2050, 2045, [2050], 2050),                 # k close to n, k >= n on the first rows
+    (2, 4, 262144, 512, [3000, 4096], 4096)])         # a long cache under a short runtime bound
+def test_topk_wave_plan_short_rows(dsa, B, S, L, k, kv, bound):
+    # Rows of at most 4096 keys by the runtime bound: one wave per row holds
+    # the row in registers and selects on its radix digits directly.
+    plan = dsa.plan_fields(dsa.dsa_describe_plan(dsa.DSA_PLAN_TOPK, B, S, L, bound, k=k))
+    assert plan["plan"] == "wave" and plan["workspace"] == "0"
+    r = rng(50 + L + k)
+    for what, sc in (("normal", torch.from_numpy(r.standard_normal((B, S, L)).astype(np.float32))),
+                     ("ints[-3,3]", integer_scores(r, (B, S, L), -3, 3)),
+                     ("indexer-like", indexer_like_scores(r, (B, S, L)))):
+        g_kv = torch.tensor(kv, dtype=torch.int32, device=DEV)
+        idx = run_topk(dsa, sc.to(DEV), g_kv, k, max_kv_len=bound)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            for s in range(S):
+                want = oracle.topk_row(sc[b, s], kv[b] - S + s, k)
+                assert np.array_equal(got[b, s], want), \
+                    f"wave {what} row ({b},{s}): {first_mismatch(got[b, s], want)}"
+
+
+def test_topk_wave_plan_exact_digits_and_deep_levels(dsa):
+    # Short rows whose k-th key sits in a cluster of tied or nearly equal keys
+    # under a wide key range (keys of +-1e30 at two positions), so that the
+    # chosen bin holds more than 64 keys at every level down to the last
+    # digit; a row of one value; a row of two values.
+    r = rng(60)
+    B, S, L = 1, 6, 4096
+    sc = np.empty((B, S, L), dtype=np.float32)
+    sc[0, 0] = 1.0 + r.integers(0, 256, size=L) * 2.0 ** -23         # low 8 bits differ
+    sc[0, 1] = 1.0 + r.integers(0, 1 << 16, size=L) * 2.0 ** -23     # low 16 bits differ
+    sc[0, 2] = 1.0 + r.integers(0, 1 << 24, size=L) * 2.0 ** -23     # low 24 bits differ
+    for s in range(3):
+        sc[0, s, 17], sc[0, s, 3000] = 1e30, -1e30
+    sc[0, 3] = 7.0
+    sc[0, 4] = np.where(np.arange(L) % 3 == 0, 5.0, 4.0)
+    sc[0, 5] = r.standard_normal(L)
+    sc = torch.from_numpy(sc)
+    for k in (1, 2, 100, 1365, 1366, 1367, 4000, 4090):
+        _check(dsa, sc, [L], k, what=f"wave deep k={k}")
+
+
 @pytest.mark.parametrize("B,S,L,k,kv", [
     (8, 8, 65536, 2048, [65536, 60000, 4000, 2049, 2048, 9, 65536, 31000]),   # 64 rows, ragged
     (1, 3, 100003, 1500, [100003]),                # 3 rows, L % 4 = 3
