@@ -46,29 +46,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "347e45cfa4fcd804",
+    "sources": "0279b996629b830d",
     "tiny_decode_1k": {
-        "indexer": 129083,
-        "topk": 31102,
-        "attention": 81912
+        "indexer": 129085,
+        "topk": 20353,
+        "attention": 81913
     },
     "spec_decode_32k": {
-        "indexer": 5436811,
-        "topk": 1324902,
-        "attention": 18116652
+        "indexer": 5436208,
+        "topk": 1309515,
+        "attention": 18115619
     },
     "prefill_128k": {
-        "indexer": 1186375683,
-        "topk": 1090370366,
-        "attention": 1944912995
+        "indexer": 1185979323,
+        "topk": 1090086837,
+        "attention": 1912310836
     },
     "int8_batched_decode_64k": {
-        "attention": 1156052047
+        "attention": 1154849080
     },
     "decode_256k": {
-        "indexer": 42209248,
-        "topk": 10642357,
-        "attention": 20333932
+        "indexer": 42208248,
+        "topk": 10669093,
+        "attention": 20332586
     }
 }
 
