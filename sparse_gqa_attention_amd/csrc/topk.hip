@@ -36,9 +36,10 @@
 //    rows: one wave per row holds the row in registers and selects exactly
 //    on 8-bit digits of key - (the row's smallest key), with no threshold
 //    estimate and no workgroup barrier.
-//  * resident  -- few rows of <= 32768 keys (speculative decode at 32K): one
-//    1024-thread workgroup per row loads the row once into LDS (128 KB of
-//    keys) and does everything there.
+//  * resident  -- few rows of <= 32768 keys by max_kv_len, whatever the
+//    cache capacity (speculative decode at 32K): one 1024-thread workgroup
+//    per row loads the row once into LDS (128 KB of keys) and does
+//    everything there.
 //  * streaming -- many rows (prefill: 2048 rows of 131072 keys): one
 //    1024-thread workgroup per row reading the row ~1.06 times (two
 //    workgroups per CU: at most 64 VGPRs, four 16-byte loads per lane in
@@ -554,7 +555,7 @@ constexpr size_t kResLds = (size_t)(kResKeys + kBins + 32 + kMiscWords + kResCap
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_resident_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int k, int vec4, int32_t* __restrict__ indices) {
+    int span, int k, int vec4, int32_t* __restrict__ indices) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   float* rowf = reinterpret_cast<float*>(lds);
   uint32_t* rowk = lds;
@@ -564,15 +565,16 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   const float* src = scores + (size_t)row * L_cap;
   int32_t* out = indices + (size_t)row * k;
 
-  // ---- the whole row into LDS, every load in flight at once.  With
-  // 16-byte rows the loads are direct global -> LDS copies that cover the
-  // L_cap-long row and go out before the row's length is known (no wait for
-  // kv_len).
+  // ---- the whole row into LDS, every load in flight at once.  Rows hold
+  // at most span = min(L_cap, max_kv_len) <= 32768 keys (the runtime bound:
+  // a long cache may hold short rows).  With 16-byte rows the loads are
+  // direct global -> LDS copies that cover the span and go out before the
+  // row's length is known (no wait for kv_len).
   if (vec4) {
     // direct global -> LDS copies: a wave's 64 lanes fill 1 KB of the row
     // at a time (lane l's 16 bytes at the wave's base + 16 l)
     constexpr int U = kResKeys / 4 / NT;
-    const int L4 = L_cap / 4;                   // L_cap % 4 == 0
+    const int L4 = (span + 3) / 4;              // <= L_cap / 4 (L_cap % 4 == 0)
     const float4* src4 = reinterpret_cast<const float4*>(src);
     float4* row4 = reinterpret_cast<float4*>(rowf);
     const int wbase = t - lane_id();
@@ -584,14 +586,14 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
                                          (__attribute__((address_space(3))) void*)(row4 + u * NT + wbase),
                                          16, 0, 0);
     }
-    const int n = row_count(kv_len, row, S, L_cap);
+    const int n = min(row_count(kv_len, row, S, L_cap), span);
     if (n <= k) {
       wait_vmem();                              // no copy may land after the workgroup ends
       write_all<NT>(out, n, k);
       return;
     }
   } else {
-    const int n = row_count(kv_len, row, S, L_cap);
+    const int n = min(row_count(kv_len, row, S, L_cap), span);
     if (n <= k) { write_all<NT>(out, n, k); return; }
     constexpr int U = 8;
     for (int b0 = 0; b0 < n; b0 += U * NT) {
@@ -608,7 +610,7 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
       }
     }
   }
-  const int n = row_count(kv_len, row, S, L_cap);
+  const int n = min(row_count(kv_len, row, S, L_cap), span);
   // The sample threshold's two histograms: hist, and the list area, which
   // is free until the candidates are listed.
   uint32_t* h1 = lidx;
@@ -709,8 +711,8 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   uint32_t* sel = s.hist;
   uint32_t* tie = s.hist + kBins / 2;
   const int lane = lane_id();
-  const int span = ((n + 63) / 64) * 64;
-  for (int r = t; r < span; r += NT) {
+  const int n64 = ((n + 63) / 64) * 64;
+  for (int r = t; r < n64; r += NT) {
     const bool valid = r < n;
     const uint32_t key = valid ? score_key(rowf[r]) : 0u;
     const uint64_t mg = __ballot(valid && key > T);
@@ -1495,7 +1497,7 @@ TopkPlan plan_topk(int B, int S, int L_cap, int max_kv_len, int k) {
     p.kind = kPlanStream;
     return p;
   }
-  if (L_cap <= kResKeys) {
+  if (max_kv_len <= kResKeys) {
     p.kind = kPlanResident;
     return p;
   }
@@ -1620,7 +1622,7 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
       return;
     case kPlanResident:
       hipLaunchKernelGGL((topk_resident_kernel<kResThreads>), dim3(p.rows), dim3(kResThreads), kResLds, st,
-                         scores, kv_len, S, L_cap, k, vec4, indices);
+                         scores, kv_len, S, L_cap, min(L_cap, max_kv_len), k, vec4, indices);
       return;
     default: {
       SplitWs w = split_carve(ws, p.rows, p.chunks);

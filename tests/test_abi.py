@@ -295,6 +295,9 @@ def test_describe_plan_names_the_launches(dsa):
     assert f["plan"] == "wave" and f["grid"] == "38" and f["keys_per_lane"] == "64"
     assert dsa.dsa_topk_workspace_bytes(1, 8, 4096, 2048) == 0
     assert F(d(dsa.DSA_PLAN_TOPK, 1, 8, 4097, k=2048))["plan"] == "resident"
+    # the runtime bound, not the capacity, picks the plan
+    f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 262144, max_kv_len=32768, k=2048))
+    assert f["plan"] == "resident" and f["workspace"] == "0"
     # 256K decode: the two-kernel split top-k on its fast path
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 8, 262144, k=2048))
     assert f["plan"] == "split" and f["chunk_grid"] == "32x8" and f["mode"] == "fast"

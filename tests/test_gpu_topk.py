@@ -218,6 +218,30 @@ def test_topk_resident_rows_unaligned_short_and_at_capacity(dsa):
     _check(dsa, sc, [32768, 9000], 1, what="resident k=1, ragged")
 
 
+def test_topk_short_runtime_bound_in_a_long_cache_uses_the_resident_plan(dsa):
+    # A 256K-capacity cache whose live lengths stay under 32768 keys: the
+    # plan follows the runtime bound max_kv_len, and the resident workgroup
+    # reads only the bound's span of each row.
+    B, S, L, k = 2, 4, 262144, 2048
+    plan = dsa.plan_fields(dsa.dsa_describe_plan(dsa.DSA_PLAN_TOPK, B, S, L, 30001, k=k))
+    assert plan["plan"] == "resident" and plan["workspace"] == "0"
+    r = rng(23)
+    sc = r.standard_normal((B, S, L)).astype(np.float32)
+    sc[:, :, 30001:] = np.inf                   # beyond the bound: never read
+    kv = [30001, 12000]
+    g_kv = torch.tensor(kv, dtype=torch.int32, device=DEV)
+    for what, m in (("normal", sc), ("indexer-like", indexer_like_scores(r, (B, S, L)).numpy())):
+        m = m.copy()
+        m[:, :, 30001:] = np.inf
+        idx = run_topk(dsa, torch.from_numpy(m).to(DEV), g_kv, k, max_kv_len=30001)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            for s in range(S):
+                want = oracle.topk_row(m[b, s], kv[b] - S + s, k)
+                assert np.array_equal(got[b, s], want), \
+                    f"bounded resident {what} row ({b},{s}): {first_mismatch(got[b, s], want)}"
+
+
 def test_topk_streaming_rows_unaligned_and_ragged(dsa):
     # The many-rows plan with row lengths that are not a multiple of 4
     # (element loads, no 16-byte path), ragged sequences, a sequence whose
