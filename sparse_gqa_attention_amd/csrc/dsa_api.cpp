@@ -288,8 +288,8 @@ size_t dsa_describe_plan(int op, int B, int S, int L_cap, int max_kv_len, int k,
     if (p.rows == 0) {
       d = "op=topk kernels=none";
     } else if (p.kind == 3) {
-      appendf(d, "op=topk plan=wave kernel=topk_wave_kernel grid=%d threads=256 rows_per_workgroup=4 "
-                 "keys_per_lane=%d workspace=0", (p.rows + 3) / 4, p.lane_keys);
+      appendf(d, "op=topk plan=small kernel=topk_small_kernel grid=%d threads=256 "
+                 "keys_per_thread=%d workspace=0", p.rows, p.lane_keys);
     } else if (p.kind == 0) {
       appendf(d, "op=topk plan=stream kernel=topk_stream_kernel grid=%d threads=1024 workspace=0",
               p.rows);

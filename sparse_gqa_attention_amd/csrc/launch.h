@@ -35,7 +35,7 @@ void launch_indexer(const IndexerLaunch& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
 struct TopkPlan {
-  int kind;            // streaming / resident / split / wave
+  int kind;            // streaming / resident / split / small
   int rows;            // B*S
   int chunk;           // keys per chunk workgroup (split)
   int chunks;          // chunks per row of L_cap keys (split; the workspace's layout)
@@ -44,7 +44,7 @@ struct TopkPlan {
   int spec;            // slots per chunk the select kernel loads up front (split; 0: none)
   int entries;         // candidates per lane of the select kernel's fast path (split)
   int exact_only;      // k beyond the candidate list: exact selection over whole rows
-  int lane_keys;       // keys per lane (wave)
+  int lane_keys;       // keys per thread (small)
   size_t ws_bytes;     // workspace the plan needs
 };
 TopkPlan plan_topk(int B, int S, int L_cap, int max_kv_len, int k);

@@ -15,7 +15,7 @@
 //    candidate (about 1.2k + 4 sqrt(e) n/sample keys).
 // 2. Collection.  One pass over the row lists the candidates; the resident
 //    and split plans keep the list in index order.
-// (The wave plan for short rows skips steps 1-2: it selects on the whole row.)
+// (The small plan for short rows skips steps 1-2: it selects on the whole row.)
 // 3. Exact selection on the list, in LDS: radix select of the k-th largest
 //    key T (index-ordered lists: 12-bit digits of key - T_lo, two levels
 //    for key spans below 2^24).  When only some of the keys equal to T fit,
@@ -32,10 +32,10 @@
 // across segments.  Every path computes the same, exact result.
 //
 // Plans (host-chosen from B*S, L_cap and the runtime bound max_kv_len):
-//  * wave      -- rows of at most 4096 keys (max_kv_len), any number of
-//    rows: one wave per row holds the row in registers and selects exactly
-//    on 8-bit digits of key - (the row's smallest key), with no threshold
-//    estimate and no workgroup barrier.
+//  * small     -- rows of at most 4096 keys (max_kv_len), any number of
+//    rows: one 256-thread workgroup per row holds the row in registers and
+//    selects exactly on 8-bit digits of key - (the row's smallest key), with
+//    no threshold estimate.
 //  * resident  -- few rows of <= 32768 keys by max_kv_len, whatever the
 //    cache capacity (speculative decode at 32K): one 1024-thread workgroup
 //    per row loads the row once into LDS (128 KB of keys) and does
@@ -72,7 +72,7 @@ static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits t
 constexpr int kStreamLoads = 4;        // 16-byte loads per lane in flight (streaming plan)
 static_assert(4 * kStreamLoads <= 32, "one hit bit per key of a lane's step");
 
-enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanSplit = 2, kPlanWave = 3 };
+enum PlanKind { kPlanStream = 0, kPlanResident = 1, kPlanSplit = 2, kPlanSmall = 3 };
 
 // Radix levels: key bits [31:21], [20:10], [9:0].
 __device__ __forceinline__ int lvl_shift(int lvl) { return lvl == 0 ? 21 : (lvl == 1 ? 10 : 0); }
@@ -874,54 +874,46 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
                        regionA + kSegWords, out, s);
 }
 
-// ====================================================================== wave plan
-// Short rows: every row at most kWaveKeys keys long (by the runtime bound
-// max_kv_len), any number of rows.  One wave per row, kWaveRows rows per
-// workgroup, no workgroup barrier (each wave touches only its own LDS).  Lane
-// l holds keys [KPL l, KPL l + KPL) of its row in registers, so the lanes hold
-// the row in index order.  Exact selection on 8-bit radix digits of
-// key - kmin (kmin, kmax: the row's smallest and largest live keys; the first
-// level takes the top 8 bits of kmax - kmin): each level is a 256-bin LDS
-// histogram of the keys that share the digits chosen so far and one wave scan
-// over its bins.  Once the chosen bin holds at most 64 keys, the wave ranks
-// them directly (each lane compares its key with all of them, ties counted).
-// Ordered emission: one wave scan of the lanes' (above, tie) counts.
-constexpr int kWaveKeys = 4096;
-constexpr int kWaveRows = 4;
-constexpr int kWaveBins = 256;
-static_assert(kWaveBins == 4 * kWave, "a lane zeroes and reads four bins");
-static_assert(kWaveKeys < 65536, "emission packs counts in 16 bits");
-
-// Orders this wave's LDS accesses around cross-lane exchanges (lanes of one
-// wave execute each LDS instruction together, in program order).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_max_u32(v), kWave - 1);
-}
+// ====================================================================== small plan
+// Short rows: every row at most kSmallKeys keys long (by the runtime bound
+// max_kv_len), any number of rows.  One 256-thread workgroup per row; thread
+// t holds keys [KPL t, KPL t + KPL) of its row in registers, so the threads
+// hold the row in index order.  There is no threshold estimate: exact
+// selection runs on 8-bit radix digits of key - kmin (kmin, kmax: the row's
+// smallest and largest live keys; the first level takes the top 8 bits of
+// kmax - kmin), each level one 256-bin LDS histogram of the keys that share
+// the digits chosen so far.  Every wave scans the whole histogram itself
+// (the four waves reach the same bin), so a level costs one barrier, and the
+// levels' histograms are zeroed up front.  Once the chosen bin holds at most
+// 64 keys they are listed and ranked directly (each lane compares its key
+// with all of them, ties counted).  Ordered emission: one block scan of the
+// threads' (above, tie) counts.  With four waves a thread holds at most 16
+// keys, so the per-key loops stay short on each SIMD.
+constexpr int kSmallKeys = 4096;
+constexpr int kSmallThreads = 256;
+constexpr int kSmallBins = 256;
+constexpr int kSmallLevels = 4;          // 8-bit digits of a 32-bit key range
+static_assert(kSmallBins == 4 * kWave, "a lane reads four bins");
+static_assert(kSmallKeys < 65536, "emission packs counts in 16 bits");
 
 template <int KPL, bool VEC>
-__global__ __launch_bounds__(kWaveRows * kWave) void topk_wave_kernel(
+__global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kv_len, int S, int L_cap,
-    int rows, int k, int32_t* __restrict__ indices) {
-  static_assert(KPL % 4 == 0 && KPL * kWave <= kWaveKeys, "whole 16-byte loads per lane");
-  __shared__ __attribute__((aligned(16))) uint32_t hist_all[kWaveRows][kWaveBins];
-  __shared__ __attribute__((aligned(16))) uint32_t list_all[kWaveRows][kWave + 4];
-  const int wave = threadIdx.x / kWave, l = lane_id();
-  const int row = blockIdx.x * kWaveRows + wave;
-  if (row >= rows) return;
-  uint32_t* hist = hist_all[wave];
-  uint32_t* list = list_all[wave];
+    int k, int32_t* __restrict__ indices) {
+  constexpr int NT = kSmallThreads;
+  constexpr int NW = NT / kWave;
+  static_assert(KPL % 4 == 0 && KPL * NT <= kSmallKeys, "whole 16-byte loads per thread");
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kSmallLevels][kSmallBins];
+  __shared__ __attribute__((aligned(16))) uint32_t list[kWave + 4];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t wmm[2 * NW];
+  const int row = blockIdx.x, t = threadIdx.x, l = lane_id(), w = t / kWave;
   const float* src = scores + (size_t)row * L_cap;
   int32_t* out = indices + (size_t)row * k;
-  const int j0 = KPL * l;
+  const int j0 = KPL * t;
 
-  // ---- the lane's keys; the loads go out before kv_len is known (they stay
-  // inside the L_cap-long row)
+  // ---- the thread's keys; the loads go out before kv_len is known (they
+  // stay inside the L_cap-long row)
   uint32_t key[KPL];
   if (VEC && j0 + KPL <= L_cap) {              // rows 16-byte aligned (L_cap % 4 == 0)
 #pragma unroll
@@ -934,49 +926,55 @@ __global__ __launch_bounds__(kWaveRows * kWave) void topk_wave_kernel(
 #pragma unroll
     for (int u = 0; u < KPL; ++u) key[u] = j0 + u < L_cap ? __float_as_uint(src[j0 + u]) : 0u;
   }
-  // rows are at most max_kv_len <= KPL * 64 keys long
-  const int n = min(row_count(kv_len, row, S, L_cap), KPL * kWave);
-  if (n <= k) {
-    for (int i = l; i < k; i += kWave) out[i] = i < n ? i : -1;
+  reinterpret_cast<uint4*>(&hist[0][0])[t] = make_uint4(0u, 0u, 0u, 0u);   // all levels' bins
+  // rows are at most max_kv_len <= KPL * NT keys long
+  const int n = min(row_count(kv_len, row, S, L_cap), KPL * NT);
+  if (n <= k) {                                // block-uniform
+    write_all<NT>(out, n, k);
     return;
   }
-  const int nv = n - j0;                       // keys of this lane inside the row (may be <= 0)
+  const int nv = n - j0;                       // keys of this thread inside the row (may be <= 0)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int u = 0; u < KPL; ++u) {
     key[u] = score_key(__uint_as_float(key[u]));
     if (u < nv) { kmin = min(kmin, key[u]); kmax = max(kmax, key[u]); }
   }
-  kmax = wave_max_uniform(kmax);
-  kmin = ~wave_max_uniform(~kmin);
+  kmax = wave_inclusive_max_u32(kmax);
+  kmin = wave_inclusive_max_u32(~kmin);
+  if (l == kWave - 1) { wmm[w] = kmax; wmm[NW + w] = kmin; }
+  __syncthreads();                             // bins zeroed, wave extremes written
+  kmax = 0u; kmin = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { kmax = max(kmax, wmm[i]); kmin = max(kmin, wmm[NW + i]); }
+  kmin = ~kmin;
 
   // ---- exact selection: T = the k-th largest key, take = how many keys
   // equal to T are kept
   const uint32_t range = kmax - kmin;
   int hi = range ? 32 - __clz(range) : 0;      // bits [sh, hi) of key - kmin are this level's
   uint32_t need = (uint32_t)k, prefix = 0u;    // digits fixed so far (bits >= hi)
-  uint32_t T, take;
-  while (true) {
+  uint32_t T = 0u, take = 0u;
+  for (int lvl = 0; lvl < kSmallLevels; ++lvl) {
     const int sh = hi > 8 ? hi - 8 : 0;
-    reinterpret_cast<uint4*>(hist)[l] = make_uint4(0u, 0u, 0u, 0u);
-    wave_lds_sync();
+    uint32_t* h = hist[lvl];
 #pragma unroll
     for (int u = 0; u < KPL; ++u) {
       const uint32_t d = key[u] - kmin;
-      if (u < nv && (hi >= 32 || (d >> hi) == (prefix >> hi))) atomicAdd(&hist[(d >> sh) & 0xFFu], 1u);
+      if (u < nv && (hi >= 32 || (d >> hi) == (prefix >> hi))) atomicAdd(&h[(d >> sh) & 0xFFu], 1u);
     }
-    wave_lds_sync();
-    // lane l holds bins 255 - 4 l - i, i = 0..3 (highest first)
-    const uint4 q = reinterpret_cast<const uint4*>(hist)[kWave - 1 - l];
-    const uint32_t h[4] = {q.w, q.z, q.y, q.x};
-    const uint32_t local = h[0] + h[1] + h[2] + h[3];
+    __syncthreads();
+    // every wave: lane l holds bins 255 - 4 l - i, i = 0..3 (highest first)
+    const uint4 q = reinterpret_cast<const uint4*>(h)[kWave - 1 - l];
+    const uint32_t b4[4] = {q.w, q.z, q.y, q.x};
+    const uint32_t local = b4[0] + b4[1] + b4[2] + b4[3];
     uint32_t before = wave_inclusive_scan(local) - local;
     int bin = -1;
     uint32_t above = 0u, cnt = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (before < need && need <= before + h[i]) { bin = kWaveBins - 1 - (4 * l + i); above = before; cnt = h[i]; }
-      before += h[i];
+      if (before < need && need <= before + b4[i]) { bin = kSmallBins - 1 - (4 * l + i); above = before; cnt = b4[i]; }
+      before += b4[i];
     }
     const int fl = (int)__builtin_ctzll(__ballot(bin >= 0)) & (kWave - 1);   // the one finder
     bin = __builtin_amdgcn_readlane(bin, fl);
@@ -986,18 +984,24 @@ __global__ __launch_bounds__(kWaveRows * kWave) void topk_wave_kernel(
     prefix |= (uint32_t)bin << sh;
     if (sh == 0) { T = kmin + prefix; take = need; break; }
     if (cnt <= (uint32_t)kWave) {
-      // the bin's keys into the list (zero-padded to whole 16-byte reads:
-      // every key is above 0, the key of no FP32 value but a negative NaN)
-      uint32_t c = 0u;
+      // the bin's keys into the list at block-scanned offsets (zero-padded
+      // to whole 16-byte reads: every key is above 0, the key of no FP32
+      // value but a negative NaN); every wave then ranks them
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int u = 0; u < KPL; ++u)
+        mine += (u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh)) ? 1u : 0u;
+      uint32_t total;
+      uint32_t slot = block_exclusive_scan<NT>(mine, scratch, &total);
 #pragma unroll
       for (int u = 0; u < KPL; ++u) {
-        const bool in = u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh);
-        const uint64_t m = __ballot(in);
-        if (in) list[c + wave_prefix_count(m)] = key[u];
-        c += (uint32_t)__popcll(m);
+        if (u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh)) {
+          list[slot] = key[u];
+          ++slot;
+        }
       }
-      if (l < 4) list[cnt + l] = 0u;
-      wave_lds_sync();
+      if (t < 4) list[cnt + t] = 0u;
+      __syncthreads();
       const uint32_t x = l < (int)cnt ? list[l] : 0u;
       uint32_t gt = 0u, ge = 0u;
       for (uint32_t j = 0; j < cnt; j += 4) {
@@ -1012,18 +1016,17 @@ __global__ __launch_bounds__(kWaveRows * kWave) void topk_wave_kernel(
       break;
     }
     hi = sh;
-    wave_lds_sync();                           // bins read before the next level zeroes them
   }
 
-  // ---- ordered emission: the lanes hold the row in index order
+  // ---- ordered emission: the threads hold the row in index order
   uint32_t gtc = 0u, eqc = 0u;
 #pragma unroll
   for (int u = 0; u < KPL; ++u) {
     gtc += (u < nv && key[u] > T) ? 1u : 0u;
     eqc += (u < nv && key[u] == T) ? 1u : 0u;
   }
-  const uint32_t packed = gtc | (eqc << 16);
-  const uint32_t ex = wave_inclusive_scan(packed) - packed;
+  uint32_t total;
+  const uint32_t ex = block_exclusive_scan<NT>(gtc | (eqc << 16), scratch + 16, &total);
   uint32_t g = ex & 0xFFFFu, e = ex >> 16;
 #pragma unroll
   for (int u = 0; u < KPL; ++u) {
@@ -1486,10 +1489,10 @@ TopkPlan plan_topk(int B, int S, int L_cap, int max_kv_len, int k) {
   TopkPlan p{};
   p.rows = B * S;
   const long long rows = p.rows;
-  if (max_kv_len <= kWaveKeys) {
-    p.kind = kPlanWave;
-    int kpl = 8;
-    while (kpl * kWave < max_kv_len) kpl *= 2;
+  if (max_kv_len <= kSmallKeys) {
+    p.kind = kPlanSmall;
+    int kpl = 4;
+    while (kpl * kSmallThreads < max_kv_len) kpl *= 2;
     p.lane_keys = kpl;
     return p;
   }
@@ -1574,14 +1577,14 @@ void launch_chunk_ns(int U, bool vec, dim3 grid, hipStream_t st, const float* sc
   }
 }
 template <int KPL>
-void launch_wave(bool vec, dim3 grid, hipStream_t st, const float* scores, const int32_t* kv_len,
-                 int S, int L_cap, int rows, int k, int32_t* indices) {
+void launch_small(bool vec, int rows, hipStream_t st, const float* scores, const int32_t* kv_len,
+                  int S, int L_cap, int k, int32_t* indices) {
   if (vec)
-    hipLaunchKernelGGL((topk_wave_kernel<KPL, true>), grid, dim3(kWaveRows * kWave), 0, st, scores,
-                       kv_len, S, L_cap, rows, k, indices);
+    hipLaunchKernelGGL((topk_small_kernel<KPL, true>), dim3(rows), dim3(kSmallThreads), 0, st,
+                       scores, kv_len, S, L_cap, k, indices);
   else
-    hipLaunchKernelGGL((topk_wave_kernel<KPL, false>), grid, dim3(kWaveRows * kWave), 0, st, scores,
-                       kv_len, S, L_cap, rows, k, indices);
+    hipLaunchKernelGGL((topk_small_kernel<KPL, false>), dim3(rows), dim3(kSmallThreads), 0, st,
+                       scores, kv_len, S, L_cap, k, indices);
 }
 }  // namespace
 
@@ -1600,16 +1603,13 @@ void launch_topk(const TopkPlan& p, const float* scores, const int32_t* kv_len, 
   }
   const int vec4 = (L_cap & 3) == 0 ? 1 : 0;
   switch (p.kind) {
-    case kPlanWave: {
-      const dim3 grid((p.rows + kWaveRows - 1) / kWaveRows);
+    case kPlanSmall:
       switch (p.lane_keys) {
-        case 8: launch_wave<8>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
-        case 16: launch_wave<16>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
-        case 32: launch_wave<32>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
-        default: launch_wave<64>(vec4, grid, st, scores, kv_len, S, L_cap, p.rows, k, indices); break;
+        case 4: launch_small<4>(vec4, p.rows, st, scores, kv_len, S, L_cap, k, indices); break;
+        case 8: launch_small<8>(vec4, p.rows, st, scores, kv_len, S, L_cap, k, indices); break;
+        default: launch_small<16>(vec4, p.rows, st, scores, kv_len, S, L_cap, k, indices); break;
       }
       return;
-    }
     case kPlanStream:
       if (vec4)
         hipLaunchKernelGGL((topk_stream_kernel<kStreamThreads, kRowCap, true>), dim3(p.rows),

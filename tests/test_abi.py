@@ -288,11 +288,11 @@ def test_describe_plan_names_the_launches(dsa):
     f = F(d(dsa.DSA_PLAN_ATTENTION_PREFILL, attention=a))
     assert f["schedule"] == "split" and f["grid"] == "1x2x8" and "merge_grid" not in f
     assert f["workspace"] == "0"
-    # rows of at most 4096 keys (by the runtime bound): one wave per row
+    # rows of at most 4096 keys (by the runtime bound): one small workgroup per row
     f = F(d(dsa.DSA_PLAN_TOPK, 1, 1, 1024, k=128))
-    assert f["plan"] == "wave" and f["grid"] == "1" and f["keys_per_lane"] == "16"
+    assert f["plan"] == "small" and f["grid"] == "1" and f["keys_per_thread"] == "4"
     f = F(d(dsa.DSA_PLAN_TOPK, 3, 50, 262144, max_kv_len=4096, k=300))
-    assert f["plan"] == "wave" and f["grid"] == "38" and f["keys_per_lane"] == "64"
+    assert f["plan"] == "small" and f["grid"] == "150" and f["keys_per_thread"] == "16"
     assert dsa.dsa_topk_workspace_bytes(1, 8, 4096, 2048) == 0
     assert F(d(dsa.DSA_PLAN_TOPK, 1, 8, 4097, k=2048))["plan"] == "resident"
     # the runtime bound, not the capacity, picks the plan

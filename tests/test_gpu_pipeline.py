@@ -40,7 +40,7 @@ SAMPLE_ROWS = {
 # form), as dsa_describe_plan reports them -- the same descriptions the bench
 # logs next to its timings.
 EXPECTED_PLANS = {
-    "tiny_decode_1k": ("indexer_score_kernel", "wave", "attention_decode/split"),
+    "tiny_decode_1k": ("indexer_score_kernel", "small", "attention_decode/split"),
     "spec_decode_32k": ("indexer_score_kernel", "resident", "attention_decode/split"),
     "prefill_128k": ("indexer_fold_kernel", "stream", "attention_prefill/wave_rows"),
     "int8_batched_decode_64k": (None, None, "attention_decode/split"),

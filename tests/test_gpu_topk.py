@@ -266,18 +266,19 @@ def test_topk_very_long_rows(dsa):
 
 
 @pytest.mark.parametrize("B,S,L,k,kv,bound", [
-    (1, 1, 1024, 128, [1024], 1024),                  # one decode row, 16 keys per lane
-    (1, 8, 4096, 2048, [4096], 4096),                 # 64 keys per lane, k = half the row
-    (1, 2, 500, 7, [500], 500),                       # 8 keys per lane, lanes past the row
-    (3, 50, 4000, 300, [4000, 2500, 60], 4000),       # 150 rows, ragged, partial last workgroup
+    (1, 1, 1024, 128, [1024], 1024),                  # one decode row, 4 keys per thread
+    (1, 8, 4096, 2048, [4096], 4096),                 # 16 keys per thread, k = half the row
+    (1, 2, 500, 7, [500], 500),                       # 4 keys per thread, threads past the row
+    (3, 50, 4000, 300, [4000, 2500, 60], 4000),       # 150 rows, ragged
     (2, 7, 3001, 1, [3001, 17], 3001),                # L % 4 = 1 (element loads), k = 1
     (1, 9, 2050, 2045, [2050], 2050),                 # k close to n, k >= n on the first rows
     (2, 4, 262144, 512, [3000, 4096], 4096)])         # a long cache under a short runtime bound
-def test_topk_wave_plan_short_rows(dsa, B, S, L, k, kv, bound):
-    # Rows of at most 4096 keys by the runtime bound: one wave per row holds
-    # the row in registers and selects on its radix digits directly.
+def test_topk_small_plan_short_rows(dsa, B, S, L, k, kv, bound):
+    # Rows of at most 4096 keys by the runtime bound: one 256-thread
+    # workgroup per row holds the row in registers and selects on its radix
+    # digits directly.
     plan = dsa.plan_fields(dsa.dsa_describe_plan(dsa.DSA_PLAN_TOPK, B, S, L, bound, k=k))
-    assert plan["plan"] == "wave" and plan["workspace"] == "0"
+    assert plan["plan"] == "small" and plan["workspace"] == "0"
     r = rng(50 + L + k)
     for what, sc in (("normal", torch.from_numpy(r.standard_normal((B, S, L)).astype(np.float32))),
                      ("ints[-3,3]", integer_scores(r, (B, S, L), -3, 3)),
@@ -289,10 +290,10 @@ def test_topk_wave_plan_short_rows(dsa, B, S, L, k, kv, bound):
             for s in range(S):
                 want = oracle.topk_row(sc[b, s], kv[b] - S + s, k)
                 assert np.array_equal(got[b, s], want), \
-                    f"wave {what} row ({b},{s}): {first_mismatch(got[b, s], want)}"
+                    f"small {what} row ({b},{s}): {first_mismatch(got[b, s], want)}"
 
 
-def test_topk_wave_plan_exact_digits_and_deep_levels(dsa):
+def test_topk_small_plan_exact_digits_and_deep_levels(dsa):
     # Short rows whose k-th key sits in a cluster of tied or nearly equal keys
     # under a wide key range (keys of +-1e30 at two positions), so that the
     # chosen bin holds more than 64 keys at every level down to the last
@@ -310,7 +311,7 @@ def test_topk_wave_plan_exact_digits_and_deep_levels(dsa):
     sc[0, 5] = r.standard_normal(L)
     sc = torch.from_numpy(sc)
     for k in (1, 2, 100, 1365, 1366, 1367, 4000, 4090):
-        _check(dsa, sc, [L], k, what=f"wave deep k={k}")
+        _check(dsa, sc, [L], k, what=f"small deep k={k}")
 
 
 @pytest.mark.parametrize("B,S,L,k,kv", [
