@@ -64,11 +64,10 @@ constexpr int kSampleBlock = 256;      // consecutive keys per sample block
 constexpr int kSegWords = 2048;        // bitmap segment: 65536 indices
 constexpr int kSegBits = kSegWords * 32;
 constexpr int kResKeys = 32768;        // longest row the resident plan holds
-constexpr int kResCap = 4096;          // candidate list; the select's histogram follows it
+constexpr int kResCap = 4096;          // candidate list of a resident row
 constexpr int kResSample = 2048;       // sample of a resident row (already in LDS)
 constexpr int kRowCap = 4096;
 static_assert(kResCap < 65536, "ordered emission packs counts in 16 bits");
-static_assert(kResCap + (1 << 12) <= kResKeys, "resident select histogram fits the row area");
 constexpr int kStreamLoads = 4;        // 16-byte loads per lane in flight (streaming plan)
 static_assert(4 * kStreamLoads <= 32, "one hit bit per key of a lane's step");
 
@@ -476,9 +475,9 @@ __device__ void select_exact_row(KeyAt key_at, int n, int k, uint32_t* sel, uint
   }
 }
 
-// Variants of radix_select (two levels) and radix_select_rel for callers
-// that zeroed one histogram per level beforehand and give each level its
-// own result words: three barriers per level instead of five.
+// A variant of radix_select (two levels) for callers that zeroed one
+// histogram per level beforehand and give each level its own result words:
+// three barriers per level instead of five.
 //
 // Lower bound of the need-th largest key: the 22-bit bin edge (low 10 bits
 // zero) after levels on bits [31:21] and [20:10].  h0, h1: kBins zeroed
@@ -501,54 +500,155 @@ __device__ void radix_lower_bound_pre(Get get, int count, uint32_t need, uint32_
   T_lo = (b0 << 21) | (misc[2] << 10);
 }
 
-// radix_select_rel over up to three zeroed histograms (hists + lvl *
-// kRelBins); misc[2 lvl], misc[2 lvl + 1] receive level lvl's results.
-template <int NT, typename KeyOf>
-__device__ void radix_select_rel_pre(KeyOf key_of, int count, uint32_t need, uint32_t base,
-                                     uint32_t range, uint32_t* hists, uint32_t* scratch,
-                                     uint32_t* misc, uint32_t& T, uint32_t& take) {
-  const int top = range ? 32 - __clz(range) : 0;
-  int hi = top > kRelBits ? top : kRelBits;
-  uint32_t prefix = 0;
-  for (int lvl = 0;; ++lvl) {                             // at most 3 levels (hi <= 32)
-    const int lo = hi > kRelBits ? hi - kRelBits : 0;
-    uint32_t* hist = hists + lvl * kRelBins;
-    for (int i = threadIdx.x; i < count; i += NT) {
-      const uint32_t d = key_of(i) - base;
-      if (hi >= 32 || (d >> hi) == (prefix >> hi))
-        atomicAdd(&hist[(d >> lo) & (kRelBins - 1)], 1u);
-    }
-    __syncthreads();
-    select_bin_rel<NT>(hist, need, scratch, misc + 2 * lvl);
-    need -= misc[2 * lvl + 1];
-    prefix |= misc[2 * lvl] << lo;
-    if (lo == 0) break;
-    const uint32_t nb = hist[misc[2 * lvl]];    // keys in the chosen bin (block-uniform)
-    if (nb <= (uint32_t)kWave) {
-      // few keys left: rank them in one wave (the next level's histogram,
-      // zeroed and unused, holds the list and its counter)
-      uint32_t* list = hists + (lvl + 1) * kRelBins;
-      for (int i = threadIdx.x; i < count; i += NT) {
-        const uint32_t k = key_of(i);
-        if (((k - base) >> lo) == (prefix >> lo)) list[atomicAdd(&list[kWave], 1u)] = k;
-      }
-      rank_small_bin<NT>(list, nb, need, misc + 2 * lvl + 2);
-      T = misc[2 * lvl + 2];
-      take = misc[2 * lvl + 3];
-      return;
-    }
-    hi = lo;
-  }
-  T = base + prefix;
-  take = need;
-}
-
 // ====================================================================== resident plan
-// Dynamic LDS: row scores [kResKeys] (later the candidates' keys and the
-// select's histogram) | hist | scratch | misc | list indices [kResCap].
+// Dynamic LDS: row scores [kResKeys] (later the select's rank list) | hist
+// (the sample threshold's, later the select's level histograms) | scratch |
+// misc | list indices [kResCap].
 // The row stays in LDS as FP32: hits are tested on floats and only the
 // sample and the candidates become keys, which keeps the per-key work of
 // the one-workgroup row small.
+constexpr int kSmallBins = 256;
+constexpr int kSmallLevels = 4;          // 8-bit digits of a 32-bit key range
+static_assert(kSmallBins == 4 * kWave, "a lane reads four bins");
+
+// One radix level over keys held in registers (thread t: KPL keys, valid
+// where u < nv, all >= base): the keys whose bits >= hi of key - base match
+// prefix count into h (256 zeroed words of LDS) by their digit bits
+// [sh, hi); after a barrier every wave scans the bins itself (lane l reads
+// four) and finds the bin holding the need-th largest of them, the keys in
+// higher bins (above) and in that bin (cnt); all waves agree.  Block-wide.
+template <int KPL>
+__device__ __forceinline__ void held_keys_level(const uint32_t (&key)[KPL], int nv, uint32_t base,
+                                                int hi, int sh, uint32_t prefix, uint32_t need,
+                                                uint32_t* h, uint32_t& bin, uint32_t& above,
+                                                uint32_t& cnt) {
+  const int l = lane_id();
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const uint32_t d = key[u] - base;
+    if (u < nv && (hi >= 32 || (d >> hi) == (prefix >> hi))) atomicAdd(&h[(d >> sh) & 0xFFu], 1u);
+  }
+  __syncthreads();
+  // lane l holds bins 255 - 4 l - i, i = 0..3 (highest first)
+  const uint4 q = reinterpret_cast<const uint4*>(h)[kWave - 1 - l];
+  const uint32_t b4[4] = {q.w, q.z, q.y, q.x};
+  const uint32_t local = b4[0] + b4[1] + b4[2] + b4[3];
+  uint32_t before = wave_inclusive_scan(local) - local;
+  int b = -1;
+  uint32_t a = 0u, c = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (before < need && need <= before + b4[i]) { b = kSmallBins - 1 - (4 * l + i); a = before; c = b4[i]; }
+    before += b4[i];
+  }
+  const int fl = (int)__builtin_ctzll(__ballot(b >= 0)) & (kWave - 1);   // the one finder
+  bin = (uint32_t)__builtin_amdgcn_readlane(b, fl);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)a, fl);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, fl);
+}
+
+// Lower bound of the need-th largest of keys held in registers (as for
+// held_keys_level): two levels of 8-bit digits of key - base, the first on
+// the top 8 bits of range; the lower edge of the chosen bin (exact when the
+// range has at most 16 bits).  hist: two levels' zeroed bins.  Block-wide.
+template <int KPL>
+__device__ uint32_t lower_bound_held_keys(const uint32_t (&key)[KPL], int nv, uint32_t base,
+                                          uint32_t range, uint32_t need,
+                                          uint32_t (*hist)[kSmallBins]) {
+  int hi = range ? 32 - __clz(range) : 0;
+  uint32_t prefix = 0u;
+  for (int lvl = 0; lvl < 2; ++lvl) {
+    const int sh = hi > 8 ? hi - 8 : 0;
+    uint32_t bin, above, cnt;
+    held_keys_level<KPL>(key, nv, base, hi, sh, prefix, need, hist[lvl], bin, above, cnt);
+    need -= above;
+    prefix |= bin << sh;
+    if (sh == 0) break;
+    hi = sh;
+  }
+  return base + prefix;
+}
+
+// Exact selection over keys held in registers: thread t holds KPL keys
+// (valid where u < nv), all in [base, base + range].  Radix digits of
+// key - base, 8 bits per level, the first level on the top 8 bits of range;
+// level lvl counts into hist[lvl] (kSmallLevels x 256 words of LDS, zeroed by
+// the caller before a barrier).  After each level's barrier every wave scans
+// the 256 bins itself and reaches the same bin, so a level needs no second
+// barrier.  Once the chosen bin holds at most 64 keys they go to `list` (68
+// words of LDS, 16-byte aligned) at block-scanned offsets and are ranked
+// (each key compared with all of them, ties counted), the comparisons spread
+// over the whole block; res (2 words of LDS) passes the result on.
+// T = the need-th largest key, take = how many keys equal to T are kept.
+// Block-wide; 1 <= need <= the number of valid keys.  scratch: NT/64 words.
+template <int NT, int KPL>
+__device__ void select_held_keys(const uint32_t (&key)[KPL], int nv, uint32_t base,
+                                 uint32_t range, uint32_t need,
+                                 uint32_t (*hist)[kSmallBins], uint32_t* list, uint32_t* scratch,
+                                 uint32_t* res, uint32_t& T, uint32_t& take) {
+  constexpr int TPK = NT / kWave;              // threads per ranked list entry
+  constexpr int EPT = kWave / TPK;             // list entries each of them compares
+  static_assert(TPK * EPT == kWave && EPT % 4 == 0 && TPK <= kWave, "whole 16-byte list reads");
+  const int t = threadIdx.x;
+  int hi = range ? 32 - __clz(range) : 0;      // bits [sh, hi) of key - base are this level's
+  uint32_t prefix = 0u;                        // digits fixed so far (bits >= hi)
+  T = 0u;
+  take = 0u;
+  for (int lvl = 0; lvl < kSmallLevels; ++lvl) {
+    const int sh = hi > 8 ? hi - 8 : 0;
+    uint32_t bin, above, cnt;
+    held_keys_level<KPL>(key, nv, base, hi, sh, prefix, need, hist[lvl], bin, above, cnt);
+    need -= above;
+    prefix |= bin << sh;
+    if (sh == 0) { T = base + prefix; take = need; return; }
+    if (cnt <= (uint32_t)kWave) {
+      // the bin's keys into the list (zero-padded to whole 16-byte reads:
+      // every key is above 0, the key of no FP32 value but a negative NaN)
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int u = 0; u < KPL; ++u)
+        mine += (u < nv && ((key[u] - base) >> sh) == (prefix >> sh)) ? 1u : 0u;
+      uint32_t total;
+      uint32_t slot = block_exclusive_scan<NT>(mine, scratch, &total);
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        if (u < nv && ((key[u] - base) >> sh) == (prefix >> sh)) {
+          list[slot] = key[u];
+          ++slot;
+        }
+      }
+      if (t < 4) list[cnt + t] = 0u;
+      __syncthreads();
+      // ranks spread over the block: TPK consecutive threads share list
+      // entry i = t / TPK, each comparing it with EPT entries, and sum their
+      // counts with lane exchanges
+      const int i = t / TPK, j0 = (t % TPK) * EPT;
+      const uint32_t x = list[i];
+      uint32_t gt = 0u, ge = 0u;
+#pragma unroll
+      for (int j = 0; j < EPT; j += 4) {
+        const uint4 y = *reinterpret_cast<const uint4*>(list + j0 + j);
+        const bool in0 = j0 + j < (int)cnt, in1 = j0 + j + 1 < (int)cnt;
+        const bool in2 = j0 + j + 2 < (int)cnt, in3 = j0 + j + 3 < (int)cnt;
+        gt += (in0 && y.x > x) + (in1 && y.y > x) + (in2 && y.z > x) + (in3 && y.w > x);
+        ge += (in0 && y.x >= x) + (in1 && y.y >= x) + (in2 && y.z >= x) + (in3 && y.w >= x);
+      }
+#pragma unroll
+      for (int off = TPK / 2; off > 0; off >>= 1) {
+        gt += (uint32_t)__shfl_xor((int)gt, off, kWave);
+        ge += (uint32_t)__shfl_xor((int)ge, off, kWave);
+      }
+      // the threads holding T agree; they write the same values
+      if (t % TPK == 0 && i < (int)cnt && gt < need && need <= ge) { res[0] = x; res[1] = need - gt; }
+      __syncthreads();
+      T = res[0];
+      take = res[1];
+      return;
+    }
+    hi = sh;
+  }
+}
+
 constexpr int kResThreads = 1024;
 constexpr size_t kResLds = (size_t)(kResKeys + kBins + 32 + kMiscWords + kResCap) * 4;
 
@@ -611,10 +711,9 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     }
   }
   const int n = min(row_count(kv_len, row, S, L_cap), span);
-  // The sample threshold's two histograms: hist, and the list area, which
-  // is free until the candidates are listed.
-  uint32_t* h1 = lidx;
-  for (int i = t; i < kBins; i += NT) { s.hist[i] = 0; h1[i] = 0; }
+  // The sample threshold's two level histograms: the first 512 words of hist.
+  if (t < 2 * kSmallBins / 4) reinterpret_cast<uint4*>(s.hist)[t] = make_uint4(0u, 0u, 0u, 0u);
+  if (t == 0) { s.misc[12] = 0u; s.misc[13] = 0u; }   // the sample's largest key, ~(its smallest)
   // Every lane reads keys that other waves copied: each wave waits for its
   // own copies (the compiler would only wait before this wave's LDS reads),
   // then the barrier.
@@ -622,15 +721,28 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
   __syncthreads();
 
   if (k <= kResCap) {
-    // ---- threshold from the sample (the row itself when short)
-    uint32_t T_lo;
-    if (n <= kResSample)
-      radix_lower_bound_pre<NT>([&](int i) { return score_key(rowf[i]); }, n, (uint32_t)k,
-                                s.hist, h1, s.scratch, s.misc, T_lo);
-    else
-      radix_lower_bound_pre<NT>(
-          [&](int i) { return score_key(rowf[sample_pos<kResSample>(i, n)]); }, kResSample,
-          (uint32_t)sample_rank(k, n, kResSample), s.hist, h1, s.scratch, s.misc, T_lo);
+    // ---- threshold from the sample (the row itself when short): two levels
+    // of 8-bit digits of key - (the sample's smallest key); T_lo is the
+    // lower edge of the bin holding the sample's r-th largest key
+    constexpr int SPT = kResSample / NT;        // sample keys per thread
+    const int ns = min(n, kResSample);
+    const int nvs = ns - SPT * t;
+    uint32_t sk[SPT];
+    uint32_t smax = 0u, sminc = 0u;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = SPT * t + u;
+      sk[u] = u < nvs ? score_key(rowf[n <= kResSample ? i : sample_pos<kResSample>(i, n)]) : 0u;
+      if (u < nvs) { smax = max(smax, sk[u]); sminc = max(sminc, ~sk[u]); }
+    }
+    smax = wave_inclusive_max_u32(smax);
+    sminc = wave_inclusive_max_u32(sminc);
+    if (lane_id() == kWave - 1) { atomicMax(&s.misc[12], smax); atomicMax(&s.misc[13], sminc); }
+    __syncthreads();
+    const uint32_t smin = ~s.misc[13];
+    const uint32_t need_s = (uint32_t)(n <= kResSample ? k : sample_rank(k, n, kResSample));
+    const uint32_t T_lo = lower_bound_held_keys<SPT>(
+        sk, nvs, smin, s.misc[12] - smin, need_s, reinterpret_cast<uint32_t (*)[kSmallBins]>(s.hist));
     // ---- candidates, in index order.  Lane t owns keys [32 t, 32 t + 32)
     // and tests them on floats: x >= f_lo <=> score_key(x) >= T_lo
     // (score_key is order-preserving and gives -0.0 the key of +0.0;
@@ -668,38 +780,49 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     }
     __syncthreads();
     if (m >= k && m <= kResCap) {
-      // The row is no longer needed beyond the candidates: their keys go to
-      // a compact array at the front of the row area, the select's
-      // histogram right after it.  The largest key - T_lo sizes the
-      // select's digits.
+      // Thread t takes list entries [MU t, MU t + MU) (index order across
+      // threads) and their keys into registers.  The largest key - T_lo
+      // sizes the select's digits; the select's level histograms take the
+      // sample threshold's histogram area, its rank list the row area's
+      // front (free once every key is in registers).
       constexpr int MU = kResCap / NT;
+      static_assert(MU == 4, "one 16-byte read of list entries per thread");
+      const uint4 ix = reinterpret_cast<const uint4*>(lidx)[t];
+      const uint32_t idx[MU] = {ix.x, ix.y, ix.z, ix.w};
+      const int nvl = m - MU * t;               // entries of this thread inside the list
       uint32_t kk[MU];
       uint32_t span = 0;
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
-        const int i = u * NT + t;
-        kk[u] = i < m ? score_key(rowf[lidx[i]]) : 0u;
-        if (i < m) span = max(span, kk[u] - T_lo);
+        kk[u] = u < nvl ? score_key(rowf[idx[u]]) : 0u;
+        if (u < nvl) span = max(span, kk[u] - T_lo);
       }
       span = wave_inclusive_max_u32(span);
       if (lane_id() == kWave - 1) atomicMax(&s.misc[11], span);
-      __syncthreads();
-      // keys to the front of the row area, the select's three level
-      // histograms zeroed right after them
-      uint32_t* hists = rowk + kResCap;
+      uint32_t (*lh)[kSmallBins] = reinterpret_cast<uint32_t (*)[kSmallBins]>(s.hist);
+      static_assert(kSmallLevels * kSmallBins <= kBins, "level histograms fit the sample's");
+      if (t < kSmallLevels * kSmallBins / 4) reinterpret_cast<uint4*>(s.hist)[t] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();                          // keys read, bins zeroed, span complete
+      uint32_t T, take;
+      select_held_keys<NT, MU>(kk, nvl, T_lo, s.misc[11], (uint32_t)k, lh, rowk, s.scratch, s.misc + 12,
+                               T, take);
+      // ---- ordered emission from the registers
+      uint32_t gtc = 0u, eqc = 0u;
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
-        const int i = u * NT + t;
-        if (i < m) rowk[i] = kk[u];
+        gtc += (u < nvl && kk[u] > T) ? 1u : 0u;
+        eqc += (u < nvl && kk[u] == T) ? 1u : 0u;
       }
-      static_assert(kResCap + 3 * kRelBins <= kResKeys, "select histograms fit the row area");
-      uint4* h4 = reinterpret_cast<uint4*>(hists);
-      for (int i = t; i < 3 * kRelBins / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-      __syncthreads();
-      uint32_t T, take;
-      radix_select_rel_pre<NT>([&](int i) { return rowk[i]; }, m, (uint32_t)k, T_lo, s.misc[11],
-                               hists, s.scratch, s.misc + 4, T, take);
-      emit_ordered<NT>(rowk, lidx, m, T, take, out, s.scratch);
+      uint32_t total;
+      const uint32_t ex = block_exclusive_scan<NT>(gtc | (eqc << 16), s.scratch + 16, &total);
+      uint32_t g = ex & 0xFFFFu, e = ex >> 16;
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const bool above = u < nvl && kk[u] > T, tie = u < nvl && kk[u] == T;
+        if (above || (tie && e < take)) out[g + min(e, take)] = (int32_t)idx[u];
+        g += above ? 1u : 0u;
+        e += tie ? 1u : 0u;
+      }
       return;
     }
   }
@@ -891,9 +1014,6 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // keys, so the per-key loops stay short on each SIMD.
 constexpr int kSmallKeys = 4096;
 constexpr int kSmallThreads = 256;
-constexpr int kSmallBins = 256;
-constexpr int kSmallLevels = 4;          // 8-bit digits of a 32-bit key range
-static_assert(kSmallBins == 4 * kWave, "a lane reads four bins");
 static_assert(kSmallKeys < 65536, "emission packs counts in 16 bits");
 
 template <int KPL, bool VEC>
@@ -907,6 +1027,7 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t list[kWave + 4];
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t wmm[2 * NW];
+  __shared__ uint32_t res[2];
   const int row = blockIdx.x, t = threadIdx.x, l = lane_id(), w = t / kWave;
   const float* src = scores + (size_t)row * L_cap;
   int32_t* out = indices + (size_t)row * k;
@@ -951,72 +1072,8 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
 
   // ---- exact selection: T = the k-th largest key, take = how many keys
   // equal to T are kept
-  const uint32_t range = kmax - kmin;
-  int hi = range ? 32 - __clz(range) : 0;      // bits [sh, hi) of key - kmin are this level's
-  uint32_t need = (uint32_t)k, prefix = 0u;    // digits fixed so far (bits >= hi)
-  uint32_t T = 0u, take = 0u;
-  for (int lvl = 0; lvl < kSmallLevels; ++lvl) {
-    const int sh = hi > 8 ? hi - 8 : 0;
-    uint32_t* h = hist[lvl];
-#pragma unroll
-    for (int u = 0; u < KPL; ++u) {
-      const uint32_t d = key[u] - kmin;
-      if (u < nv && (hi >= 32 || (d >> hi) == (prefix >> hi))) atomicAdd(&h[(d >> sh) & 0xFFu], 1u);
-    }
-    __syncthreads();
-    // every wave: lane l holds bins 255 - 4 l - i, i = 0..3 (highest first)
-    const uint4 q = reinterpret_cast<const uint4*>(h)[kWave - 1 - l];
-    const uint32_t b4[4] = {q.w, q.z, q.y, q.x};
-    const uint32_t local = b4[0] + b4[1] + b4[2] + b4[3];
-    uint32_t before = wave_inclusive_scan(local) - local;
-    int bin = -1;
-    uint32_t above = 0u, cnt = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (before < need && need <= before + b4[i]) { bin = kSmallBins - 1 - (4 * l + i); above = before; cnt = b4[i]; }
-      before += b4[i];
-    }
-    const int fl = (int)__builtin_ctzll(__ballot(bin >= 0)) & (kWave - 1);   // the one finder
-    bin = __builtin_amdgcn_readlane(bin, fl);
-    above = (uint32_t)__builtin_amdgcn_readlane((int)above, fl);
-    cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, fl);
-    need -= above;
-    prefix |= (uint32_t)bin << sh;
-    if (sh == 0) { T = kmin + prefix; take = need; break; }
-    if (cnt <= (uint32_t)kWave) {
-      // the bin's keys into the list at block-scanned offsets (zero-padded
-      // to whole 16-byte reads: every key is above 0, the key of no FP32
-      // value but a negative NaN); every wave then ranks them
-      uint32_t mine = 0u;
-#pragma unroll
-      for (int u = 0; u < KPL; ++u)
-        mine += (u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh)) ? 1u : 0u;
-      uint32_t total;
-      uint32_t slot = block_exclusive_scan<NT>(mine, scratch, &total);
-#pragma unroll
-      for (int u = 0; u < KPL; ++u) {
-        if (u < nv && ((key[u] - kmin) >> sh) == (prefix >> sh)) {
-          list[slot] = key[u];
-          ++slot;
-        }
-      }
-      if (t < 4) list[cnt + t] = 0u;
-      __syncthreads();
-      const uint32_t x = l < (int)cnt ? list[l] : 0u;
-      uint32_t gt = 0u, ge = 0u;
-      for (uint32_t j = 0; j < cnt; j += 4) {
-        const uint4 y = *reinterpret_cast<const uint4*>(list + j);
-        gt += (y.x > x) + (y.y > x) + (y.z > x) + (y.w > x);
-        ge += (y.x >= x) + (y.y >= x) + (y.z >= x) + (y.w >= x);
-      }
-      const bool hit = l < (int)cnt && gt < need && need <= ge;   // the lanes holding T agree
-      const int hl = (int)__builtin_ctzll(__ballot(hit)) & (kWave - 1);
-      T = (uint32_t)__builtin_amdgcn_readlane((int)x, hl);
-      take = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, hl);
-      break;
-    }
-    hi = sh;
-  }
+  uint32_t T, take;
+  select_held_keys<NT, KPL>(key, nv, kmin, kmax - kmin, (uint32_t)k, hist, list, scratch, res, T, take);
 
   // ---- ordered emission: the threads hold the row in index order
   uint32_t gtc = 0u, eqc = 0u;
@@ -1072,6 +1129,7 @@ constexpr int kSelThreads = 512;
 constexpr int kListCap = 8192;          // candidates the general path holds in LDS
 static_assert(kListCap < 65536, "ordered emission packs counts in 16 bits");
 constexpr int kSpecMax = 16384;         // entries the fast path holds (kSelThreads x 32)
+static_assert(kSpecMax == kSelThreads * 32, "fast-path entries: 32 per select lane at most");
 constexpr int kMaxSplitChunks = 2048;   // chunks per row (L_cap <= 2^24 with CH = 8192)
 constexpr int kMinSample = 1024;        // smaller valid samples are drawn again over the row
 static_assert(kListCap >= 2 * kSegWords, "fallback segments fit the list area");
