@@ -511,6 +511,21 @@ constexpr int kSmallBins = 256;
 constexpr int kSmallLevels = 4;          // 8-bit digits of a 32-bit key range
 static_assert(kSmallBins == 4 * kWave, "a lane reads four bins");
 
+// Sum over aligned groups of G lanes (G = 4 or 16); every lane of a group
+// gets its group's sum.  DPP lane moves: two quad permutations, then (16)
+// two rotations of the 16-lane row by 4 and by 8.
+template <int G>
+__device__ __forceinline__ uint32_t group_sum(uint32_t v) {
+  static_assert(G == 4 || G == 16, "quads or DPP rows");
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if constexpr (G == 16) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  }
+  return v;
+}
+
 // One radix level over keys held in registers (thread t: KPL keys, valid
 // where u < nv, all >= base): the keys whose bits >= hi of key - base match
 // prefix count into h (256 zeroed words of LDS) by their digit bits
@@ -588,7 +603,7 @@ __device__ void select_held_keys(const uint32_t (&key)[KPL], int nv, uint32_t ba
                                  uint32_t* res, uint32_t& T, uint32_t& take) {
   constexpr int TPK = NT / kWave;              // threads per ranked list entry
   constexpr int EPT = kWave / TPK;             // list entries each of them compares
-  static_assert(TPK * EPT == kWave && EPT % 4 == 0 && TPK <= kWave, "whole 16-byte list reads");
+  static_assert(TPK * EPT == kWave && EPT % 4 == 0, "whole 16-byte list reads");
   const int t = threadIdx.x;
   int hi = range ? 32 - __clz(range) : 0;      // bits [sh, hi) of key - base are this level's
   uint32_t prefix = 0u;                        // digits fixed so far (bits >= hi)
@@ -633,11 +648,8 @@ __device__ void select_held_keys(const uint32_t (&key)[KPL], int nv, uint32_t ba
         gt += (in0 && y.x > x) + (in1 && y.y > x) + (in2 && y.z > x) + (in3 && y.w > x);
         ge += (in0 && y.x >= x) + (in1 && y.y >= x) + (in2 && y.z >= x) + (in3 && y.w >= x);
       }
-#pragma unroll
-      for (int off = TPK / 2; off > 0; off >>= 1) {
-        gt += (uint32_t)__shfl_xor((int)gt, off, kWave);
-        ge += (uint32_t)__shfl_xor((int)ge, off, kWave);
-      }
+      gt = group_sum<TPK>(gt);
+      ge = group_sum<TPK>(ge);
       // the threads holding T agree; they write the same values
       if (t % TPK == 0 && i < (int)cnt && gt < need && need <= ge) { res[0] = x; res[1] = need - gt; }
       __syncthreads();
