@@ -46,29 +46,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "0279b996629b830d",
+    "sources": "2e15cb78c87c1adb",
     "tiny_decode_1k": {
-        "indexer": 129085,
-        "topk": 20353,
-        "attention": 81913
+        "indexer": 129079,
+        "topk": 16130,
+        "attention": 81916
     },
     "spec_decode_32k": {
-        "indexer": 5436208,
-        "topk": 1309515,
-        "attention": 18115619
+        "indexer": 5436189,
+        "topk": 1315648,
+        "attention": 18115506
     },
     "prefill_128k": {
-        "indexer": 1185979323,
-        "topk": 1090086837,
-        "attention": 1912310836
+        "indexer": 1186067013,
+        "topk": 1089600173,
+        "attention": 1921153427
     },
     "int8_batched_decode_64k": {
-        "attention": 1154849080
+        "attention": 1155535251
     },
     "decode_256k": {
-        "indexer": 42208248,
-        "topk": 10669093,
-        "attention": 20332586
+        "indexer": 42208291,
+        "topk": 10651749,
+        "attention": 20332578
     }
 }
 
