@@ -63,12 +63,6 @@ struct AttnParams {
   int rows;           // B * S
 };
 
-__device__ __forceinline__ void store_out(void* out, size_t i, float v, int dt) {
-  if (dt == kF32) ((float*)out)[i] = v;
-  else if (dt == kF16) ((_Float16*)out)[i] = (_Float16)v;
-  else ((__bf16*)out)[i] = (__bf16)v;
-}
-
 // out[i .. i+3] = O / L (0 where L == 0), rounded to the output dtype.
 __device__ __forceinline__ void store_out4(void* out, size_t i, f32x4 O, float L, int dt) {
   f32x4 r;
