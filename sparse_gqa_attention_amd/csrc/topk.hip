@@ -1020,10 +1020,11 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // the digits chosen so far.  Every wave scans the whole histogram itself
 // (the four waves reach the same bin), so a level costs one barrier, and the
 // levels' histograms are zeroed up front.  Once the chosen bin holds at most
-// 64 keys they are listed and ranked directly (each lane compares its key
-// with all of them, ties counted).  Ordered emission: one block scan of the
-// threads' (above, tie) counts.  With four waves a thread holds at most 16
-// keys, so the per-key loops stay short on each SIMD.
+// 64 keys they are listed and ranked directly (each compared with all of
+// them, ties counted; the comparisons spread over the workgroup).  Ordered
+// emission: one block scan of the threads' (above, tie) counts.  With four
+// waves a thread holds at most 16 keys, so the per-key loops stay short on
+// each SIMD (select_held_keys, shared with the resident plan's select).
 constexpr int kSmallKeys = 4096;
 constexpr int kSmallThreads = 256;
 static_assert(kSmallKeys < 65536, "emission packs counts in 16 bits");
