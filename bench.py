@@ -46,29 +46,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "2e15cb78c87c1adb",
+    "sources": "57485c44ce9bb965",
     "tiny_decode_1k": {
-        "indexer": 129079,
-        "topk": 16130,
-        "attention": 81916
+        "indexer": 129082,
+        "topk": 17793,
+        "attention": 81911
     },
     "spec_decode_32k": {
-        "indexer": 5436189,
-        "topk": 1315648,
-        "attention": 18115506
+        "indexer": 5436416,
+        "topk": 1315651,
+        "attention": 18115733
     },
     "prefill_128k": {
-        "indexer": 1186067013,
-        "topk": 1089600173,
-        "attention": 1921153427
+        "indexer": 1185965477,
+        "topk": 1090321186,
+        "attention": 1921075531
     },
     "int8_batched_decode_64k": {
-        "attention": 1155535251
+        "attention": 1154981111
     },
     "decode_256k": {
-        "indexer": 42208291,
-        "topk": 10651749,
-        "attention": 20332578
+        "indexer": 42208193,
+        "topk": 10647747,
+        "attention": 20332538
     }
 }
 
