@@ -1,12 +1,14 @@
-"""Seeded random shapes across the top-k plans and the attention schedules.
+"""Seeded random shapes across the indexer plans, the top-k plans and the
+attention schedules.
 
 Each case draws its sizes, live lengths, runtime bound and score or input
 distribution from a fixed seed, so a failure names a reproducible case.
 The plans and schedules a case lands on are whatever the planner picks for
 those sizes: the sweep covers plan boundaries (4096 and 32768 keys, 128
 rows, the split counts of the decode attention) that hand-picked tests may
-straddle.  Top-k results are bit-exact against the oracle's full sort;
-attention outputs pass the same gate as the other attention tests.
+straddle.  Indexer scores (integer inputs) and top-k indices are
+bit-exact against the oracle; attention outputs pass the same gate as the
+other attention tests.
 """
 import numpy as np
 import pytest
@@ -14,7 +16,8 @@ import torch
 
 import oracle
 from dsa_synth import SPEC_DECODE_32K, indexer_like_scores, make_inputs, scaled, torch_dtype
-from gpu_util import DEV, dsa, first_mismatch, run_attention, run_topk, say, upload  # noqa: F401
+from gpu_util import (DEV, dsa, first_mismatch, run_attention, run_indexer, run_topk,  # noqa: F401
+                      say, upload)
 from parity import assert_output_close
 from test_gpu_attention import COMBOS, random_selection
 
@@ -94,3 +97,38 @@ def test_attention_random_shapes(dsa, seed):
         assert rel <= 1e-5, f"seed {seed} {combo}: FP32 output rel RMSE {rel:.2e}"
     say(f"attention seed={seed} {combo} B={B} S={S} L={L} k={k} max_kv_len={mx} kv_len={kv} "
         f"decode={decode}: rel={rel:.2e} max={mx_err:.2e}")
+
+
+def _indexer_case(seed):
+    r = np.random.default_rng(4000 + seed)
+    B = int(r.integers(1, 4))
+    S = int(r.choice([1, 2, 5, 8, 9, 33, 70]))
+    H = int(r.integers(1, 17))
+    Di = int(r.choice([32, 64, 128]))
+    L = int(r.choice([S + 3, 500, 2049, 9000, 40000, 90000]))
+    dt = "bf16" if r.integers(0, 2) == 0 else "f16"
+    mx = int(r.integers(S, L + 1))
+    kv = [int(r.integers(S, mx + 1)) for _ in range(B)]
+    kv[int(r.integers(0, B))] = mx              # the bound is reached
+    return B, S, H, Di, L, dt, mx, kv
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_indexer_random_shapes(dsa, seed):
+    B, S, H, Di, L, dt, mx, kv = _indexer_case(seed)
+    plan = dsa.plan_fields(dsa.dsa_describe_plan(dsa.DSA_PLAN_INDEXER, B, S, L, mx, D_idx=Di))["kernel"]
+    say(f"indexer seed={seed} B={B} S={S} H={H} D={Di} L={L} {dt} max_kv_len={mx} kv_len={kv} {plan}")
+    w = scaled(SPEC_DECODE_32K, B=B, S=S, H_idx=H, D_idx=Di, L=L, H_q=2, H_kv=1, D=64,
+               idx_dtype=dt, seed=5000 + seed)
+    x = make_inputs(w, kv_len=kv)
+    g = upload(x)
+    scores = run_indexer(dsa, g, L, max_kv_len=mx)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_scores(x["q_idx"], x["w_idx"], x["key_state"], kv, S)
+    got = scores.cpu().double().numpy()
+    for b in range(B):
+        for s in range(S):
+            pos = kv[b] - S + s
+            a, want = got[b, s, :pos + 1], ref[b, s, :pos + 1]
+            assert np.array_equal(a, want), f"seed {seed} ({plan}) b={b} s={s}: {first_mismatch(a, want)}"
+        assert np.all(np.isnan(got[b, :, kv[b]:])), f"seed {seed} ({plan}): wrote past kv_len"
