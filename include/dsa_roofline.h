@@ -2,8 +2,8 @@
  * dsa_roofline.h -- ceiling probes of the benchmark (libdsa_roofline.so).
  *
  * These kernels are not part of the attention path.  They measure, on the
- * GPU and in the run that times the path, the rates its kernels are judged
- * against: streaming HBM read and copy, back-to-back BF16 MFMA, and random
+ * GPU and in the run that times the path, the rates its kernels are compared
+ * with: streaming HBM read and copy, back-to-back BF16 MFMA, and random
  * 256-byte row gathers.  Pointers are caller-owned device memory (16-byte
  * aligned); calls only enqueue on `stream` (a hipStream_t as void*; NULL is
  * the null stream).  Return 0 on success, 1 if the launch failed, 2 for an
