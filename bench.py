@@ -46,29 +46,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "57485c44ce9bb965",
+    "sources": "5c6bed52f476e4a3",
     "tiny_decode_1k": {
-        "indexer": 129082,
-        "topk": 17793,
-        "attention": 81911
+        "indexer": 129079,
+        "topk": 17794,
+        "attention": 81917
     },
     "spec_decode_32k": {
-        "indexer": 5436416,
-        "topk": 1315651,
-        "attention": 18115733
+        "indexer": 5436464,
+        "topk": 1315666,
+        "attention": 18115887
     },
     "prefill_128k": {
-        "indexer": 1185965477,
-        "topk": 1090321186,
-        "attention": 1921075531
+        "indexer": 1185994241,
+        "topk": 1090307340,
+        "attention": 1914773469
     },
     "int8_batched_decode_64k": {
-        "attention": 1154981111
+        "attention": 1154679632
     },
     "decode_256k": {
-        "indexer": 42208193,
-        "topk": 10647747,
-        "attention": 20332538
+        "indexer": 42208080,
+        "topk": 10647735,
+        "attention": 20332468
     }
 }
 

@@ -13,7 +13,10 @@
 // for 32 consecutive keys and lanes 32..63 token t1's: one coalesced
 // 128-byte store per half wave.
 //
-// Prefill (indexer_stream_kernel): a workgroup holds 32 query tokens (8
+// Prefill (S > 8) folds the head weights into the query first
+// (indexer_fold_kernel, below).  The per-head streaming kernel
+// (indexer_stream_kernel) serves very long decode contexts, and prefill
+// when L_cap >= 2^24: a workgroup holds 32 query tokens (8
 // waves x 2 token pairs; 16 tokens, one pair per wave, at D_idx 128) in
 // registers and streams a range of keys through two LDS buffers.  Each run of
 // keys is copied by direct global->LDS loads (16-byte chunks XOR-swizzled by
@@ -37,9 +40,10 @@
 //
 // The XCD-aware renumbering dispatches the token blocks that share a key
 // range consecutively on one XCD and deals key ranges to the XCDs in turn,
-// so key-state runs are read through L2 (about 33 MB of HBM-side fetch for
-// a 2048-token prefill at 128K, against 1 GiB of LDS copies) and every XCD
-// gets an equal share of every sequence.
+// so key-state runs are read through L2 (for the per-head streaming kernel
+// at a 2048-token prefill over 128K keys: 52-74 MB of HBM-side fetch
+// against 1 GiB of LDS copies) and every XCD gets an equal share of every
+// sequence.
 #include <type_traits>
 
 #include "dsa_device.h"

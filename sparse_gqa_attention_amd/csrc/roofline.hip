@@ -1,5 +1,5 @@
 // Ceiling probes for the benchmark (libdsa_roofline.so, include/dsa_roofline.h):
-// the rates the hot-path kernels are judged against, measured on the same
+// the rates the hot-path kernels are compared with, measured on the same
 // GPU in the same run as the path itself.
 //  * streaming read and copy of large buffers (the HBM ceiling);
 //  * back-to-back v_mfma_f32_32x32x16_bf16 on register operands (the MFMA

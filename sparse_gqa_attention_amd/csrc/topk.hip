@@ -8,7 +8,8 @@
 // 1. Threshold estimate.  A sample of the row (all of it when the row is
 //    short, else blocks of 256 consecutive keys spread evenly over the row:
 //    2048 keys for an LDS-resident row, 8192 when streaming, 2048 or 4096 in
-//    the split plan) goes through two radix levels (the top 11 + 11 key bits) to the
+//    the split plan) goes through two radix levels (the top 11 + 11 key bits;
+//    the resident plan: 8 + 8 bits of key - the sample's smallest key) to the
 //    bin of the key of rank r = ceil(1.2e + 4 sqrt(e)) + 8, where e = k *
 //    sample / n is the expected sample rank of the k-th largest key.  The
 //    bin's lower edge T_lo is at or below that key; every key >= T_lo is a
@@ -16,10 +17,12 @@
 // 2. Collection.  One pass over the row lists the candidates; the resident
 //    and split plans keep the list in index order.
 // (The small plan for short rows skips steps 1-2: it selects on the whole row.)
-// 3. Exact selection on the list, in LDS: radix select of the k-th largest
-//    key T (index-ordered lists: 12-bit digits of key - T_lo, two levels
-//    for key spans below 2^24).  When only some of the keys equal to T fit,
-//    the lowest indices win.  Exactly k entries.
+// 3. Exact selection on the list: radix select of the k-th largest key T
+//    on digits of key - T_lo (the split plan: 12-bit digits, two levels for
+//    key spans below 2^24; the resident plan: the candidates held in
+//    registers, 8-bit digits, and a direct rank once a bin holds at most 64
+//    keys).  When only some of the keys equal to T fit, the lowest indices
+//    win.  Exactly k entries.
 // 4. Ordered emission.  An index-ordered list is compacted by one block scan
 //    (a key equal to T is kept while fewer than `take` equal keys precede
 //    it).  The streaming plan's unordered list sets the kept indices in an
