@@ -503,6 +503,24 @@ __device__ void radix_lower_bound_pre(Get get, int count, uint32_t need, uint32_
   T_lo = (b0 << 21) | (misc[2] << 10);
 }
 
+// Hit bits of x[0..N) against a threshold's float image f_lo: bit u is set
+// when x[u] >= f_lo.  For a finite f_lo (the caller branches on it,
+// block-uniformly) the test is the sign of x - g, g = f_lo but -0.0 for a
+// zero threshold (so that -0.0 - g = +0.0): the difference of two distinct
+// finite floats is nonzero and keeps its sign (FP32 denormals are not
+// flushed), equal ones give +0.0, and x = +-inf gives +-inf.  Two VALU
+// operations per key (subtract, shift the sign bit in), with no compare and
+// no condition-register hazard.
+template <int N>
+__device__ __forceinline__ uint32_t hits_finite(const float (&x)[N], float f_lo) {
+  static_assert(N <= 32, "one bit per key");
+  const float g = f_lo == 0.0f ? -0.0f : f_lo;
+  uint32_t miss = 0;
+#pragma unroll
+  for (int u = N - 1; u >= 0; --u) miss = __builtin_amdgcn_alignbit(miss, __float_as_uint(x[u] - g), 31);
+  return N == 32 ? ~miss : (~miss & ((1u << N) - 1u));
+}
+
 // ====================================================================== resident plan
 // Dynamic LDS: row scores [kResKeys] (later the select's rank list) | hist
 // (the sample threshold's, later the select's level histograms) | scratch |
@@ -775,13 +793,23 @@ __global__ __launch_bounds__(NT) void topk_resident_kernel(
     if (t == 0) s.misc[11] = 0;                 // ordered by the scan's barrier
     const float4* row4 = reinterpret_cast<const float4*>(rowf);
     uint32_t mask = 0;
+    if (__builtin_isfinite(f_lo)) {             // block-uniform
+      float x[KPL];                             // read i's keys at 4 i (rotated back below)
 #pragma unroll
-    for (int i = KPL / 4 - 1; i >= 0; --i) {
-      const float4 q = row4[(KPL / 4) * t + ((i + t) & (KPL / 4 - 1))];
-      mask = (mask << 1) | (q.w >= f_lo ? 1u : 0u);
-      mask = (mask << 1) | (q.z >= f_lo ? 1u : 0u);
-      mask = (mask << 1) | (q.y >= f_lo ? 1u : 0u);
-      mask = (mask << 1) | (q.x >= f_lo ? 1u : 0u);
+      for (int i = 0; i < KPL / 4; ++i) {
+        const float4 q = row4[(KPL / 4) * t + ((i + t) & (KPL / 4 - 1))];
+        x[4 * i] = q.x; x[4 * i + 1] = q.y; x[4 * i + 2] = q.z; x[4 * i + 3] = q.w;
+      }
+      mask = hits_finite<KPL>(x, f_lo);
+    } else {
+#pragma unroll
+      for (int i = KPL / 4 - 1; i >= 0; --i) {
+        const float4 q = row4[(KPL / 4) * t + ((i + t) & (KPL / 4 - 1))];
+        mask = (mask << 1) | (q.w >= f_lo ? 1u : 0u);
+        mask = (mask << 1) | (q.z >= f_lo ? 1u : 0u);
+        mask = (mask << 1) | (q.y >= f_lo ? 1u : 0u);
+        mask = (mask << 1) | (q.x >= f_lo ? 1u : 0u);
+      }
     }
     const uint32_t rot = 4u * (uint32_t)(t & (KPL / 4 - 1));
     mask = (mask << rot) | (mask >> ((32u - rot) & 31u));
@@ -950,6 +978,7 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
       // (score_key is order-preserving and gives -0.0 the key of +0.0;
       // denormals are preserved in comparisons).  Only hits become keys.
       const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
+      const bool fin = __builtin_isfinite(f_lo);
       for (int b4 = 0; b4 < n4; b4 += V * NT) {
         float x[4 * V];
         uint32_t hm = 0;
@@ -966,11 +995,18 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
           }
           x[4 * u + 0] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
         }
+        if (fin) {                              // block-uniform
+          hm = hits_finite<4 * V>(x, f_lo);
 #pragma unroll
-        for (int u = 0; u < V; ++u) {
-          const bool ok = b4 + u * NT + t < n4;
+          for (int u = 0; u < V; ++u)
+            if (b4 + u * NT + t >= n4) hm &= ~(0xFu << (4 * u));
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hm |= (uint32_t)(ok && x[4 * u + e] >= f_lo) << (4 * u + e);
+          for (int u = 0; u < V; ++u) {
+            const bool ok = b4 + u * NT + t < n4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hm |= (uint32_t)(ok && x[4 * u + e] >= f_lo) << (4 * u + e);
+          }
         }
         if (__ballot(hm != 0u) == 0) continue;            // wave-uniform
         uint32_t slot = wave_reserve((uint32_t)__popc(hm), &s.misc[8]);
@@ -1294,8 +1330,13 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   // pattern and no hits; K2 then selects from the whole row.
   const float f_lo = __uint_as_float((T_lo & 0x80000000u) ? (T_lo & 0x7FFFFFFFu) : ~T_lo);
   uint32_t hits = 0;
+  if (__builtin_isfinite(f_lo)) {               // block-uniform
+    const int nv = n - jl;                      // keys of this lane inside the row
+    hits = hits_finite<U>(v, f_lo) & (nv >= U ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u));
+  } else {
 #pragma unroll
-  for (int u = 0; u < U; ++u) hits |= (uint32_t)(jl + u < n && v[u] >= f_lo) << u;
+    for (int u = 0; u < U; ++u) hits |= (uint32_t)(jl + u < n && v[u] >= f_lo) << u;
+  }
   // The lane's keys go to LDS so that the write loop visits its hits only
   // (a key picked by a per-lane bit index cannot be read from registers).
   // Each lane reads back only what it wrote itself: no barrier.
