@@ -46,29 +46,29 @@ BY_WORKLOAD = ("tiny_decode_1k", "prefill_128k", "int8_batched_decode_64k", "dec
 # profiles/<workload>_hot_path_kernels.txt.  Reported only while the kernel
 # sources still have that digest.
 MEASURED_TRAFFIC = {
-    "sources": "5c6bed52f476e4a3",
+    "sources": "dd5f41cca957d375",
     "tiny_decode_1k": {
-        "indexer": 129079,
-        "topk": 17794,
-        "attention": 81917
+        "indexer": 129082,
+        "topk": 17793,
+        "attention": 81911
     },
     "spec_decode_32k": {
-        "indexer": 5436464,
-        "topk": 1315666,
-        "attention": 18115887
+        "indexer": 5436168,
+        "topk": 1321780,
+        "attention": 18115341
     },
     "prefill_128k": {
-        "indexer": 1185994241,
-        "topk": 1090307340,
-        "attention": 1914773469
+        "indexer": 1185967203,
+        "topk": 1090173510,
+        "attention": 1912552308
     },
     "int8_batched_decode_64k": {
-        "attention": 1154679632
+        "attention": 1153657589
     },
     "decode_256k": {
-        "indexer": 42208080,
-        "topk": 10647735,
-        "attention": 20332468
+        "indexer": 42208151,
+        "topk": 10656706,
+        "attention": 20332493
     }
 }
 
